@@ -1,0 +1,201 @@
+/*
+ * dsa.h -- C ABI of the DSA (lightning indexer + top-k + sparse MLA) hot path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method, as "TokenSpeed Kimi K3.1" (section "Integrating sparse attention
+ * with the K3 stack") lays it out, runs per attention layer in four steps:
+ * Write the new token's FP8 index key, Score every cached key with the
+ * indexer's 32 heads, Select the 2,048 highest-scoring positions per query
+ * row, and Attend with MLA over only those latent rows. This library covers
+ * Score, Select and Attend.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are device pointers unless a comment says "host". `stream` is a
+ *    hipStream_t passed as void* (NULL = the default stream). All work is
+ *    enqueued asynchronously on that stream; nothing synchronises the host.
+ *  - The caller owns every buffer, workspace included. The library never
+ *    allocates or frees memory and keeps no pointer after a call returns. It
+ *    holds no state between calls; calls on different streams with disjoint
+ *    outputs and workspaces may run concurrently.
+ *  - Errors are returned as dsa_status codes, never thrown. Arguments are
+ *    checked on the host before anything is enqueued; on any error nothing is
+ *    enqueued. DSA_ERR_HIP reports a failed launch (see dsa_last_error()).
+ *  - Rows are request-major: row = b * rows_per_request + r. Row r of request
+ *    b sits at position ctx_len[b] - rows_per_request + r and sees the tokens
+ *    0..position, its own token included (the Write step precedes Score).
+ *    Decode verification rows and prefill chunks follow the same rule.
+ *  - FP8 is the OCP E4M3 encoding (bias 7, max 448, no infinities).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent sizes */
+  DSA_ERR_UNSUPPORTED = -2, /* a shape this build does not implement */
+  DSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than dsa_workspace_size() */
+  DSA_ERR_HIP = -4          /* a HIP launch failed; nothing else was enqueued after it */
+} dsa_status;
+
+enum { DSA_Q_BF16 = 0, DSA_Q_FP8 = 1 };
+
+/* Workspace kinds for dsa_workspace_size(). */
+enum { DSA_WS_TOPK = 1, DSA_WS_MLA_DECODE = 2, DSA_WS_MLA_PREFILL = 3, DSA_WS_DECODE = 4 };
+
+#define DSA_BLOCK 64        /* tokens per cache page */
+#define DSA_IDX_HEADS 32    /* indexer heads */
+#define DSA_IDX_DIM 128     /* indexer head dim */
+#define DSA_LAT_DIM 576     /* latent width: 512 compressed KV + 64 RoPE dims */
+#define DSA_V_DIM 512       /* value width: the first 512 latent dims */
+#define DSA_MLA_HEADS 16    /* MLA heads per call */
+#define DSA_MAX_TOPK 2048
+
+/*
+ * Paged cache, split planes, 64-token pages. One page id addresses the same
+ * 64 tokens in all four planes ("TokenSpeed Kimi K3.1", section "Storing index
+ * keys in the flat KV cache": the index-key plane sits next to the latent
+ * rows and shares their page).
+ *   key_fp8   [num_blocks][64][128] E4M3 index keys (128 B per token)
+ *   key_scale [num_blocks][64]      fp32 per-token key scale (4 B)
+ *   lat_fp8   [num_blocks][64][576] E4M3 latent rows
+ *   lat_scale [num_blocks][64]      fp32 per-token latent scale
+ * A key or latent dequantises as code value * scale. Planes must be 16-byte
+ * aligned.
+ */
+typedef struct {
+  const uint8_t* key_fp8;
+  const float* key_scale;
+  const uint8_t* lat_fp8;
+  const float* lat_scale;
+  int32_t num_blocks;
+  int32_t block_size; /* must be 64 */
+} dsa_cache;
+
+/*
+ * A batch of requests over the cache.
+ *   ctx_len     device int32 [num_requests]: context length of each request,
+ *               counting its rows_per_request new rows; rows_per_request <=
+ *               ctx_len[b] <= max_ctx.
+ *   block_table device int32 [num_requests][max_blocks]: page id of each
+ *               64-token logical block; entries past a request's length may
+ *               hold anything (-1 by convention) and are never read.
+ *   max_blocks  host: row stride of block_table; max_blocks*64 >= max_ctx.
+ *   max_ctx     host: an upper bound of every ctx_len (sizes the launch grid).
+ */
+typedef struct {
+  int32_t num_requests;
+  int32_t rows_per_request;
+  const int32_t* ctx_len;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  int32_t max_ctx;
+} dsa_batch;
+
+/*
+ * Score: the lightning indexer. For every row and every token s the row sees,
+ *   scores[row * ld + s] = sum_h w[row][h] * ReLU(q[row][h] . khat_s)
+ * with khat_s = key_fp8[s] * key_scale[s] and q[row][h] the row's query for
+ * head h (DeepSeek-V3.2 form, to which "vLLM Day-0 Support for Kimi K3.1
+ * Pro", section "What Kimi K3.1 Pro changes", points; 32 heads x 128 dims,
+ * 132-byte FP8 keys). Each key is read once for all rows of its request
+ * ("TokenSpeed Kimi K3.1", section "Reducing indexer overhead on AMD
+ * MI350X").
+ *   q        q_dtype DSA_Q_BF16: bf16 [rows][32][128];
+ *            q_dtype DSA_Q_FP8:  E4M3 [rows][32][128] with q_scale fp32 [rows]
+ *            (each row dequantises as code * q_scale[row]); q_scale must be
+ *            NULL for BF16.
+ *   w        bf16 [rows][32] head weights (any sign).
+ *   scores   fp32 [rows][ld], ld >= max_ctx. Entries s > position(row) are not
+ *            written.
+ * Accumulation is fp32; products of bf16 or E4M3 query values with E4M3 key
+ * values are exact.
+ */
+int32_t dsa_index_score(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t q_dtype,
+                        const float* q_scale, const void* w, float* scores, int64_t ld, void* stream);
+
+/*
+ * Select: per row, the k highest scores among scores[row * ld + 0 .. row_len[row]-1]
+ * ("TokenSpeed Kimi K3.1", step 3: a radix top-k keeps the 2,048
+ * highest-scoring positions for each query). The selection is exact: ranking
+ * is by score (fp32 total order, -0 < +0), ties go to the lower position, so
+ * the selected set is unique and identical across runs.
+ *   row_len  device int32 [rows], 0 <= row_len[row] <= ld.
+ *   idx      int32 [rows][k]: the selected positions in unspecified order;
+ *            if row_len < k the first row_len entries hold every position and
+ *            the rest are -1.
+ *   ws       workspace of at least dsa_workspace_size(DSA_WS_TOPK, rows, ld, k, 0) bytes.
+ * 1 <= k <= 2048. Scores must not be NaN.
+ */
+int32_t dsa_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows, int32_t k,
+                 int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Attend: exact MLA over the selected latent rows only ("vLLM Day-0 Support
+ * for Kimi K3.1 Pro", section "What Kimi K3.1 Pro changes": MLA runs exactly
+ * over only the selected tokens; latent = 512 compressed KV + 64 RoPE dims,
+ * "Kimi K3.1 Pro on AMD Instinct", model overview). For each row and head h:
+ *   logit_j = softmax_scale * q[row][h] . chat_j  over all 576 dims,
+ *   out[row][h][v] = sum_j softmax(logit)_j * chat_j[v]  for v < 512,
+ *   lse[row][h] = log(sum_j exp(logit_j))  (natural log),
+ * with chat_j = lat_fp8[j] * lat_scale[j] and j over idx[row][0..k-1];
+ * entries < 0 are skipped. A row with no valid entry gets out = 0 and
+ * lse = -inf. Positions index the row's request through block_table.
+ *   q        bf16 [rows][num_heads][576]
+ *   idx      int32 [rows][k], each entry -1 or a position the row sees.
+ *   out      bf16 [rows][num_heads][512]
+ *   lse      fp32 [rows][num_heads] or NULL.
+ *   ws       workspace of dsa_workspace_size(DSA_WS_MLA_DECODE or _PREFILL, rows, 0, k, num_heads).
+ * num_heads == 16, 1 <= k <= 2048. The decode variant splits each row's k
+ * positions over several workgroups and merges them by log-sum-exp; the
+ * prefill variant gives each row one workgroup.
+ */
+int32_t dsa_sparse_mla_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t num_heads,
+                              const int32_t* idx, int32_t k, float softmax_scale, void* out, float* lse,
+                              void* ws, size_t ws_bytes, void* stream);
+int32_t dsa_sparse_mla_prefill(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t num_heads,
+                               const int32_t* idx, int32_t k, float softmax_scale, void* out, float* lse,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole decode step: Score (bf16 queries) -> Select (top-k) -> Attend, as
+ * one call on one stream. The pages' problem statement: for every query row
+ * the indexer scores one FP8 key per earlier token, the top k are kept, and
+ * MLA runs over only those rows ("TokenSpeed Kimi K3.1", section
+ * "Integrating sparse attention with the K3 stack", steps 2-4).
+ *   q_idx    bf16 [rows][32][128], w bf16 [rows][32]  (as dsa_index_score)
+ *   q_mla    bf16 [rows][num_heads][576]              (as dsa_sparse_mla_decode)
+ *   out      bf16 [rows][num_heads][512]; lse fp32 [rows][num_heads] or NULL
+ *   idx_out  int32 [rows][k] or NULL: receives the selection.
+ *   ws       workspace of dsa_workspace_size(DSA_WS_DECODE, rows, max_ctx, k, num_heads)
+ *            (holds the fp32 scores, the selection and the attention partials).
+ */
+int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                   const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale, void* out,
+                   float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes an entry point needs (0 if it needs none). For DSA_WS_TOPK,
+ * `max_ctx` is the longest row_len. Returns 0 and no error for an unknown kind. */
+size_t dsa_workspace_size(int32_t kind, int32_t rows, int64_t max_ctx, int32_t k, int32_t num_heads);
+
+/* Text of a status code (static storage). */
+const char* dsa_status_string(int32_t status);
+
+/* Message of the last DSA_ERR_HIP or argument error on the calling host thread
+ * (thread-local static storage; empty if none). */
+const char* dsa_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

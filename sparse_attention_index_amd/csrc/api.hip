@@ -1,0 +1,285 @@
+// C ABI of libdsa: host-side argument checks, workspace carving and launch
+// sequencing. Declarations and semantics are in include/dsa.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/dsa.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace dsa;
+
+namespace {
+
+thread_local char g_err[512];
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t check_batch(const dsa_batch* b) {
+  if (!b) return fail(DSA_ERR_INVALID_ARG, "batch is null");
+  if (b->num_requests < 1 || b->rows_per_request < 1)
+    return fail(DSA_ERR_INVALID_ARG, "num_requests and rows_per_request must be >= 1");
+  if (!b->ctx_len || !b->block_table) return fail(DSA_ERR_INVALID_ARG, "ctx_len or block_table is null");
+  if (b->max_ctx < b->rows_per_request) return fail(DSA_ERR_INVALID_ARG, "max_ctx < rows_per_request");
+  if ((int64_t)b->max_blocks * DSA_BLOCK < b->max_ctx)
+    return fail(DSA_ERR_INVALID_ARG, "max_blocks * 64 < max_ctx");
+  if ((int64_t)b->num_requests * b->rows_per_request > INT32_MAX / 2)
+    return fail(DSA_ERR_UNSUPPORTED, "too many rows");
+  return DSA_OK;
+}
+
+int32_t check_cache(const dsa_cache* c, bool keys, bool lat) {
+  if (!c) return fail(DSA_ERR_INVALID_ARG, "cache is null");
+  if (c->block_size != DSA_BLOCK) return fail(DSA_ERR_UNSUPPORTED, "block_size must be 64");
+  if (c->num_blocks < 1) return fail(DSA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (keys && (!c->key_fp8 || !c->key_scale)) return fail(DSA_ERR_INVALID_ARG, "key planes are null");
+  if (lat && (!c->lat_fp8 || !c->lat_scale)) return fail(DSA_ERR_INVALID_ARG, "latent planes are null");
+  if (keys && !aligned(c->key_fp8, 16)) return fail(DSA_ERR_INVALID_ARG, "key_fp8 must be 16-byte aligned");
+  if (lat && !aligned(c->lat_fp8, 16)) return fail(DSA_ERR_INVALID_ARG, "lat_fp8 must be 16-byte aligned");
+  return DSA_OK;
+}
+
+int32_t check_mla(int32_t num_heads, int32_t k, const void* q, const int32_t* idx, const void* out, bool need_idx) {
+  if (num_heads != DSA_MLA_HEADS) return fail(DSA_ERR_UNSUPPORTED, "num_heads must be 16");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in [1, 2048]");
+  if (!q || (need_idx && !idx) || !out) return fail(DSA_ERR_INVALID_ARG, "q, idx or out is null");
+  if (!aligned(q, 16)) return fail(DSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  return DSA_OK;
+}
+
+int64_t decode_ld(int32_t max_ctx) { return ((int64_t)max_ctx + 63) / 64 * 64; }
+
+struct DecodeWs {
+  float* scores;
+  int32_t* row_len;
+  int32_t* idx;
+  void* topk;
+  void* mla;
+};
+
+size_t decode_ws_parts(int32_t rows, int64_t max_ctx, int32_t k, DecodeWs* out, void* base) {
+  const int64_t ld = decode_ld((int32_t)max_ctx);
+  size_t off = 0;
+  const size_t s_scores = align256((size_t)rows * ld * sizeof(float));
+  const size_t s_len = align256((size_t)rows * sizeof(int32_t));
+  const size_t s_idx = align256((size_t)rows * k * sizeof(int32_t));
+  const size_t s_topk = align256(topk_ws_bytes(rows, ld));
+  const size_t s_mla = align256(mla_ws_bytes(rows, k, true));
+  if (out) {
+    char* p = static_cast<char*>(base);
+    out->scores = reinterpret_cast<float*>(p + off);
+    off += s_scores;
+    out->row_len = reinterpret_cast<int32_t*>(p + off);
+    off += s_len;
+    out->idx = reinterpret_cast<int32_t*>(p + off);
+    off += s_idx;
+    out->topk = p + off;
+    off += s_topk;
+    out->mla = s_mla ? p + off : nullptr;
+    off += s_mla;
+    return off;
+  }
+  return s_scores + s_len + s_idx + s_topk + s_mla;
+}
+
+int32_t run_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows, int32_t k, int32_t* idx,
+                 void* ws, bool have_hist, hipStream_t st) {
+  const TopkWs w = topk_ws_carve(ws, rows, ld);
+  if (!have_hist) {
+    int32_t r = hip_status(launch_topk_clear(w, rows, st), "topk clear");
+    if (r) return r;
+    r = hip_status(launch_topk_hist(scores, ld, row_len, rows, ld, w, st), "topk hist");
+    if (r) return r;
+  }
+  return hip_status(launch_topk_select(scores, ld, row_len, rows, ld, k, idx, w, st), "topk select");
+}
+
+int32_t run_mla(const dsa_batch* batch, const dsa_cache* cache, const void* q, const int32_t* idx, int32_t k,
+                float softmax_scale, void* out, float* lse, void* ws, bool split, hipStream_t st) {
+  MlaArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.idx = idx;
+  a.lat_fp8 = cache->lat_fp8;
+  a.lat_scale = cache->lat_scale;
+  a.block_table = batch->block_table;
+  a.max_blocks = batch->max_blocks;
+  a.R = batch->rows_per_request;
+  a.k = k;
+  a.sm_scale = softmax_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  const int rows = batch->num_requests * batch->rows_per_request;
+  return hip_status(launch_sparse_mla(a, rows, split, ws, st), "sparse mla");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_index_score(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t q_dtype,
+                        const float* q_scale, const void* w, float* scores, int64_t ld, void* stream) {
+  g_err[0] = 0;
+  int32_t r = check_batch(batch);
+  if (r) return r;
+  if ((r = check_cache(cache, true, false))) return r;
+  if (!q || !w || !scores) return fail(DSA_ERR_INVALID_ARG, "q, w or scores is null");
+  if (q_dtype == DSA_Q_BF16) {
+    if (q_scale) return fail(DSA_ERR_INVALID_ARG, "q_scale must be null for bf16 queries");
+  } else if (q_dtype == DSA_Q_FP8) {
+    if (!q_scale) return fail(DSA_ERR_INVALID_ARG, "q_scale is required for FP8 queries");
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "q_dtype must be DSA_Q_BF16 or DSA_Q_FP8");
+  }
+  if (ld < batch->max_ctx) return fail(DSA_ERR_INVALID_ARG, "ld < max_ctx");
+  if (!aligned(q, 16)) return fail(DSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  ScoreArgs a;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.w = static_cast<const uint16_t*>(w);
+  a.key_fp8 = cache->key_fp8;
+  a.key_scale = cache->key_scale;
+  a.ctx_len = batch->ctx_len;
+  a.block_table = batch->block_table;
+  a.max_blocks = batch->max_blocks;
+  a.R = batch->rows_per_request;
+  a.scores = scores;
+  a.ld = ld;
+  a.hist = nullptr;
+  return hip_status(launch_index_score(a, batch->num_requests, batch->max_ctx, q_dtype == DSA_Q_FP8,
+                                       static_cast<hipStream_t>(stream)),
+                    "index score");
+}
+
+int32_t dsa_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows, int32_t k, int32_t* idx,
+                 void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (rows < 0 || ld < 1) return fail(DSA_ERR_INVALID_ARG, "rows must be >= 0 and ld >= 1");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in [1, 2048]");
+  if (rows == 0) return DSA_OK;
+  if (!scores || !row_len || !idx) return fail(DSA_ERR_INVALID_ARG, "scores, row_len or idx is null");
+  if (ld > INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "rows longer than 2^31 scores");
+  const size_t need = dsa_workspace_size(DSA_WS_TOPK, rows, ld, k, 0);
+  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "topk needs %zu workspace bytes", need);
+  return run_topk(scores, ld, row_len, rows, k, idx, ws, false, static_cast<hipStream_t>(stream));
+}
+
+static int32_t mla_entry(bool split, const dsa_batch* batch, const dsa_cache* cache, const void* q,
+                         int32_t num_heads, const int32_t* idx, int32_t k, float softmax_scale, void* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int32_t r = check_batch(batch);
+  if (r) return r;
+  if ((r = check_cache(cache, false, true))) return r;
+  if ((r = check_mla(num_heads, k, q, idx, out, true))) return r;
+  const int32_t rows = batch->num_requests * batch->rows_per_request;
+  const size_t need = dsa_workspace_size(split ? DSA_WS_MLA_DECODE : DSA_WS_MLA_PREFILL, rows, 0, k, num_heads);
+  if (need && (!ws || ws_bytes < need)) return fail(DSA_ERR_WORKSPACE, "sparse mla needs %zu workspace bytes", need);
+  return run_mla(batch, cache, q, idx, k, softmax_scale, out, lse, ws, split, static_cast<hipStream_t>(stream));
+}
+
+int32_t dsa_sparse_mla_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t num_heads,
+                              const int32_t* idx, int32_t k, float softmax_scale, void* out, float* lse, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return mla_entry(true, batch, cache, q, num_heads, idx, k, softmax_scale, out, lse, ws, ws_bytes, stream);
+}
+
+int32_t dsa_sparse_mla_prefill(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t num_heads,
+                               const int32_t* idx, int32_t k, float softmax_scale, void* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return mla_entry(false, batch, cache, q, num_heads, idx, k, softmax_scale, out, lse, ws, ws_bytes, stream);
+}
+
+int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                   const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale, void* out, float* lse,
+                   int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int32_t r = check_batch(batch);
+  if (r) return r;
+  if ((r = check_cache(cache, true, true))) return r;
+  if (!q_idx || !w) return fail(DSA_ERR_INVALID_ARG, "q_idx or w is null");
+  if (!aligned(q_idx, 16)) return fail(DSA_ERR_INVALID_ARG, "q_idx must be 16-byte aligned");
+  if ((r = check_mla(num_heads, k, q_mla, idx_out, out, false))) return r;
+  const int32_t rows = batch->num_requests * batch->rows_per_request;
+  const size_t need = dsa_workspace_size(DSA_WS_DECODE, rows, batch->max_ctx, k, num_heads);
+  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "decode needs %zu workspace bytes", need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DecodeWs p;
+  decode_ws_parts(rows, batch->max_ctx, k, &p, ws);
+  const int64_t ld = decode_ld(batch->max_ctx);
+  int32_t* idx = idx_out ? idx_out : p.idx;
+  const TopkWs tw = topk_ws_carve(p.topk, rows, ld);
+  // 1. clear the first-digit histograms, derive visible lengths
+  if ((r = hip_status(launch_topk_clear(tw, rows, st, p.row_len, batch->ctx_len, batch->rows_per_request),
+                      "decode clear")))
+    return r;
+  // 2. score, building the first-digit histogram on the fly
+  ScoreArgs a;
+  a.q = q_idx;
+  a.q_scale = nullptr;
+  a.w = static_cast<const uint16_t*>(w);
+  a.key_fp8 = cache->key_fp8;
+  a.key_scale = cache->key_scale;
+  a.ctx_len = batch->ctx_len;
+  a.block_table = batch->block_table;
+  a.max_blocks = batch->max_blocks;
+  a.R = batch->rows_per_request;
+  a.scores = p.scores;
+  a.ld = ld;
+  a.hist = tw.hist;
+  if ((r = hip_status(launch_index_score(a, batch->num_requests, batch->max_ctx, false, st), "decode score")))
+    return r;
+  // 3. select
+  if ((r = run_topk(p.scores, ld, p.row_len, rows, k, idx, p.topk, true, st))) return r;
+  // 4. attend
+  return run_mla(batch, cache, q_mla, idx, k, softmax_scale, out, lse, p.mla, true, st);
+}
+
+size_t dsa_workspace_size(int32_t kind, int32_t rows, int64_t max_ctx, int32_t k, int32_t num_heads) {
+  (void)num_heads;
+  if (rows <= 0) return 0;
+  switch (kind) {
+    case DSA_WS_TOPK:
+      return topk_ws_bytes(rows, max_ctx < 1 ? 1 : max_ctx);
+    case DSA_WS_MLA_DECODE:
+      return mla_ws_bytes(rows, k, true);
+    case DSA_WS_MLA_PREFILL:
+      return mla_ws_bytes(rows, k, false);
+    case DSA_WS_DECODE:
+      return decode_ws_parts(rows, max_ctx < 1 ? 1 : max_ctx, k, nullptr, nullptr);
+    default:
+      return 0;
+  }
+}
+
+const char* dsa_status_string(int32_t status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+int32_t dsa_version(void) { return 100; }
+
+}  // extern "C"

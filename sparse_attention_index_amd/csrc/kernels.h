@@ -1,0 +1,69 @@
+// Launch interfaces of the gfx950 DSA kernels (internal to libdsa).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct ScoreArgs {
+  const void* q;            // bf16 [rows][32][128] or E4M3 [rows][32][128]
+  const float* q_scale;     // fp32 [rows] (E4M3 queries) or null
+  const uint16_t* w;        // bf16 [rows][32]
+  const uint8_t* key_fp8;   // [num_blocks][64][128]
+  const float* key_scale;   // [num_blocks][64]
+  const int32_t* ctx_len;   // [B]
+  const int32_t* block_table;  // [B][max_blocks]
+  int32_t max_blocks;
+  int32_t R;                // rows per request
+  float* scores;            // [rows][ld]
+  int64_t ld;
+  uint32_t* hist;           // [rows][2048] first-digit histogram to add into, or null
+};
+
+// Scores every (row, visible token). B requests, max_ctx bounds ctx_len.
+hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st);
+
+struct TopkWs {
+  uint32_t* hist;   // [rows][2048]
+  uint32_t* ctr;    // [rows][4]: {emitted above the first-digit bin, candidates}
+  uint2* cand;      // [rows][cap] (ordered key, position)
+  int32_t cap;
+};
+
+size_t topk_ws_bytes(int rows, int64_t max_len);
+TopkWs topk_ws_carve(void* ws, int rows, int64_t max_len);
+
+// Zero the histogram and counters of `rows` rows. With row_len != null, also
+// writes row_len[row] = ctx_len[row / R] - R + row % R + 1 (visible tokens).
+hipError_t launch_topk_clear(const TopkWs& w, int rows, hipStream_t st, int32_t* row_len = nullptr,
+                             const int32_t* ctx_len = nullptr, int R = 1);
+// First-digit histogram of each row (skipped when the scorer already built it).
+hipError_t launch_topk_hist(const float* scores, int64_t ld, const int32_t* row_len, int rows, int64_t max_len,
+                            const TopkWs& w, hipStream_t st);
+// Selection given the histogram: emits everything above the threshold digit,
+// collects the threshold digit's candidates, then resolves them exactly.
+hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* row_len, int rows, int64_t max_len,
+                              int k, int32_t* idx, const TopkWs& w, hipStream_t st);
+
+struct MlaArgs {
+  const uint16_t* q;        // bf16 [rows][16][576]
+  const int32_t* idx;       // [rows][k]
+  const uint8_t* lat_fp8;   // [num_blocks][64][576]
+  const float* lat_scale;   // [num_blocks][64]
+  const int32_t* block_table;
+  int32_t max_blocks;
+  int32_t R;
+  int32_t k;
+  float sm_scale;
+  uint16_t* out;            // bf16 [rows][16][512]
+  float* lse;               // [rows][16] or null
+};
+
+size_t mla_ws_bytes(int rows, int k, bool split);
+// split == true spreads each row's k positions over several workgroups and
+// merges the partial results by log-sum-exp; false gives each row one workgroup.
+hipError_t launch_sparse_mla(const MlaArgs& a, int rows, bool split, void* ws, hipStream_t st);
+
+}  // namespace dsa

@@ -1,0 +1,179 @@
+"""GPU parity of each stage and of the fused decode against the oracle.
+
+Sizes are small enough for the float64 oracle to finish in seconds while
+spanning several tiles, pages and workgroups, ragged lengths, permuted page
+tables, partial last pages, 1-8 rows per request and both query precisions.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_run import gpu_decode, gpu_mla, gpu_scores, gpu_topk, row_len_of
+from tests.parity import check_attention, check_scores, check_topk_band, check_topk_exact
+from workloads import make_case
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "1x1_8k": dict(B=1, R=1, lengths=[8192], seed=101),
+    "2x4_ragged_perm": dict(B=2, R=4, lengths=[3000, 5001], seed=102, permute_blocks=True),
+    "3x3_short_perm": dict(B=3, R=3, lengths=[700, 64, 4099], seed=103, permute_blocks=True),
+    "1x8": dict(B=1, R=8, lengths=[2500], seed=104),
+    "2x5": dict(B=2, R=5, lengths=[1000, 1300], seed=105),
+    "1x2_tiny": dict(B=1, R=2, lengths=[130], seed=106),
+    "fp8q_1x64": dict(B=1, R=64, lengths=[2048 + 64], seed=107, fp8_query=True),
+    "fp8q_2x7": dict(B=2, R=7, lengths=[5000, 3333], seed=108, fp8_query=True, permute_blocks=True),
+}
+
+
+def _case(name, **over):
+    kw = dict(CASES[name])
+    kw.update(over)
+    print(f"\n[case] {name} {kw}", flush=True)
+    return make_case(name=name, **kw).to("cuda")
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_scores_match_oracle_and_respect_causality(gpu, name):
+    case = _case(name)
+    scores = gpu_scores(case).cpu().numpy()
+    pos = case.positions().numpy()
+    for row in range(case.rows):
+        ref = oracle.row_scores(case, row)
+        check_scores(scores[row, : pos[row] + 1], ref, f"{name} row {row}")
+        assert np.all(np.isnan(scores[row, pos[row] + 1 :])), f"{name} row {row}: wrote past its position"
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("k", [2048, 100])
+def test_topk_exact_on_gpu_scores(gpu, name, k):
+    case = _case(name)
+    scores = gpu_scores(case, sentinel=0.0)
+    idx = gpu_topk(scores, row_len_of(case), k).cpu().numpy()
+    s = scores.cpu().numpy()
+    pos = case.positions().numpy()
+    for row in range(case.rows):
+        check_topk_exact(idx[row], s[row, : pos[row] + 1], k, f"{name} row {row}")
+
+
+@pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "fp8q_2x7"])
+def test_topk_within_band_of_oracle_scores(gpu, name):
+    case = _case(name)
+    scores = gpu_scores(case, sentinel=0.0)
+    idx = gpu_topk(scores, row_len_of(case), case.topk).cpu().numpy()
+    for row in range(case.rows):
+        check_topk_band(idx[row], oracle.row_scores(case, row), case.topk, f"{name} row {row}")
+
+
+def _rows_tensor(rows):
+    L = max(len(r) for r in rows) or 1
+    ld = (L + 63) // 64 * 64
+    t = torch.zeros((len(rows), ld), dtype=torch.float32)
+    for i, r in enumerate(rows):
+        t[i, : len(r)] = torch.as_tensor(r, dtype=torch.float32)
+    return t.cuda(), torch.tensor([len(r) for r in rows], dtype=torch.int32).cuda()
+
+
+def test_topk_edge_cases(gpu):
+    rng = np.random.default_rng(7)
+    rows = [
+        np.zeros(10000),  # one bin, more ties than the candidate buffer: full-row path
+        np.zeros(3000),  # one bin, ties resolved among candidates
+        rng.standard_normal(1500),  # fewer than k: all + padding
+        np.zeros(0),  # empty row: all padding
+        rng.integers(0, 20, 20000).astype(np.float64),  # heavy ties at the threshold
+        np.concatenate([-np.abs(rng.standard_normal(5000)), np.array([-0.0, 0.0] * 50)]),  # signs and zeros
+        rng.standard_normal(70000) * 1e-30,  # tiny magnitudes
+        np.full(4096, 3.25),  # exactly 2k ties
+        np.where(rng.random(300000) < 0.01, 5.0 + rng.random(300000), rng.random(300000)),  # planted cluster
+    ]
+    print("\n[case] topk edge rows", [len(r) for r in rows], flush=True)
+    scores, row_len = _rows_tensor(rows)
+    for k in (2048, 1, 1000):
+        idx = gpu_topk(scores, row_len, k).cpu().numpy()
+        s32 = scores.cpu().numpy()
+        for i, r in enumerate(rows):
+            check_topk_exact(idx[i], s32[i, : len(r)], k, f"edge row {i} k {k}")
+
+
+def test_topk_all_ties_pick_lowest_positions(gpu):
+    scores, row_len = _rows_tensor([np.ones(9000), np.ones(2500)])
+    idx = gpu_topk(scores, row_len, 2048).cpu().numpy()
+    assert sorted(idx[0].tolist()) == list(range(2048))
+    assert sorted(idx[1].tolist()) == list(range(2048))
+
+
+@pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "3x3_short_perm", "2x5", "fp8q_1x64"])
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("k", [2048, 100])
+def test_sparse_mla_matches_oracle_on_gpu_selection(gpu, name, split, k):
+    case = _case(name)
+    scores = gpu_scores(case, sentinel=0.0)
+    idx = gpu_topk(scores, row_len_of(case), k)
+    out, lse = gpu_mla(case, idx, split=split)
+    out, lse, idx_h = out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
+    for row in range(case.rows):
+        ro, rl = oracle.dense_attend_row(case, row, idx_h[row])
+        check_attention(out[row], lse[row], ro, rl, f"{name} row {row} split {split} k {k}")
+
+
+def test_sparse_mla_short_context_equals_dense(gpu):
+    case = _case("1x2_tiny")
+    case2 = make_case(2, 4, [2048, 1000], seed=110, permute_blocks=True).to("cuda")
+    for c in (case, case2):
+        idx = gpu_topk(gpu_scores(c, sentinel=0.0), row_len_of(c), 2048)
+        out, lse = gpu_mla(c, idx)
+        pos = c.positions().numpy()
+        for row in range(c.rows):
+            ro, rl = oracle.dense_attend_row(c, row, np.arange(pos[row] + 1))
+            check_attention(out[row].float().cpu().numpy(), lse[row].cpu().numpy(), ro, rl, f"dense row {row}")
+
+
+def test_sparse_mla_skips_invalid_entries(gpu):
+    case = _case("2x4_ragged_perm")
+    rng = np.random.default_rng(3)
+    pos = case.positions().numpy()
+    k = 300
+    idx = np.full((case.rows, k), -1, np.int32)
+    for row in range(case.rows):
+        if row == 3:
+            continue  # an all-invalid row
+        sel = rng.choice(pos[row] + 1, size=200, replace=False)
+        slots = rng.choice(k, size=200, replace=False)
+        idx[row, slots] = sel
+    idx_t = torch.from_numpy(idx).cuda()
+    for split in (True, False):
+        out, lse = gpu_mla(case, idx_t, split=split)
+        out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+        for row in range(case.rows):
+            ro, rl = oracle.dense_attend_row(case, row, idx[row])
+            check_attention(out[row], lse[row], ro, rl, f"holes row {row} split {split}")
+        assert np.all(out[3] == 0) and np.all(np.isneginf(lse[3]))
+
+
+@pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "3x3_short_perm", "1x8"])
+def test_fused_decode_matches_oracle_and_stages(gpu, name):
+    case = _case(name)
+    out, lse, idx = gpu_decode(case)
+    # stage-by-stage run of the same kernels selects the identical set
+    s_idx = gpu_topk(gpu_scores(case, sentinel=0.0), row_len_of(case), case.topk).cpu().numpy()
+    idx_h = idx.cpu().numpy()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    res = oracle.dsa_rows(case, idx=idx_h)
+    for row in range(case.rows):
+        assert set(idx_h[row].tolist()) == set(s_idx[row].tolist()), f"{name} row {row}: fused vs staged"
+        check_topk_band(idx_h[row], res[row]["scores"], case.topk, f"{name} row {row}")
+        check_attention(out[row], lse[row], res[row]["out"], res[row]["lse"], f"{name} row {row}")
+
+
+def test_fused_decode_selection_is_deterministic(gpu):
+    case = _case("2x4_ragged_perm")
+    a = gpu_decode(case)
+    b = gpu_decode(case)
+    ia, ib = a[2].cpu().numpy(), b[2].cpu().numpy()
+    for row in range(case.rows):
+        assert set(ia[row].tolist()) == set(ib[row].tolist())
+    check_attention(a[0].float().cpu().numpy(), a[1].cpu().numpy(), b[0].float().cpu().numpy(),
+                    b[1].cpu().numpy(), "repeat")
