@@ -1,0 +1,50 @@
+"""Algorithmic HBM bytes of the DSA decode step and of each kernel (for rooflines).
+
+Per request, every context token's 132-byte index key (128 E4M3 values + fp32
+scale) is read once for all of its rows. Per query row: the 2,048 selected
+latent rows (576 E4M3 values + fp32 scale = 580 bytes) and the fp32 score of
+every visible token, written by the scorer and read by the selection (the
+pages count this round trip too: "TokenSpeed Kimi K3.1", section "Sparse
+attention in Kimi K3.1 Pro", about 1 MB of scores at 128K tokens).
+Small per-row terms (queries, head weights, selection, outputs) are included
+where a kernel moves them.
+"""
+
+from __future__ import annotations
+
+KEY_BYTES = 132
+LAT_ROW_BYTES = 580
+SCORE_BYTES = 4
+Q_IDX_BYTES = 32 * 128 * 2 + 32 * 2  # bf16 indexer query + bf16 head weights per row
+Q_MLA_BYTES = 16 * 576 * 2
+OUT_BYTES = 16 * 512 * 2 + 16 * 4
+
+
+def visible(ctx_lens, R):
+    """Visible tokens of every row (position + 1)."""
+    return [L - R + r + 1 for L in ctx_lens for r in range(R)]
+
+
+def scorer_bytes(ctx_lens, R):
+    vis = visible(ctx_lens, R)
+    return sum(ctx_lens) * KEY_BYTES + SCORE_BYTES * sum(vis) + len(vis) * Q_IDX_BYTES
+
+
+def topk_bytes(ctx_lens, R, k):
+    vis = visible(ctx_lens, R)
+    return SCORE_BYTES * sum(vis) + 4 * k * len(vis)
+
+
+def mla_bytes(ctx_lens, R, k):
+    vis = visible(ctx_lens, R)
+    return sum(min(k, v) * (LAT_ROW_BYTES + 4) for v in vis) + len(vis) * (Q_MLA_BYTES + OUT_BYTES)
+
+
+def decode_step_bytes(ctx_lens, R, k):
+    """Keys once per request + per row: selected latents and the score round trip."""
+    vis = visible(ctx_lens, R)
+    return sum(ctx_lens) * KEY_BYTES + sum(min(k, v) * LAT_ROW_BYTES + 2 * SCORE_BYTES * v for v in vis)
+
+
+def scorer_flops(ctx_lens, R, heads=32, dim=128):
+    return 2 * heads * dim * sum(visible(ctx_lens, R))

@@ -83,5 +83,6 @@ def check_attention(out_g, lse_g, out_r, lse_r, what=""):
     if lse_g is not None:
         lg, lr = np.asarray(lse_g, np.float64), np.asarray(lse_r, np.float64)
         both_inf = np.isneginf(lg) & np.isneginf(lr)
-        d = np.where(both_inf, 0.0, np.abs(lg - lr))
+        with np.errstate(invalid="ignore"):
+            d = np.where(both_inf, 0.0, np.abs(lg - lr))
         assert np.all(d <= LSE_TOL * np.maximum(1.0, np.abs(lr))), f"{what}: lse off by {d.max():.3g}"
