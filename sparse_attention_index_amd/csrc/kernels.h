@@ -26,7 +26,8 @@ struct ScoreArgs {
 hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st);
 
 struct TopkWs {
-  uint32_t* hist;   // [rows][2048]
+  uint32_t* hist;   // [rows][2048] first digit of every score
+  uint32_t* hist2;  // [rows][2048] second digit of the first-digit candidates
   uint32_t* ctr;    // [rows][4]: {emitted above the first-digit bin, candidates}
   uint2* cand;      // [rows][cap] (ordered key, position)
   int32_t cap;

@@ -49,11 +49,12 @@ DSA_DEV i32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
 }
 
-__global__ __launch_bounds__(256) void sparse_mla_kernel(MlaArgs a, MlaPart part) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void sparse_mla_kernel(MlaArgs a, MlaPart part) {
   __shared__ __attribute__((aligned(16))) uint8_t lat_s[TK * PITCH];
   __shared__ __attribute__((aligned(16))) __bf16 p_s[kMlaHeads * PP];
+  __shared__ int32_t rowaddr_s[kMaxTopk];
   __shared__ float scl_s[TK];
-  __shared__ long long rowaddr_s[TK];
   __shared__ float red_s[2][4][kMlaHeads];
 
   const int tid = threadIdx.x;
@@ -66,8 +67,18 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(MlaArgs a, MlaPart part
   const int b = row / a.R;
   const int kbeg = split * part.keys_per_split;
   const int kend = min(a.k, kbeg + part.keys_per_split);
+  const int nkeys = max(0, kend - kbeg);
   const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
   const int32_t* sel = a.idx + (size_t)row * a.k;
+
+  // Resolve every selected position of this split to a cache row up front
+  // (-1: skipped), so the tile loop has no dependent index loads.
+  for (int j = tid; j < nkeys; j += 256) {
+    int32_t ra = -1;
+    const int pos = sel[kbeg + j];
+    if (pos >= 0 && pos < a.max_blocks * kBlock) ra = table[pos >> 6] * kBlock + (pos & 63);
+    rowaddr_s[j] = ra;
+  }
 
   // Query fragments: lane holds head n, dims 32s + 8g + [0,8) for step s.
   bf16x8 qa[18];
@@ -87,31 +98,43 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(MlaArgs a, MlaPart part
     m_run[i] = -INFINITY;
     l_run[i] = 0.f;
   }
+  __syncthreads();
 
-  for (int t0 = kbeg; t0 < kend; t0 += TK) {
-    // 1. positions -> cache rows
+  // Each thread moves 9 of the tile's 64 x 36 sixteen-byte chunks; the next
+  // tile's chunks are in flight while the current one is computed.
+  constexpr int kPer = TK * kChunks / 256;
+  u32x4 stage[kPer];
+  float sstage = 0.f;
+  auto load_tile = [&](int t0) {
     if (tid < TK) {
-      const int j = t0 + tid;
-      long long ra = -1;
-      if (j < kend) {
-        const int pos = sel[j];
-        if (pos >= 0 && pos < a.max_blocks * kBlock) ra = (long long)table[pos >> 6] * kBlock + (pos & 63);
-      }
-      rowaddr_s[tid] = ra;
-      scl_s[tid] = ra >= 0 ? a.lat_scale[ra] : 0.f;
+      const int ra = (t0 + tid < nkeys) ? rowaddr_s[t0 + tid] : -1;
+      sstage = ra >= 0 ? a.lat_scale[ra] : 0.f;
     }
-    __syncthreads();
-    for (int c = tid; c < TK * kChunks; c += 256) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + 256 * i;
       const int r = c / kChunks;
       const int q16 = c - r * kChunks;
-      const long long ra = rowaddr_s[r];
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ra >= 0) v = *reinterpret_cast<const u32x4*>(a.lat_fp8 + ra * kLat + q16 * 16);
-      *reinterpret_cast<u32x4*>(lat_s + r * PITCH + q16 * 16) = v;
+      const int ra = (t0 + r < nkeys) ? rowaddr_s[t0 + r] : -1;
+      stage[i] = u32x4{0u, 0u, 0u, 0u};
+      if (ra >= 0) stage[i] = *reinterpret_cast<const u32x4*>(a.lat_fp8 + (size_t)ra * kLat + q16 * 16);
     }
+  };
+  if (nkeys > 0) load_tile(0);
+
+  for (int t0 = 0; t0 < nkeys; t0 += TK) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / kChunks;
+      const int q16 = c - r * kChunks;
+      *reinterpret_cast<u32x4*>(lat_s + r * PITCH + q16 * 16) = stage[i];
+    }
+    if (tid < TK) scl_s[tid] = sstage;
+    if (t0 + TK < nkeys) load_tile(t0 + TK);
     __syncthreads();
 
-    // 2. logits for tokens 16*wave + n, heads 4g + i
+    // QK: logits for tokens 16*wave + n, heads 4g + i
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
     {
       const uint8_t* kr = lat_s + (16 * wave + n) * PITCH + 8 * g;
@@ -122,15 +145,16 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(MlaArgs a, MlaPart part
       }
     }
     const int tok = 16 * wave + n;
-    const bool valid = rowaddr_s[tok] >= 0;
-    const float f = a.sm_scale * scl_s[tok];
+    const bool valid = (t0 + tok < nkeys) && rowaddr_s[t0 + tok] >= 0;
+    const float sc = valid ? scl_s[tok] : 0.f;
+    const float f = a.sm_scale * sc;
     float x[4], mx[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[i] = valid ? sacc[i] * f : -INFINITY;
       mx[i] = x[i];
     }
-    // 3. per-head max and sum over the tile's 64 tokens
+    // online softmax: per-head max and sum over the tile's 64 tokens
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1)
 #pragma unroll
@@ -149,7 +173,7 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(MlaArgs a, MlaPart part
       p[i] = (x[i] == -INFINITY) ? 0.f : __expf(x[i] - mnew);
       m_run[i] = mnew;
       sm[i] = p[i];
-      p_s[h * PP + tok] = (__bf16)(p[i] * scl_s[tok]);
+      p_s[h * PP + tok] = (__bf16)(p[i] * sc);
     }
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1)
@@ -166,7 +190,7 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(MlaArgs a, MlaPart part
       l_run[i] = l_run[i] * alpha[i] + tsum;
     }
 
-    // 4. out[:, 128w .. 128w+128) += P . V
+    // PV: out[:, 128w .. 128w+128) += P . V
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -214,9 +238,10 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(MlaArgs a, MlaPart part
 }
 
 // Merge split partials: out = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}.
+// Grid (8, rows): workgroup x handles dims [64x, 64x + 64) of all 16 heads.
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaPart part, uint16_t* out_bits, float* lse) {
   __shared__ float wgt_s[64][kMlaHeads];  // per split, per head weight e^{m_s - M} / L
-  const int row = blockIdx.x;
+  const int row = blockIdx.y;
   const int S = part.splits;
   const float* ml = part.ml + (size_t)row * S * kMlaHeads * 2;
   if (threadIdx.x < kMlaHeads) {
@@ -232,22 +257,27 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaPart part, uint16_t
       const float m = ml[(s * kMlaHeads + h) * 2];
       wgt_s[s][h] = (L > 0.f && m != -INFINITY) ? __expf(m - M) / L : 0.f;
     }
-    if (lse) lse[(size_t)row * kMlaHeads + h] = L > 0.f ? M + __logf(L) : -INFINITY;
+    if (lse && blockIdx.x == 0) lse[(size_t)row * kMlaHeads + h] = L > 0.f ? M + __logf(L) : -INFINITY;
   }
   __syncthreads();
   __bf16* out = reinterpret_cast<__bf16*>(out_bits) + (size_t)row * kMlaHeads * kV;
   const float* po = part.o + (size_t)row * S * kMlaHeads * kV;
-  for (int e = threadIdx.x; e < kMlaHeads * kV; e += 256) {
-    const int h = e / kV;
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) acc += po[(size_t)s * kMlaHeads * kV + e] * wgt_s[s][h];
-    out[e] = (__bf16)acc;
+  // 16 heads x 64 dims = 1024 outputs, 4 per thread (one float4 per split)
+  const int h = threadIdx.x >> 4;
+  const int d = 64 * blockIdx.x + 4 * (threadIdx.x & 15);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(po + ((size_t)s * kMlaHeads + h) * kV + d);
+    const float wgt = wgt_s[s][h];
+    acc += v * wgt;
   }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[h * kV + d + e] = (__bf16)acc[e];
 }
 
 static int splits_for(int rows, int k) {
   int s = (512 + rows - 1) / rows;  // aim at ~512 workgroups
-  const int max_s = (k + TK * 2 - 1) / (TK * 2);  // at least two tiles per split
+  const int max_s = (k + TK * 4 - 1) / (TK * 4);  // at least four tiles per split
   if (s > max_s) s = max_s;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
@@ -266,13 +296,14 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int rows, bool split, void* ws, h
   part.splits = split ? splits_for(rows, a.k) : 1;
   int kps = (a.k + part.splits - 1) / part.splits;
   kps = (kps + TK - 1) / TK * TK;
+
   part.keys_per_split = kps;
   part.o = reinterpret_cast<float*>(ws);
   part.ml = part.o ? part.o + (size_t)rows * part.splits * kMlaHeads * kV : nullptr;
   hipLaunchKernelGGL(sparse_mla_kernel, dim3(part.splits, rows), dim3(256), 0, st, a, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || part.splits == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(rows), dim3(256), 0, st, part, a.out, a.lse);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(kV / 64, rows), dim3(256), 0, st, part, a.out, a.lse);
   return hipGetLastError();
 }
 
