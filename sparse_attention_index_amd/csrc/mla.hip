@@ -6,17 +6,24 @@
 // Pro on AMD Instinct", model overview) with one fp32 scale; the logits use
 // all 576 dims and the values are the first 512.
 //
-// One workgroup (4 waves) handles one query row (16 heads) over a range of
-// its selected positions, in tiles of 64 positions:
-//  1. the 64 latent rows are gathered through the block table into LDS
-//     (16-byte loads, one padded row per token);
-//  2. QK: wave w computes the 16 heads x 16 tokens [16w, 16w+16) logits with
-//     18 v_mfma_f32_16x16x32_bf16 steps (queries bf16 in VGPRs for the whole
-//     call, latent E4M3 widened to bf16 exactly);
-//  3. online softmax: running max and sum per head, combined across the 4
-//     waves through LDS so that every wave rescales identically;
+// One workgroup (8 waves, one workgroup per CU) handles one query row (16
+// heads) over a range of its selected positions, in tiles of 128 positions:
+//  1. gather: the tile's 128 latent rows (72 KB) are copied from HBM straight
+//     into LDS with global_load_lds_dwordx4 (no VGPR staging) into a ring of
+//     two tile buffers, so the next tile is in flight while one is computed.
+//     Completion is tracked with explicit vmcnt waits and raw s_barrier (a
+//     full __syncthreads would also wait for the copy in flight). Rows are
+//     stored unpadded with their 16-byte chunks rotated by the row index,
+//     which spreads both read patterns below over distinct LDS banks;
+//  2. QK: wave w computes the logits of 16 heads x 16 tokens [16w, 16w+16)
+//     with 18 v_mfma_f32_16x16x32_bf16 steps (queries bf16 in VGPRs for the
+//     whole call, latent E4M3 widened to bf16 exactly);
+//  3. online softmax: per-head tile maxima (DPP row reductions over the 16
+//     tokens a lane group holds) are combined across the 8 waves in LDS so
+//     that every wave rescales identically; row sums stay per wave and are
+//     combined once at the end;
 //  4. PV: probabilities (times the token's latent scale) go to LDS as bf16;
-//     wave w accumulates out dims [128w, 128w+128) with 16x16x32 bf16 MFMA.
+//     wave w accumulates out dims [64w, 64w+64) with 16x16x32 bf16 MFMA.
 //     The V operand needs 8 consecutive tokens of one dim per lane; it comes
 //     from the row-major LDS tile through ds_read_b64_tr_b8, which transposes
 //     an 8x16 byte block across each 16-lane group.
@@ -31,10 +38,13 @@
 
 namespace dsa {
 
-static constexpr int TK = 64;       // tokens per tile
-static constexpr int PITCH = 592;   // LDS bytes per staged latent row (576 + 16 pad)
-static constexpr int PP = 72;       // LDS bf16 per probability row (64 + 8 pad)
-static constexpr int kChunks = kLat / 16;  // 16-byte chunks per latent row
+static constexpr int TK = 128;                        // tokens per tile
+static constexpr int NBUF = 2;                       // tile buffers in the LDS ring
+static constexpr int kChunks = kLat / 16;            // 16-byte chunks per latent row
+static constexpr int TILE_B = TK * kLat;             // 73,728 bytes
+static constexpr int kWaves = 8;
+static constexpr int kPer = TK * kChunks / (64 * kWaves);  // chunk copies per lane per tile (9)
+static constexpr int PP = TK + 8;                    // LDS bf16 per probability row (padded)
 
 struct MlaPart {
   float* o;   // [rows][splits][16][512]
@@ -49,13 +59,67 @@ DSA_DEV i32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void sparse_mla_kernel(MlaArgs a, MlaPart part) {
-  __shared__ __attribute__((aligned(16))) uint8_t lat_s[TK * PITCH];
+// 16 (4) bytes per lane from global memory straight into LDS at
+// lds_base + 16 (4) * lane; lds_base must be the same for the whole wave.
+// Issued through inline asm so that the compiler neither counts these copies
+// nor inserts waits for them: every consumer waits with wait_vmcnt below.
+DSA_DEV void copy16_to_lds(const void* src, void* lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory");
+}
+DSA_DEV void copy4_to_lds(const void* src, void* lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(base) : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+DSA_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global->LDS copies.
+DSA_DEV void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS byte offset of 16-byte chunk j of tile row r (chunks rotated by r).
+DSA_DEV int lat_off(int r, int j) {
+  int jp = j + (r % kChunks);
+  if (jp >= kChunks) jp -= kChunks;
+  return r * kLat + jp * 16;
+}
+
+// Max / sum over the 16 lanes of a DPP row (row_ror 1, 2, 4, 8).
+template <int CTRL>
+DSA_DEV float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+DSA_DEV float row_max16(float v) {
+  v = fmaxf(v, dpp_f<0x121>(v));
+  v = fmaxf(v, dpp_f<0x122>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  return fmaxf(v, dpp_f<0x128>(v));
+}
+DSA_DEV float row_sum16(float v) {
+  v += dpp_f<0x121>(v);
+  v += dpp_f<0x122>(v);
+  v += dpp_f<0x124>(v);
+  return v + dpp_f<0x128>(v);
+}
+
+__global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF][TILE_B];
+  __shared__ __attribute__((aligned(16))) float scl_r[NBUF][TK];
   __shared__ __attribute__((aligned(16))) __bf16 p_s[kMlaHeads * PP];
+  __shared__ float mx_s[kWaves][kMlaHeads];
   __shared__ int32_t rowaddr_s[kMaxTopk];
-  __shared__ float scl_s[TK];
-  __shared__ float red_s[2][4][kMlaHeads];
+  __shared__ uint32_t tile_bad[kMaxTopk / TK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -68,18 +132,20 @@ void sparse_mla_kernel(MlaArgs a, MlaPart part) {
   const int kbeg = split * part.keys_per_split;
   const int kend = min(a.k, kbeg + part.keys_per_split);
   const int nkeys = max(0, kend - kbeg);
+  const int ntiles = (nkeys + TK - 1) / TK;
   const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
   const int32_t* sel = a.idx + (size_t)row * a.k;
 
   // Resolve every selected position of this split to a cache row up front
-  // (-1: skipped), so the tile loop has no dependent index loads.
-  for (int j = tid; j < nkeys; j += 256) {
+  // (-1: skipped; also the padding of the last tile).
+  for (int j = tid; j < ntiles * TK; j += 512) {
     int32_t ra = -1;
-    const int pos = sel[kbeg + j];
-    if (pos >= 0 && pos < a.max_blocks * kBlock) ra = table[pos >> 6] * kBlock + (pos & 63);
+    if (j < nkeys) {
+      const int pos = sel[kbeg + j];
+      if (pos >= 0 && pos < a.max_blocks * kBlock) ra = table[pos >> 6] * kBlock + (pos & 63);
+    }
     rowaddr_s[j] = ra;
   }
-
   // Query fragments: lane holds head n, dims 32s + 8g + [0,8) for step s.
   bf16x8 qa[18];
   {
@@ -88,128 +154,144 @@ void sparse_mla_kernel(MlaArgs a, MlaPart part) {
 #pragma unroll
     for (int s = 0; s < 18; ++s) qa[s] = qp[4 * s];
   }
+  __syncthreads();  // rowaddr_s complete
+  if (tid < ntiles) {
+    uint32_t bad = 0;
+    for (int r = 0; r < TK; ++r) bad |= (uint32_t)(rowaddr_s[tid * TK + r] < 0);
+    tile_bad[tid] = bad;
+  }
 
-  f32x4 o[8];
+  // This lane's copy map, the same for every tile: chunk slot
+  // c_i = 64 (9 wave + i) + lane of the tile holds row r_i, global chunk j_i.
+  int cr[kPer], cj[kPer];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kPer; ++i) {
+    const int c = 64 * (kPer * wave + i) + lane;
+    cr[i] = c / kChunks;
+    int j = c - cr[i] * kChunks - (cr[i] % kChunks);
+    if (j < 0) j += kChunks;
+    cj[i] = j;
+  }
+  // Copy tile t into ring slot t % 2 (skipped rows read row 0 and are zeroed
+  // after arrival). Waves 0 and 1 also copy the tile's 128 scales.
+  auto issue = [&](int t) {
+    uint8_t* dst = ring[t % NBUF];
+    const int rb = t * TK;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int ra = rowaddr_s[rb + cr[i]];
+      const uint8_t* src = a.lat_fp8 + (size_t)(ra >= 0 ? ra : 0) * kLat + cj[i] * 16;
+      copy16_to_lds(src, dst + 1024 * (kPer * wave + i));
+    }
+    if (wave < 2) {
+      const int ra = rowaddr_s[rb + 64 * wave + lane];
+      copy4_to_lds(a.lat_scale + (ra >= 0 ? ra : 0), &scl_r[t % NBUF][64 * wave]);
+    }
+  };
+
+  f32x4 o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[4], l_run[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     m_run[i] = -INFINITY;
     l_run[i] = 0.f;
   }
-  __syncthreads();
+  wait_vmcnt<0>();  // query fragments in VGPRs before any copy is counted
+  if (ntiles > 0) issue(0);
 
-  // Each thread moves 9 of the tile's 64 x 36 sixteen-byte chunks; the next
-  // tile's chunks are in flight while the current one is computed.
-  constexpr int kPer = TK * kChunks / 256;
-  u32x4 stage[kPer];
-  float sstage = 0.f;
-  auto load_tile = [&](int t0) {
-    if (tid < TK) {
-      const int ra = (t0 + tid < nkeys) ? rowaddr_s[t0 + tid] : -1;
-      sstage = ra >= 0 ? a.lat_scale[ra] : 0.f;
-    }
+  for (int t = 0; t < ntiles; ++t) {
+    uint8_t* tile = ring[t % NBUF];
+    float* scl = scl_r[t % NBUF];
+    wait_vmcnt<0>();  // tile t is the only copy in flight
+    if (tile_bad[t]) {  // zero the skipped rows this lane copied
+      const int rb = t * TK;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / kChunks;
-      const int q16 = c - r * kChunks;
-      const int ra = (t0 + r < nkeys) ? rowaddr_s[t0 + r] : -1;
-      stage[i] = u32x4{0u, 0u, 0u, 0u};
-      if (ra >= 0) stage[i] = *reinterpret_cast<const u32x4*>(a.lat_fp8 + (size_t)ra * kLat + q16 * 16);
+      for (int i = 0; i < kPer; ++i)
+        if (rowaddr_s[rb + cr[i]] < 0)
+          *reinterpret_cast<u32x4*>(tile + 16 * (64 * (kPer * wave + i) + lane)) = u32x4{0u, 0u, 0u, 0u};
+      if (wave < 2 && rowaddr_s[rb + 64 * wave + lane] < 0) scl[64 * wave + lane] = 0.f;
     }
-  };
-  if (nkeys > 0) load_tile(0);
-
-  for (int t0 = 0; t0 < nkeys; t0 += TK) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / kChunks;
-      const int q16 = c - r * kChunks;
-      *reinterpret_cast<u32x4*>(lat_s + r * PITCH + q16 * 16) = stage[i];
-    }
-    if (tid < TK) scl_s[tid] = sstage;
-    if (t0 + TK < nkeys) load_tile(t0 + TK);
-    __syncthreads();
+    lds_barrier();  // tile t complete in LDS for all waves; tile t-1 fully consumed
+    if (t + 1 < ntiles) issue(t + 1);  // into the slot tile t-1 used
 
     // QK: logits for tokens 16*wave + n, heads 4g + i
+    const int tok = 16 * wave + n;
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
     {
-      const uint8_t* kr = lat_s + (16 * wave + n) * PITCH + 8 * g;
+      int jp = (g >> 1) + (tok % kChunks);
+      if (jp >= kChunks) jp -= kChunks;
+      const uint8_t* kr = tile + tok * kLat + 8 * (g & 1);
 #pragma unroll
       for (int s = 0; s < 18; ++s) {
-        const uint2 v = *reinterpret_cast<const uint2*>(kr + 32 * s);
+        const uint2 v = *reinterpret_cast<const uint2*>(kr + 16 * jp);
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], e4m3x8_bf16(v.x, v.y), sacc, 0, 0, 0);
+        jp += 2;
+        if (jp >= kChunks) jp -= kChunks;
       }
     }
-    const int tok = 16 * wave + n;
-    const bool valid = (t0 + tok < nkeys) && rowaddr_s[t0 + tok] >= 0;
-    const float sc = valid ? scl_s[tok] : 0.f;
+    const bool valid = rowaddr_s[t * TK + tok] >= 0;
+    const float sc = scl[tok];
     const float f = a.sm_scale * sc;
-    float x[4], mx[4];
+    float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[i] = valid ? sacc[i] * f : -INFINITY;
-      mx[i] = x[i];
+      const float mx = row_max16(x[i]);
+      if (n == 0) mx_s[wave][4 * g + i] = mx;
     }
-    // online softmax: per-head max and sum over the tile's 64 tokens
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], off));
-    if (n == 0)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red_s[0][wave][4 * g + i] = mx[i];
-    __syncthreads();
-    float alpha[4], p[4], sm[4];
+    lds_barrier();
+    float alpha[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * g + i;
-      const float tmax = fmaxf(fmaxf(red_s[0][0][h], red_s[0][1][h]), fmaxf(red_s[0][2][h], red_s[0][3][h]));
+      float tmax = mx_s[0][h];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) tmax = fmaxf(tmax, mx_s[w][h]);
       const float mnew = fmaxf(m_run[i], tmax);
       alpha[i] = (mnew == -INFINITY) ? 1.f : __expf(m_run[i] - mnew);
-      p[i] = (x[i] == -INFINITY) ? 0.f : __expf(x[i] - mnew);
+      const float p = (x[i] == -INFINITY) ? 0.f : __expf(x[i] - mnew);
       m_run[i] = mnew;
-      sm[i] = p[i];
-      p_s[h * PP + tok] = (__bf16)(p[i] * sc);
+      p_s[h * PP + tok] = (__bf16)(p * sc);
+      l_run[i] = l_run[i] * alpha[i] + row_sum16(p);
     }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm[i] += __shfl_xor(sm[i], off);
-    if (n == 0)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red_s[1][wave][4 * g + i] = sm[i];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * g + i;
-      const float tsum = red_s[1][0][h] + red_s[1][1][h] + red_s[1][2][h] + red_s[1][3][h];
-      l_run[i] = l_run[i] * alpha[i] + tsum;
-    }
+    lds_barrier();
 
-    // PV: out[:, 128w .. 128w+128) += P . V
+    // PV: out[:, 64w .. 64w+64) += P . V over the tile's 128 tokens
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < TK / 32; ++s) {
       const bf16x8 pa = *reinterpret_cast<const bf16x8*>(p_s + n * PP + 32 * s + 8 * g);
-      const uint8_t* vrow = lat_s + (32 * s + 8 * g + (n >> 1)) * PITCH + 128 * wave + 8 * (n & 1);
+      const int r = 32 * s + 8 * g + (n >> 1);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const i32x2 v = lds_read_tr8(vrow + 16 * j);
+      for (int j = 0; j < 4; ++j) {
+        const i32x2 v = lds_read_tr8(tile + lat_off(r, 4 * wave + j) + 8 * (n & 1));
         o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]), o[j], 0, 0,
                                                        0);
       }
     }
-    __syncthreads();
   }
 
-  // Output: lane holds dims 128w + 16j + n, heads 4g + i.
+  // Row sums: every wave holds the part of its own tokens.
+  __syncthreads();
+  if (n == 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx_s[wave][4 * g + i] = l_run[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) l += mx_s[w][h];
+    l_run[i] = l;
+  }
+
+  // Output: lane holds dims 64w + 16j + n, heads 4g + i.
   if (part.splits == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -217,7 +299,7 @@ void sparse_mla_kernel(MlaArgs a, MlaPart part) {
       const float inv = l_run[i] > 0.f ? 1.f / l_run[i] : 0.f;
       __bf16* orow = reinterpret_cast<__bf16*>(a.out) + ((size_t)row * kMlaHeads + h) * kV;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) orow[128 * wave + 16 * j + n] = (__bf16)(o[j][i] * inv);
+      for (int j = 0; j < 4; ++j) orow[64 * wave + 16 * j + n] = (__bf16)(o[j][i] * inv);
       if (a.lse && wave == 0 && n == 0)
         a.lse[(size_t)row * kMlaHeads + h] = l_run[i] > 0.f ? m_run[i] + __logf(l_run[i]) : -INFINITY;
     }
@@ -228,7 +310,7 @@ void sparse_mla_kernel(MlaArgs a, MlaPart part) {
       const int h = 4 * g + i;
       float* orow = part.o + (base * kMlaHeads + h) * kV;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) orow[128 * wave + 16 * j + n] = o[j][i];
+      for (int j = 0; j < 4; ++j) orow[64 * wave + 16 * j + n] = o[j][i];
       if (wave == 0 && n == 0) {
         part.ml[(base * kMlaHeads + h) * 2 + 0] = m_run[i];
         part.ml[(base * kMlaHeads + h) * 2 + 1] = l_run[i];
@@ -276,8 +358,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaPart part, uint16_t
 }
 
 static int splits_for(int rows, int k) {
-  int s = (512 + rows - 1) / rows;  // aim at ~512 workgroups
-  const int max_s = (k + TK * 4 - 1) / (TK * 4);  // at least four tiles per split
+  int s = (256 + rows - 1) / rows;  // aim at one workgroup per CU
+  const int max_s = (k + TK - 1) / TK;  // at least one tile per split
   if (s > max_s) s = max_s;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
@@ -300,7 +382,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int rows, bool split, void* ws, h
   part.keys_per_split = kps;
   part.o = reinterpret_cast<float*>(ws);
   part.ml = part.o ? part.o + (size_t)rows * part.splits * kMlaHeads * kV : nullptr;
-  hipLaunchKernelGGL(sparse_mla_kernel, dim3(part.splits, rows), dim3(256), 0, st, a, part);
+  hipLaunchKernelGGL(sparse_mla_kernel, dim3(part.splits, rows), dim3(512), 0, st, a, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || part.splits == 1) return e;
   hipLaunchKernelGGL(mla_combine_kernel, dim3(kV / 64, rows), dim3(256), 0, st, part, a.out, a.lse);
@@ -308,3 +390,4 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int rows, bool split, void* ws, h
 }
 
 }  // namespace dsa
+
