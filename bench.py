@@ -11,8 +11,13 @@ hit in the 256 MB Infinity Cache.
 
 Prints one JSON line. `value` is context tokens scanned per second (the sum
 of the requests' context lengths per step over the step time); rows/s, the
-whole-step HBM fraction, per-stage times, the dominant kernel's roofline and a
-float64 CPU oracle baseline are added beside it.
+whole-step HBM fraction, per-stage times, the roofline of the dominant kernel
+(the indexer scorer, timed over back-to-back launches with HIP events on its
+stream) and a float64 CPU oracle baseline are added beside it.
+
+`--workload prefill_4096_on_128k` measures a prefill chunk instead (FP8-query
+indexer over the causal history, per-row top-k, sparse MLA prefill) and reports
+the scorer against the FP8 MFMA peak.
 """
 
 from __future__ import annotations
@@ -29,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
 MALL_BYTES = 256 << 20
 METRIC = "DSA decode: context tokens scanned/s + query rows/s; % of HBM roofline"
 
@@ -36,7 +42,7 @@ METRIC = "DSA decode: context tokens scanned/s + query rows/s; % of HBM roofline
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200, help="timed steps")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_16x4_32k")
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough to exceed 3x the MALL)")
@@ -54,38 +60,58 @@ def kernel_source_hash(names):
 
 
 def counters_for(kernel_file, workload):
-    """HBM traffic measured by rocprofv3 counters for this kernel source, if current."""
-    path = os.path.join(ROOT, "profiles", "counters.json")
+    """HBM bytes per launch of a kernel, from the committed rocprofv3 counter summary.
+
+    profiles/hbm_counters.txt holds one line per (kernel source, workload):
+    `<file> <workload> <kernel> <source hash> <fetch bytes> <write bytes>` (already scaled by
+    the copy-kernel calibration). The entry counts only while the kernel source is unchanged.
+    """
+    path = os.path.join(ROOT, "profiles", "hbm_counters.txt")
     if not os.path.exists(path):
         return None
+    want = kernel_source_hash([kernel_file, "common.h"])
     with open(path) as f:
-        data = json.load(f)
-    entry = data.get(f"{kernel_file}:{workload}")
-    if not entry or entry.get("source_hash") != kernel_source_hash([kernel_file, "common.h"]):
-        return None
-    return entry.get("bytes_per_launch")
+        for line in f:
+            parts = line.split()
+            if len(parts) == 6 and not line.startswith("#") and parts[0] == kernel_file and parts[1] == workload:
+                if parts[3] != want:
+                    return None
+                return float(parts[4]) + float(parts[5])
+    return None
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return 1
 
 
 def cpu_baseline(workload_name, budget_s):
     """The float64 oracle (as it stands) on a bounded sample of the same workload."""
-    import numpy as np  # noqa: F401
-
     import oracle
     from workloads import case_config, make_case
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     cfg = case_config(workload_name)
     R, lens = cfg["R"], cfg["lengths"]
+    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query")}
+    if R > 64:  # prefill chunk: one request, sample its query rows
+        case = make_case(1, R, lens[:1], seed=cfg["seed"] + 1000, **kw)
+        rows, spent = 0, 0.0
+        step = max(1, R // 64)
+        while rows < R and (spent < budget_s or rows == 0):
+            t0 = time.perf_counter()
+            oracle.dsa_rows(case, rows=[(rows * step) % R])
+            spent += time.perf_counter() - t0
+            rows += 1
+        return {"value": rows / spent, "unit": "rows/s", "cores": _threads(), "kind": "oracle",
+                "sample": f"{rows} of {R} query rows (spread over the chunk), all stages, numpy float64 "
+                          f"on the host, {spent:.1f} s"}
     done, tokens, rows, spent = 0, 0, 0, 0.0
     while done < len(lens) and (spent < budget_s or done == 0):
-        case = make_case(1, R, [lens[done]], seed=cfg["seed"] + 1000 + done,
-                         permute_blocks=cfg.get("permute_blocks", False),
-                         plant_frac=cfg.get("plant_frac", 0.0), fp8_query=cfg.get("fp8_query", False))
+        case = make_case(1, R, [lens[done]], seed=cfg["seed"] + 1000 + done, **kw)
         t0 = time.perf_counter()
         oracle.dsa_rows(case)
         spent += time.perf_counter() - t0
@@ -96,29 +122,46 @@ def cpu_baseline(workload_name, budget_s):
         "value": tokens / spent,
         "unit": "tokens/s",
         "rows_per_s": rows / spent,
-        "cores": threads,
+        "cores": _threads(),
         "kind": "oracle",
         "sample": f"{done} of {len(lens)} requests ({rows} rows, context {lens[0]}), all stages, "
                   f"numpy float64 on the host, {spent:.1f} s",
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the DSA path here has no "
-              "multi-GPU mode. Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+def time_launches(torch, fn, n):
+    """Average time of n back-to-back calls of fn(i) on the current stream, from HIP events
+    recorded on that stream (the host stays ahead: the GPU is kept busy while it enqueues)."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(5e7))
+    ev0.record()
+    for i in range(n):
+        fn(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    return 1e3 * ev0.elapsed_time(ev1) / n
 
-    import torch
 
-    import sparse_attention_index_amd as dsa
-    from sparse_attention_index_amd import traffic
-    from workloads import case_config, make_case
+def stage_times(torch, stages, n):
+    """Per-stage event times when the stages run in order, repeated n times."""
+    evs = {s: [] for s, _ in stages}
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    for i in range(n):
+        for s, fn in stages:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(i)
+            e1.record()
+            evs[s].append((e0, e1))
+    torch.cuda.synchronize()
+    return {s: 1e3 * sum(a.elapsed_time(b) for a, b in v) / n for s, v in evs.items()}
 
-    dsa.load()
-    torch.cuda.set_device(0)
-    cfg = case_config(args.workload)
+
+def run_decode(args, torch, dsa, traffic, cfg):
+    from workloads import make_case
+
     B, R, lens = cfg["B"], cfg["R"], cfg["lengths"]
     k = 2048
     rows = B * R
@@ -176,7 +219,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / steps_run
 
-    # ---- per-stage kernel times (stage-wise entry points, same inputs, host kept ahead of the GPU)
+    # ---- stage-wise entry points on the same inputs
     ld = (max_ctx + 63) // 64 * 64
     scores = torch.empty((rows, ld), dtype=torch.float32, device="cuda")
     row_len = [(c.positions() + 1).to(torch.int32).cuda() for c in cases]
@@ -184,41 +227,29 @@ def main():
     mla_ws_n = dsa.dsa_workspace_size(dsa.DSA_WS_MLA_DECODE, rows, 0, k)
     mla_ws = dsa.workspace(mla_ws_n) if mla_ws_n else None
     n_stage = min(args.steps, 100)
-    names = ("score", "topk", "attend")
-    evs = {s: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_stage)]
-           for s in names}
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(2e8))  # keep the GPU busy while the host enqueues every stage call
-    for i in range(n_stage):
-        c, j = cases[i % nsets], i % nsets
-        e = evs["score"][i]
-        e[0].record()
-        dsa.dsa_index_score(batches[j], caches[j], c.q_idx, c.w, scores)
-        e[1].record()
-        e = evs["topk"][i]
-        e[0].record()
-        dsa.dsa_topk(scores, row_len[j], k, idx, tk_ws)
-        e[1].record()
-        e = evs["attend"][i]
-        e[0].record()
-        dsa.dsa_sparse_mla_decode(batches[j], caches[j], c.q_mla, idx, c.sm_scale, out, lse, mla_ws)
-        e[1].record()
-    torch.cuda.synchronize()
-    stage_us = {s: 1e3 * sum(a.elapsed_time(b) for a, b in evs[s]) / n_stage for s in names}
 
-    # ---- dominant kernel roofline: the indexer scorer (one kernel per call) or sparse MLA
-    alg = {
-        "score": (traffic.scorer_bytes(lens, R), "score.hip", "score_kernel"),
-        "attend": (traffic.mla_bytes(lens, R, k), "mla.hip", "sparse_mla_kernel"),
-    }
-    dom = max(("score", "attend"), key=lambda s: stage_us[s])
-    dom_bytes, dom_file, dom_kernel = alg[dom]
-    achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
-    measured = counters_for(dom_file, args.workload)
+    def score(i):
+        j = i % nsets
+        dsa.dsa_index_score(batches[j], caches[j], cases[j].q_idx, cases[j].w, scores)
+
+    def topk(i):
+        dsa.dsa_topk(scores, row_len[i % nsets], k, idx, tk_ws)
+
+    def attend(i):
+        j = i % nsets
+        dsa.dsa_sparse_mla_decode(batches[j], caches[j], cases[j].q_mla, idx, cases[j].sm_scale, out, lse, mla_ws)
+
+    stage_us = stage_times(torch, [("score", score), ("topk", topk), ("attend", attend)], n_stage)
+
+    # ---- dominant kernel: the indexer scorer (one kernel per dsa_index_score call; its share
+    # of the step grows with context). Average launch time of back-to-back launches.
+    score_us = time_launches(torch, score, n_stage)
+    dom_bytes = traffic.scorer_bytes(lens, R)
+    achieved = dom_bytes / (score_us * 1e-6) / 1e9
 
     tokens = sum(lens)
     sec = ms_step * 1e-3
-    result = {
+    return {
         "metric": METRIC,
         "value": tokens / sec,
         "unit": "tokens/s",
@@ -249,16 +280,119 @@ def main():
         "wall_s": wall,
         "roofline": {
             "bound": "hbm",
-            "kernel": dom_kernel,
+            "kernel": "score_kernel",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured,
+            "traffic": counters_for("score.hip", args.workload),
             "algorithmic_bytes": dom_bytes,
-            "avg_launch_us": stage_us[dom],
+            "avg_launch_us": score_us,
         },
     }
+
+
+def run_prefill(args, torch, dsa, traffic, cfg):
+    """Prefill chunk: FP8-query indexer over the whole causal history, per-row top-k, sparse MLA."""
+    from workloads import make_case
+
+    R, L = cfg["R"], cfg["lengths"][0]
+    k = 2048
+    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query")}
+    case = make_case(1, R, [L], seed=cfg["seed"], device="cuda", name=args.workload, **kw)
+    batch, cache = dsa.Batch.of(case), dsa.Cache.of(case)
+    ld = (L + 63) // 64 * 64
+    scores = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+    row_len = (case.positions() + 1).to(torch.int32).cuda()
+    tk_ws = dsa.workspace(dsa.dsa_workspace_size(dsa.DSA_WS_TOPK, R, ld, k))
+    idx = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((R, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, 16), dtype=torch.float32, device="cuda")
+
+    def score(i):
+        dsa.dsa_index_score(batch, cache, case.q_idx, case.w, scores, q_scale=case.q_idx_scale)
+
+    def topk(i):
+        dsa.dsa_topk(scores, row_len, k, idx, tk_ws)
+
+    def attend(i):
+        dsa.dsa_sparse_mla_prefill(batch, cache, case.q_mla, idx, case.sm_scale, out, lse)
+
+    def step(i):
+        score(i)
+        topk(i)
+        attend(i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    n_stage = min(args.steps, 10)
+    stage_us = stage_times(torch, [("score", score), ("topk", topk), ("attend", attend)], n_stage)
+    score_us = time_launches(torch, score, n_stage)
+    flops = traffic.scorer_flops([L], R)
+    tflops = flops / (score_us * 1e-6) / 1e12
+    sec = ms_step * 1e-3
+    return {
+        "metric": "DSA prefill chunk: query rows/s; indexer % of FP8 MFMA roofline",
+        "value": R / sec,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": R, "history": L - R, "keys": L, "topk": k,
+                   "indexer": "FP8 q (row scale) x E4M3 keys, 32h x 128d", "mla": "16h x 576 -> 512"},
+        "context_tokens_per_s": L / sec,
+        "stages_us": stage_us,
+        "wall_s": wall,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "score_kernel",
+            "achieved": tflops,
+            "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / FP8_PEAK_TFLOPS,
+            "traffic": counters_for("score.hip", args.workload),
+            "algorithmic_flops": flops,
+            "avg_launch_us": score_us,
+        },
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the DSA path here has no "
+              "multi-GPU mode. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_attention_index_amd as dsa
+    from sparse_attention_index_amd import traffic
+    from workloads import case_config
+
+    dsa.load()
+    torch.cuda.set_device(0)
+    cfg = case_config(args.workload)
+    if cfg["R"] > 64:
+        result = run_prefill(args, torch, dsa, traffic, cfg)
+    else:
+        result = run_decode(args, torch, dsa, traffic, cfg)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
     print(json.dumps(result), flush=True)
