@@ -51,6 +51,32 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _need(t, name: str, dtypes, numel: int = 0, contiguous: bool = True):
+    """Tensor checks the C ABI cannot make (it sees raw pointers): device, dtype, size, layout."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF16 = (torch.bfloat16,)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+_CODES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _check_scores(scores, rows: int, cols: int):
+    _need(scores, "scores", _F32, contiguous=False)
+    if scores.dim() != 2 or scores.stride(1) != 1 or scores.shape[0] < rows or scores.shape[1] < cols:
+        raise ValueError(f"scores must be fp32 [>= {rows}, >= {cols}] with unit column stride")
+
+
 def _check(status: int, what: str):
     if status != DSA_OK:
         lib = load()
@@ -63,6 +89,17 @@ class Cache:
     lat_fp8 u8 [nb,64,576], lat_scale f32 [nb,64]."""
 
     def __init__(self, key_fp8, key_scale, lat_fp8, lat_scale):
+        if key_fp8 is not None:
+            _need(key_fp8, "key_fp8", _CODES)
+            nb = key_fp8.shape[0]
+            if tuple(key_fp8.shape[1:]) != (64, 128):
+                raise ValueError("key_fp8 must be [num_blocks, 64, 128]")
+            _need(key_scale, "key_scale", _F32, nb * 64)
+        if lat_fp8 is not None:
+            _need(lat_fp8, "lat_fp8", _CODES)
+            if tuple(lat_fp8.shape[1:]) != (64, 576):
+                raise ValueError("lat_fp8 must be [num_blocks, 64, 576]")
+            _need(lat_scale, "lat_scale", _F32, lat_fp8.shape[0] * 64)
         self.key_fp8, self.key_scale, self.lat_fp8, self.lat_scale = key_fp8, key_scale, lat_fp8, lat_scale
         nb = key_fp8.shape[0] if key_fp8 is not None else lat_fp8.shape[0]
         self.c = _lib.DsaCacheC(
@@ -79,6 +116,10 @@ class Batch:
     max_ctx is a host-side bound of ctx_len."""
 
     def __init__(self, rows_per_request: int, ctx_len, block_table, max_ctx: int):
+        _need(ctx_len, "ctx_len", _I32)
+        _need(block_table, "block_table", _I32)
+        if block_table.dim() != 2 or block_table.shape[0] != ctx_len.shape[0]:
+            raise ValueError("block_table must be [num_requests, max_blocks]")
         self.ctx_len, self.block_table = ctx_len, block_table
         self.R = int(rows_per_request)
         self.B = int(ctx_len.shape[0])
@@ -107,6 +148,14 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 def dsa_index_score(batch: Batch, cache: Cache, q, w, scores, q_scale=None, stream=None):
     """scores[row, s] for every visible token s (fp32 [rows, ld])."""
     q_dtype = DSA_Q_FP8 if q_scale is not None else DSA_Q_BF16
+    rows = batch.rows
+    if q_scale is None:
+        _need(q, "q", _BF16, rows * 32 * 128)
+    else:
+        _need(q, "q", _CODES, rows * 32 * 128)
+        _need(q_scale, "q_scale", _F32, rows)
+    _need(w, "w", _BF16, rows * 32)
+    _check_scores(scores, rows, batch.max_ctx)
     st = load().dsa_index_score(
         ctypes.byref(batch.c), ctypes.byref(cache.c), _ptr(q), q_dtype, _ptr(q_scale), _ptr(w),
         _ptr(scores), int(scores.stride(0)), _stream(stream),
@@ -117,6 +166,11 @@ def dsa_index_score(batch: Batch, cache: Cache, q, w, scores, q_scale=None, stre
 def dsa_topk(scores, row_len, k: int, idx, ws, stream=None):
     """idx[row, :] = positions of the k largest scores[row, :row_len[row]] (set; -1 padded)."""
     rows = int(scores.shape[0])
+    _check_scores(scores, rows, 1)
+    _need(row_len, "row_len", _I32, rows)
+    _need(idx, "idx", _I32, rows * int(k))
+    if ws is not None:
+        _need(ws, "ws", (torch.uint8,))
     st = load().dsa_topk(
         _ptr(scores), int(scores.stride(0)), _ptr(row_len), rows, int(k), _ptr(idx),
         _ptr(ws), int(ws.numel()) if ws is not None else 0, _stream(stream),
@@ -125,6 +179,18 @@ def dsa_topk(scores, row_len, k: int, idx, ws, stream=None):
 
 
 def _mla(fn, name, batch, cache, q, idx, softmax_scale, out, lse, ws, stream):
+    rows = batch.rows
+    _need(q, "q", _BF16)
+    if q.dim() != 3 or q.shape[0] != rows or q.shape[2] != 576:
+        raise ValueError(f"q must be bf16 [{rows}, heads, 576]")
+    _need(idx, "idx", _I32)
+    if idx.dim() != 2 or idx.shape[0] != rows:
+        raise ValueError(f"idx must be int32 [{rows}, k]")
+    _need(out, "out", _BF16, rows * int(q.shape[1]) * 512)
+    if lse is not None:
+        _need(lse, "lse", _F32, rows * int(q.shape[1]))
+    if ws is not None:
+        _need(ws, "ws", (torch.uint8,))
     st = fn(
         ctypes.byref(batch.c), ctypes.byref(cache.c), _ptr(q), int(q.shape[1]), _ptr(idx), int(idx.shape[1]),
         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), int(ws.numel()) if ws is not None else 0,
@@ -145,6 +211,19 @@ def dsa_sparse_mla_prefill(batch, cache, q, idx, softmax_scale, out, lse=None, w
 
 def dsa_decode(batch, cache, q_idx, w, q_mla, k, softmax_scale, out, lse=None, idx_out=None, ws=None,
                stream=None):
+    rows = batch.rows
+    _need(q_idx, "q_idx", _BF16, rows * 32 * 128)
+    _need(w, "w", _BF16, rows * 32)
+    _need(q_mla, "q_mla", _BF16)
+    if q_mla.dim() != 3 or q_mla.shape[0] != rows or q_mla.shape[2] != 576:
+        raise ValueError(f"q_mla must be bf16 [{rows}, heads, 576]")
+    _need(out, "out", _BF16, rows * int(q_mla.shape[1]) * 512)
+    if lse is not None:
+        _need(lse, "lse", _F32, rows * int(q_mla.shape[1]))
+    if idx_out is not None:
+        _need(idx_out, "idx_out", _I32, rows * int(k))
+    if ws is not None:
+        _need(ws, "ws", (torch.uint8,))
     st = load().dsa_decode(
         ctypes.byref(batch.c), ctypes.byref(cache.c), _ptr(q_idx), _ptr(w), _ptr(q_mla), int(q_mla.shape[1]),
         int(k), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws),

@@ -99,14 +99,11 @@ size_t decode_ws_parts(int32_t rows, int64_t max_ctx, int32_t k, DecodeWs* out, 
 }
 
 int32_t run_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows, int32_t k, int32_t* idx,
-                 void* ws, bool have_hist, hipStream_t st) {
+                 void* ws, bool cleared, hipStream_t st) {
   const TopkWs w = topk_ws_carve(ws, rows, ld);
-  if (!have_hist) {
-    int32_t r = hip_status(launch_topk_clear(w, rows, st), "topk clear");
-    if (r) return r;
-    r = hip_status(launch_topk_hist(scores, ld, row_len, rows, ld, w, st), "topk hist");
-    if (r) return r;
-  }
+  int32_t r;
+  if (!cleared && (r = hip_status(launch_topk_clear(w, rows, st), "topk clear"))) return r;
+  if ((r = hip_status(launch_topk_hist(scores, ld, row_len, rows, ld, w, st), "topk hist"))) return r;
   return hip_status(launch_topk_select(scores, ld, row_len, rows, ld, k, idx, w, st), "topk select");
 }
 
@@ -160,7 +157,6 @@ int32_t dsa_index_score(const dsa_batch* batch, const dsa_cache* cache, const vo
   a.R = batch->rows_per_request;
   a.scores = scores;
   a.ld = ld;
-  a.hist = nullptr;
   return hip_status(launch_index_score(a, batch->num_requests, batch->max_ctx, q_dtype == DSA_Q_FP8,
                                        static_cast<hipStream_t>(stream)),
                     "index score");
@@ -228,7 +224,7 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
   if ((r = hip_status(launch_topk_clear(tw, rows, st, p.row_len, batch->ctx_len, batch->rows_per_request),
                       "decode clear")))
     return r;
-  // 2. score, building the first-digit histogram on the fly
+  // 2. score
   ScoreArgs a;
   a.q = q_idx;
   a.q_scale = nullptr;
@@ -241,10 +237,9 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
   a.R = batch->rows_per_request;
   a.scores = p.scores;
   a.ld = ld;
-  a.hist = tw.hist;
   if ((r = hip_status(launch_index_score(a, batch->num_requests, batch->max_ctx, false, st), "decode score")))
     return r;
-  // 3. select
+  // 3. select: first-digit histogram, threshold, winners
   if ((r = run_topk(p.scores, ld, p.row_len, rows, k, idx, p.topk, true, st))) return r;
   // 4. attend
   return run_mla(batch, cache, q_mla, idx, k, softmax_scale, out, lse, p.mla, true, st);

@@ -19,7 +19,6 @@ struct ScoreArgs {
   int32_t R;                // rows per request
   float* scores;            // [rows][ld]
   int64_t ld;
-  uint32_t* hist;           // [rows][2048] first-digit histogram to add into, or null
 };
 
 // Scores every (row, visible token). B requests, max_ctx bounds ctx_len.

@@ -59,35 +59,6 @@ DSA_DEV i32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
 }
 
-// 16 (4) bytes per lane from global memory straight into LDS at
-// lds_base + 16 (4) * lane; lds_base must be the same for the whole wave.
-// Issued through inline asm so that the compiler neither counts these copies
-// nor inserts waits for them: every consumer waits with wait_vmcnt below.
-DSA_DEV void copy16_to_lds(const void* src, void* lds_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory");
-}
-DSA_DEV void copy4_to_lds(const void* src, void* lds_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(base) : "memory");
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-DSA_DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS
-// operations, not for its outstanding global->LDS copies.
-DSA_DEV void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt unconstrained
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // LDS byte offset of 16-byte chunk j of tile row r (chunks rotated by r).
 DSA_DEV int lat_off(int r, int j) {
   int jp = j + (r % kChunks);

@@ -10,8 +10,15 @@
 // scales are read from HBM once, staged in LDS and used by all the group's
 // rows ("TokenSpeed Kimi K3.1", section "Reducing indexer overhead on AMD
 // MI350X": each key is loaded once for all of a request's verification
-// rows). The next page is in flight in registers while the current one is
-// computed.
+// rows). The workgroup's page ids are read from the block table once, up
+// front, into LDS. A fifth wave only moves data: it copies pages from HBM
+// straight into a ring of kRing LDS slots (global_load_lds, no VGPR staging)
+// and keeps kRing - 1 pages in flight, waiting on its own vmcnt, while the
+// four compute waves read keys from LDS and write scores. Keeping loads and
+// stores in different waves keeps each wave's vmcnt a precise count of its
+// own copies, so the waits never drain the pipeline. One barrier per page
+// hands a full slot to the compute waves and the slot they finished back to
+// the copy wave.
 //
 // The dot products run on v_mfma_scale_f32_32x32x64_f8f6f4 with the raw E4M3
 // key bytes as the B operand (no conversion). Queries enter as E4M3:
@@ -39,29 +46,95 @@
 namespace dsa {
 
 static constexpr int kKeyBytes = kBlock * kIdxDim;  // one page of keys, 8 KB
+static constexpr int kRing = 4;                     // LDS page slots per workgroup
+static constexpr int kMaxWgPages = 2048;            // pages one workgroup walks at most
+static constexpr int kThreads = 320;                // 4 compute waves + 1 copy wave
+static constexpr int kCopies = kKeyBytes / 1024 + 1;  // copy instructions per page (keys + scales)
 
 // LDS position of 16-byte chunk j of key n within a staged page: rows of
 // 128 B with the chunk index XOR-swizzled by (n >> 1) & 7 so that the 16
 // lanes of each read phase hit distinct banks.
 DSA_DEV int key_chunk_off(int n, int j) { return n * kIdxDim + ((j ^ ((n >> 1) & 7)) << 4); }
 
+// max(x, 0) as one integer max on the bit pattern: non-negative floats
+// (+0 included) are non-negative integers, negative floats and -0 are
+// negative integers. The operands are finite MFMA sums.
+DSA_DEV float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Byte offset past every row's visible prefix: buffer stores there are dropped.
+static constexpr uint32_t kPastEnd = 0x80000000u;
+
 DSA_DEV uint32_t e4m3x2_from_f32(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
 
-template <int RPW, bool QFP8, bool HIST>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void score_kernel(ScoreArgs a) {
+
+// The E4M3 A operands of one query row: q * 2^e = hi + lo (bf16 queries) or
+// the query codes as they are; returns the factor 2^-e (or the row scale)
+// that multiplies the head's dot products.
+template <bool QFP8>
+DSA_DEV float load_query(const ScoreArgs& a, size_t row, int n, int g, i32x8 (&A)[QFP8 ? 1 : 2][2]) {
+  if constexpr (QFP8) {
+    const i32x8* qp = reinterpret_cast<const i32x8*>(reinterpret_cast<const uint8_t*>(a.q) +
+                                                     (row * kIdxHeads + n) * kIdxDim + 64 * g);
+    A[0][0] = qp[0];
+    A[0][1] = qp[1];
+    return a.q_scale[row];
+  } else {
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) +
+                                                       (row * kIdxHeads + n) * kIdxDim + 64 * g);
+    float x[64];
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const bf16x8 v = qp[c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[8 * c + e] = (float)v[e];
+        amax = fmaxf(amax, fabsf(x[8 * c + e]));
+      }
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));  // whole head: both lane halves
+    int ex = 0;
+    if (amax > 0.f) {
+      int e2;
+      const float m = frexpf(amax, &e2);  // amax = m * 2^e2, m in [0.5, 1)
+      ex = (m <= 0.875f ? 9 : 8) - e2;    // amax * 2^ex in (224, 448]
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        uint32_t hw = 0, lw = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const float x0 = ldexpf(x[32 * s + 4 * d + e], ex), x1 = ldexpf(x[32 * s + 4 * d + e + 1], ex);
+          const uint32_t hb = e4m3x2_from_f32(x0, x1);
+          const auto hf = __builtin_amdgcn_cvt_pk_f32_fp8(hb, false);
+          const uint32_t lb = e4m3x2_from_f32(x0 - hf[0], x1 - hf[1]);
+          hw |= hb << (8 * e);
+          lw |= lb << (8 * e);
+        }
+        A[0][s][d] = (int)hw;
+        A[1][s][d] = (int)lw;
+      }
+    }
+    return ldexpf(1.0f, -ex);
+  }
+}
+
+template <int RPW, bool QFP8>
+__global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   constexpr int ROWS = 4 * RPW;
   constexpr int NT = QFP8 ? 1 : 2;  // E4M3 terms per query value
-  __shared__ __attribute__((aligned(16))) uint8_t key_s[kKeyBytes];
-  __shared__ float ks_s[kBlock];
+  __shared__ __attribute__((aligned(16))) uint8_t key_s[kRing][kKeyBytes];
+  __shared__ __attribute__((aligned(16))) float ks_s[kRing][kBlock];
+  __shared__ int32_t tbl_s[kMaxWgPages];
   __shared__ __attribute__((aligned(16))) float w_s[ROWS][kIdxHeads];
-  __shared__ uint32_t lhist[HIST ? ROWS * kHistBins : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 5;   // lane half
   const int n = lane & 31;   // A row (head) / B and D column (key)
   const int b = blockIdx.y;
@@ -72,195 +145,209 @@ void score_kernel(ScoreArgs a) {
   const int pos0 = L - R + r0;                // position of the group's first row
   const int blk_lim = ((pos0 + nr - 1) >> 6) + 1;  // pages any row of the group sees
   const size_t row0 = (size_t)b * R + r0;
-  const int wr0 = wave * RPW;                 // this wave's first row within the group
 
-  if constexpr (HIST) {
-    for (int i = tid; i < ROWS * kHistBins; i += 256) lhist[i] = 0;
-  }
-
-  // ---- query fragments (E4M3 terms) and per-head weights for this wave's rows
-  i32x8 A[RPW][NT][2];
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    const int gr = min(wr0 + rr, nr - 1);  // clamp: rows past the group reuse a valid row, never written
-    const size_t row = row0 + gr;
-    float head_scale = 1.0f;  // multiplies the dot product of head n
-    if constexpr (QFP8) {
-      const i32x8* qp = reinterpret_cast<const i32x8*>(reinterpret_cast<const uint8_t*>(a.q) +
-                                                       (row * kIdxHeads + n) * kIdxDim + 64 * g);
-      A[rr][0][0] = qp[0];
-      A[rr][0][1] = qp[1];
-      head_scale = a.q_scale[row];
-    } else {
-      const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) +
-                                                         (row * kIdxHeads + n) * kIdxDim + 64 * g);
-      float x[64];
-      float amax = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const bf16x8 v = qp[c];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          x[8 * c + e] = (float)v[e];
-          amax = fmaxf(amax, fabsf(x[8 * c + e]));
-        }
-      }
-      amax = fmaxf(amax, __shfl_xor(amax, 32));  // whole head: both lane halves
-      int ex = 0;
-      if (amax > 0.f) {
-        int e2;
-        const float m = frexpf(amax, &e2);  // amax = m * 2^e2, m in [0.5, 1)
-        ex = (m <= 0.875f ? 9 : 8) - e2;    // amax * 2^ex in (224, 448]
-      }
-      head_scale = ldexpf(1.0f, -ex);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          uint32_t hw = 0, lw = 0;
-#pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            const float x0 = ldexpf(x[32 * s + 4 * d + e], ex), x1 = ldexpf(x[32 * s + 4 * d + e + 1], ex);
-            const uint32_t hb = e4m3x2_from_f32(x0, x1);
-            const auto hf = __builtin_amdgcn_cvt_pk_f32_fp8(hb, false);
-            const uint32_t lb = e4m3x2_from_f32(x0 - hf[0], x1 - hf[1]);
-            hw |= hb << (8 * e);
-            lw |= lb << (8 * e);
-          }
-          A[rr][0][s][d] = (int)hw;
-          A[rr][1][s][d] = (int)lw;
-        }
-      }
-    }
-    // head weights with the head's scale folded in: w_s[row][head]
-    if (g == 0) {
-      const float wv = __uint_as_float((uint32_t)a.w[row * kIdxHeads + n] << 16);
-      w_s[wr0 + rr][n] = wv * head_scale;
-    }
-  }
-  __syncthreads();
-  // the 16 heads this lane reduces (rows 8*(i/4) + 4g + i%4 of the 32x32 tile);
-  // kept in VGPRs for up to two rows per wave, read from LDS otherwise
-  constexpr int WREG = RPW <= 2 ? RPW : 1;
-  float wv[WREG][16];
-#pragma unroll
-  for (int rr = 0; rr < WREG; ++rr)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) wv[rr][i] = w_s[wr0 + rr][8 * (i >> 2) + 4 * g + (i & 3)];
-
-  // ---- stream pages: this workgroup takes blocks blockIdx.x, +gridDim.x, ...
-  const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
+  // this workgroup's pages: blockIdx.x, +gridDim.x, ... below blk_lim
   const int stride = gridDim.x;
-  u32x4 st0, st1;  // 32 bytes of the next page per thread
-  float sst = 0.f;
-  auto fetch = [&](int blk) {
-    const size_t page = (size_t)table[blk];
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.key_fp8 + page * kKeyBytes);
-    st0 = src[tid];
-    st1 = src[tid + 256];
-    if (tid < kBlock) sst = a.key_scale[page * kBlock + tid];
-  };
-  int blk = blockIdx.x;
-  if (blk < blk_lim) fetch(blk);
-  for (; blk < blk_lim; blk += stride) {
-    __syncthreads();  // the previous page is consumed
-    {
-      const int c0 = tid, c1 = tid + 256;  // chunk c: key c >> 3, chunk c & 7
-      *reinterpret_cast<u32x4*>(key_s + key_chunk_off(c0 >> 3, c0 & 7)) = st0;
-      *reinterpret_cast<u32x4*>(key_s + key_chunk_off(c1 >> 3, c1 & 7)) = st1;
-      if (tid < kBlock) ks_s[tid] = sst;
-    }
-    if (blk + stride < blk_lim) fetch(blk + stride);
-    __syncthreads();
+  const int n_my = blk_lim > (int)blockIdx.x ? (blk_lim - (int)blockIdx.x + stride - 1) / stride : 0;
+  {
+    const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
+    for (int i = tid; i < n_my; i += kThreads) tbl_s[i] = table[blockIdx.x + i * stride];
+  }
 
+  if (wave == 4) {
+    // ---- copy wave. Copy j of a page moves LDS chunks 64j .. 64j+63 of the
+    // page's swizzled layout: lane l fetches the global chunk that belongs at
+    // LDS chunk 64j + l. The last copy moves the page's 64 scales.
+    int src_off[kCopies - 1];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key = 32 * h + n;
-      i32x8 B[2];
+    for (int j = 0; j < kCopies - 1; ++j) {
+      const int c = 64 * j + lane;
+      const int key = c >> 3;
+      src_off[j] = key * kIdxDim + (((c & 7) ^ ((key >> 1) & 7)) << 4);
+    }
+    __syncthreads();  // tbl_s and w_s ready
+    auto issue = [&](int i) {
+      const int slot = i % kRing;
+      const size_t page = (size_t)tbl_s[i];
+      const uint8_t* pg = a.key_fp8 + page * kKeyBytes;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(key_s + key_chunk_off(key, 4 * g + 2 * s));
-        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(key_s + key_chunk_off(key, 4 * g + 2 * s + 1));
-        B[s] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                     (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+      for (int j = 0; j < kCopies - 1; ++j) copy16_to_lds(pg + src_off[j], key_s[slot] + 1024 * j);
+      copy4_to_lds(a.key_scale + page * kBlock + lane, ks_s[slot]);
+    };
+    for (int i = 0; i < kRing - 1 && i < n_my; ++i) issue(i);
+    for (int i = 0; i < n_my; ++i) {
+      // pages issued after page i: min(kRing - 2, n_my - 1 - i)
+      if (i + kRing - 2 < n_my) wait_vmcnt<kCopies * (kRing - 2)>();
+      else wait_vmcnt<0>();
+      lds_barrier();  // page i is in LDS; the slot of page i - 1 is free
+      if (i + kRing - 1 < n_my) issue(i + kRing - 1);
+    }
+  } else {
+    // ---- compute waves: wave w owns rows w*RPW .. w*RPW + RPW - 1 of the group
+    const int wr0 = wave * RPW;
+    i32x8 A[RPW][NT][2];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int gr = min(wr0 + rr, nr - 1);  // clamp: rows past the group reuse a valid row, never written
+      const size_t row = row0 + gr;
+      const float head_scale = load_query<QFP8>(a, row, n, g, A[rr]);
+      // head weights with the head's scale folded in: w_s[row][head]
+      if (g == 0) {
+        const float wv = __uint_as_float((uint32_t)a.w[row * kIdxHeads + n] << 16);
+        w_s[wr0 + rr][n] = wv * head_scale;
       }
-      const float ks = ks_s[key];
+    }
+    __syncthreads();  // tbl_s and w_s ready
+    // the 16 heads this lane reduces (rows 8*(i/4) + 4g + i%4 of the 32x32 tile);
+    // kept in VGPRs for one row per wave, read from LDS otherwise
+    constexpr int WREG = 1;
+    float wv[WREG][16];
+#pragma unroll
+    for (int rr = 0; rr < WREG; ++rr)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wv[rr][i] = w_s[wr0 + rr][8 * (i >> 2) + 4 * g + (i & 3)];
+
+    // Score stores go through one buffer descriptor per row whose size is
+    // the row's visible prefix (positions 0 .. pos): the hardware drops any
+    // store at or past it, which is the causal mask, and lanes that hold no
+    // row's total store at an offset past every prefix. The epilogue is
+    // therefore branch-free.
+    __amdgpu_buffer_rsrc_t rs[RPW];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int gr = wr0 + rr;
+      const int gv = min(gr, nr - 1);
+      const int bytes = gr < nr ? 4 * (pos0 + gr + 1) : 0;
+      rs[rr] = __builtin_amdgcn_make_buffer_rsrc(a.scores + (row0 + gv) * a.ld, (short)0, bytes, 0x00020000);
+    }
+    constexpr int HALF = (RPW + 1) / 2;  // lanes < 32 total row j, lanes >= 32 row j + HALF
+    // head-weighted ReLU sum of one 32-key half for all rows of the wave,
+    // and its stores (keys 32h .. 32h+31 of page blk)
+    auto epilogue = [&](const f32x16 (&acc)[RPW], float ks, int blk, int h) {
       float p[RPW];
 #pragma unroll
       for (int rr = 0; rr < RPW; ++rr) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[rr][t][s], B[s], acc, 0, 0, 0, 127, 0, 127);
         float sum = 0.f;
-        if constexpr (RPW <= 2) {
+        if constexpr (RPW == 1) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sum = __builtin_fmaf(wv[rr][i], fmaxf(acc[i], 0.f), sum);
+          for (int i2 = 0; i2 < 16; ++i2) sum = __builtin_fmaf(wv[rr][i2], relu(acc[rr][i2]), sum);
         } else {
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const f32x4 w4 = *reinterpret_cast<const f32x4*>(&w_s[wr0 + rr][8 * q4 + 4 * g]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sum = __builtin_fmaf(w4[e], fmaxf(acc[4 * q4 + e], 0.f), sum);
+            for (int e = 0; e < 4; ++e) sum = __builtin_fmaf(w4[e], relu(acc[rr][4 * q4 + e]), sum);
           }
         }
         p[rr] = sum;
       }
-      // combine lane halves: lanes < 32 get row j, lanes >= 32 row j + HALF
-      constexpr int HALF = (RPW + 1) / 2;
-      const int tokpos = blk * kBlock + key;
+      const uint32_t off = 4u * (uint32_t)(blk * kBlock + 32 * h + n);  // blk < 0: past every prefix
 #pragma unroll
       for (int j = 0; j < HALF; ++j) {
-        const float tot = halves_sum_pair(p[j], (j + HALF < RPW) ? p[j + HALF] : p[j]);
-        const int rr = (RPW == 1) ? 0 : j + g * HALF;
-        if ((RPW == 1 && g == 1) || rr >= RPW) continue;
-        const int gr = wr0 + rr;
-        if (gr < nr && tokpos <= pos0 + gr) {
-          const float v = tot * ks;
-          a.scores[(row0 + gr) * a.ld + tokpos] = v;
-          if constexpr (HIST) atomicAdd(&lhist[gr * kHistBins + (ordered_key(v) >> 21)], 1u);
+        const float v = halves_sum_pair(p[j], (j + HALF < RPW) ? p[j + HALF] : p[j]) * ks;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs[j], g == 0 ? off : kPastEnd, 0, 0);
+        if (j + HALF < RPW)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs[j + HALF], g == 1 ? off : kPastEnd, 0, 0);
+      }
+    };
+    auto mfma_half = [&](f32x16 (&acc)[RPW], const i32x8 (&Bh)[2]) {
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        acc[rr] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            acc[rr] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[rr][t][s], Bh[s], acc[rr], 0, 0, 0, 127, 0,
+                                                                      127);
+      }
+    };
+    // Software pipeline over 32-key halves: the MFMAs of one half run while
+    // the VALU epilogue of the previous half (of this page or the previous
+    // one) is issued between them. With four rows per wave the second set of
+    // accumulators does not fit beside the queries; those waves take the
+    // halves one after the other and rely on the other waves of the SIMD to
+    // fill the matrix cores.
+    if constexpr (RPW > 2) {
+      for (int i = 0; i < n_my; ++i) {
+        lds_barrier();  // page i is in LDS
+        const uint8_t* kbuf = key_s[i % kRing];
+        const float* ksb = ks_s[i % kRing];
+        const int blk = (int)blockIdx.x + i * stride;
+#pragma unroll 1
+        for (int h = 0; h < 2; ++h) {
+          const int key = 32 * h + n;
+          i32x8 B[2];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s));
+            const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s + 1));
+            B[s] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                         (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+          }
+          f32x16 acc[RPW];
+          mfma_half(acc, B);
+          epilogue(acc, ksb[key], blk, h);
         }
       }
+      return;
     }
-  }
-
-  if constexpr (HIST) {
-    __syncthreads();
-    for (int i = tid; i < ROWS * kHistBins; i += 256) {
-      const uint32_t c = lhist[i];
-      const int gr = i / kHistBins;
-      if (c != 0 && gr < nr) atomicAdd(&a.hist[(row0 + gr) * kHistBins + (i % kHistBins)], c);
+    f32x16 acc0[RPW], acc1[RPW];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) acc1[rr] = f32x16{};
+    float ks1 = 0.f;
+    int blk_prev = -1;
+    for (int i = 0; i < n_my; ++i) {
+      lds_barrier();  // page i is in LDS
+      const uint8_t* kbuf = key_s[i % kRing];
+      const float* ksb = ks_s[i % kRing];
+      const int blk = (int)blockIdx.x + i * stride;
+      i32x8 B[2][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int key = 32 * h + n;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s));
+          const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s + 1));
+          B[h][s] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                          (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+        }
+      }
+      const float ks0 = ksb[n];
+      const float ks1_next = ksb[32 + n];
+      mfma_half(acc0, B[0]);
+      epilogue(acc1, ks1, blk_prev, 1);  // second half of the previous page
+      mfma_half(acc1, B[1]);
+      epilogue(acc0, ks0, blk, 0);
+      ks1 = ks1_next;
+      blk_prev = blk;
     }
+    epilogue(acc1, ks1, blk_prev, 1);
   }
 }
 
 template <int RPW, bool QFP8>
 static void launch_variant(const ScoreArgs& a, dim3 grid, hipStream_t st) {
-  if constexpr (RPW <= 2) {
-    if (a.hist) {
-      hipLaunchKernelGGL((score_kernel<RPW, QFP8, true>), grid, dim3(256), 0, st, a);
-      return;
-    }
-  }
-  hipLaunchKernelGGL((score_kernel<RPW, QFP8, false>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((score_kernel<RPW, QFP8>), grid, dim3(kThreads), 0, st, a);
 }
 
 hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st) {
   // Rows per wave: one for decode-sized requests; more when a request brings
   // many rows (prefill chunks), so that more rows share each staged page.
   int rpw = 1;
-  if (a.R > 4) rpw = 2;
+  if (q_fp8 && a.R > 4) rpw = 2;
   if (q_fp8 && a.R > 16) rpw = 4;
-  if (a.hist && rpw > 2) rpw = 2;
   const int groups = (a.R + 4 * rpw - 1) / (4 * rpw);
   const int max_blk = (max_ctx + kBlock - 1) / kBlock;
-  // About three workgroups per CU over the whole grid, at least 2 pages each.
-  long long per_req = (768 + (long long)B * groups - 1) / ((long long)B * groups);
+  // Two workgroups per CU (their occupancy limit) in one round over the
+  // whole grid, at least 2 pages each, and no workgroup past kMaxWgPages.
+  long long per_req = (512 + (long long)B * groups - 1) / ((long long)B * groups);
   long long cap = (max_blk + 1) / 2;
   if (per_req > cap) per_req = cap;
   if (per_req < 1) per_req = 1;
+  const long long need = (max_blk + kMaxWgPages - 1) / kMaxWgPages;
+  if (per_req < need) per_req = need;
   const dim3 grid((unsigned)per_req, B, groups);
   if (q_fp8) {
     switch (rpw) {
@@ -269,8 +356,7 @@ hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8
       default: launch_variant<4, true>(a, grid, st); break;
     }
   } else {
-    if (rpw == 1) launch_variant<1, false>(a, grid, st);
-    else launch_variant<2, false>(a, grid, st);
+    launch_variant<1, false>(a, grid, st);
   }
   return hipGetLastError();
 }

@@ -102,3 +102,15 @@ def test_argument_errors_are_reported_before_any_launch(lib):
         _lib.DSA_ERR_WORKSPACE
     assert lib.dsa_decode(ctypes.byref(b), ctypes.byref(_cache(lat_fp8=0)), P, P, P, 16, 2048, 0.1, P, None, None, P,
                           1 << 30, None) == _lib.DSA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors():
+    """Tensor checks in the binding run before the library is called."""
+    import torch
+
+    import sparse_attention_index_amd as dsa
+
+    ctx = torch.tensor([100], dtype=torch.int32)
+    table = torch.zeros((1, 2), dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensor"):
+        dsa.Batch(1, ctx, table, 100)

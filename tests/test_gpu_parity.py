@@ -9,6 +9,8 @@ import numpy as np
 import pytest
 import torch
 
+import sparse_attention_index_amd as dsa
+
 import oracle
 from tests.gpu_run import gpu_decode, gpu_mla, gpu_scores, gpu_topk, row_len_of
 from tests.parity import check_attention, check_scores, check_topk_band, check_topk_exact
@@ -177,3 +179,19 @@ def test_fused_decode_selection_is_deterministic(gpu):
         assert set(ia[row].tolist()) == set(ib[row].tolist())
     check_attention(a[0].float().cpu().numpy(), a[1].cpu().numpy(), b[0].float().cpu().numpy(),
                     b[1].cpu().numpy(), "repeat")
+
+
+def test_binding_rejects_mismatched_tensors_before_launch(gpu):
+    """The fused decode takes bf16 indexer queries: E4M3 query codes (half the
+    bytes) must be refused by the binding before any kernel reads them."""
+    case = _case("fp8q_2x7")
+    rows, k = case.rows, case.topk
+    ws = torch.empty(1, dtype=torch.uint8, device="cuda")
+    out = torch.empty((rows, 16, 512), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="q_idx"):
+        dsa.dsa_decode(dsa.Batch.of(case), dsa.Cache.of(case), case.q_idx, case.w, case.q_mla, k, case.sm_scale,
+                       out, None, None, ws)
+    scores = torch.empty((rows, 64), dtype=torch.float32, device="cuda")  # narrower than the context
+    with pytest.raises(ValueError, match="scores"):
+        dsa.dsa_index_score(dsa.Batch.of(case), dsa.Cache.of(case), case.q_idx, case.w, scores,
+                            q_scale=case.q_idx_scale)
