@@ -11,14 +11,23 @@
 // rows ("TokenSpeed Kimi K3.1", section "Reducing indexer overhead on AMD
 // MI350X": each key is loaded once for all of a request's verification
 // rows). The workgroup's page ids are read from the block table once, up
-// front, into LDS. A fifth wave only moves data: it copies pages from HBM
-// straight into a ring of kRing LDS slots (global_load_lds, no VGPR staging)
-// and keeps kRing - 1 pages in flight, waiting on its own vmcnt, while the
-// four compute waves read keys from LDS and write scores. Keeping loads and
-// stores in different waves keeps each wave's vmcnt a precise count of its
-// own copies, so the waits never drain the pipeline. One barrier per page
-// hands a full slot to the compute waves and the slot they finished back to
-// the copy wave.
+// front, into LDS.
+//
+// Streaming. The page copies go from HBM straight into a ring of kRing LDS
+// slots (global_load_lds, no VGPR staging) and kRing - 1 pages stay in
+// flight. Waves 0-2 each issue a third of every page's copies and wait on
+// their own vmcnt; their scores go to LDS, and wave 3 stores all rows'
+// scores. A wave that issues both loads and stores can only wait for all of
+// its outstanding operations, so keeping the copying waves free of global
+// stores keeps their vmcnt an exact count of copies and the waits never
+// drain the ring. One barrier per page hands a full slot to the waves and
+// the slot they finished back to the copiers. Workgroups of four waves take
+// one wave slot per SIMD, so several fit a CU and overlap each other's MFMA
+// and VALU work; the copy and store duties are spread so that no wave (and
+// no SIMD) carries much more than the others.
+// Score stores use buffer descriptors sized to each row's visible prefix:
+// the hardware drops stores past it, which applies the causal mask without
+// branches.
 //
 // The dot products run on v_mfma_scale_f32_32x32x64_f8f6f4 with the raw E4M3
 // key bytes as the B operand (no conversion). Queries enter as E4M3:
@@ -35,11 +44,16 @@
 //    and the keys need no widening.
 // The 32x32 output tile puts 16 heads of one key in each lane, so the
 // head-weighted ReLU reduction is 16 in-lane max+fma steps plus one
-// permlane32 swap between the lane halves. 2^-e, the key scale and the
+// permlane32 swap between the lane halves. With one or two rows per wave the
+// MFMAs of each 32-key half are interleaved with the epilogue of the half
+// before it. 2^-e, the key scale and the
 // query row scale are positive and are applied after the ReLU.
 //
 // K (the 128 key dims) is permuted identically in both operands: lane half
 // g of a 32x32x64 step s holds dims 64g + 32s + [0, 32).
+#include <atomic>
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -48,8 +62,11 @@ namespace dsa {
 static constexpr int kKeyBytes = kBlock * kIdxDim;  // one page of keys, 8 KB
 static constexpr int kRing = 4;                     // LDS page slots per workgroup
 static constexpr int kMaxWgPages = 2048;            // pages one workgroup walks at most
-static constexpr int kThreads = 320;                // 4 compute waves + 1 copy wave
+static constexpr int kThreads = 256;                // 4 waves
 static constexpr int kCopies = kKeyBytes / 1024 + 1;  // copy instructions per page (keys + scales)
+static constexpr int kCopiers = 3;                  // waves that issue copies
+static constexpr int kCopiesPerWave = kCopies / kCopiers;
+static_assert(kCopies % kCopiers == 0, "copies split evenly");
 
 // LDS position of 16-byte chunk j of key n within a staged page: rows of
 // 128 B with the chunk index XOR-swizzled by (n >> 1) & 7 so that the 16
@@ -123,14 +140,21 @@ DSA_DEV float load_query(const ScoreArgs& a, size_t row, int n, int g, i32x8 (&A
   }
 }
 
+// Roles of the waves: every wave scores RPW rows and writes its scores to
+// LDS; waves 0-2 also move the pages into LDS, wave 3 stores the scores.
+enum WaveRole { kCopier, kFlusher };
+
 template <int RPW, bool QFP8>
 __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   constexpr int ROWS = 4 * RPW;
   constexpr int NT = QFP8 ? 1 : 2;  // E4M3 terms per query value
+  constexpr bool PIPE = RPW <= 2;   // software-pipelined halves (see below)
+  constexpr int LAG = PIPE ? 2 : 1;  // a page's scores are complete LAG barriers later
   __shared__ __attribute__((aligned(16))) uint8_t key_s[kRing][kKeyBytes];
   __shared__ __attribute__((aligned(16))) float ks_s[kRing][kBlock];
   __shared__ int32_t tbl_s[kMaxWgPages];
   __shared__ __attribute__((aligned(16))) float w_s[ROWS][kIdxHeads];
+  __shared__ float sc_s[LAG + 1][ROWS][kBlock];  // scores of the group's rows, by page
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -154,83 +178,74 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
     for (int i = tid; i < n_my; i += kThreads) tbl_s[i] = table[blockIdx.x + i * stride];
   }
 
-  if (wave == 4) {
-    // ---- copy wave. Copy j of a page moves LDS chunks 64j .. 64j+63 of the
-    // page's swizzled layout: lane l fetches the global chunk that belongs at
-    // LDS chunk 64j + l. The last copy moves the page's 64 scales.
-    int src_off[kCopies - 1];
+  // ---- queries of this wave's rows (E4M3 terms) and head weights
+  const int wr0 = wave * RPW;
+  i32x8 A[RPW][NT][2];
 #pragma unroll
-    for (int j = 0; j < kCopies - 1; ++j) {
-      const int c = 64 * j + lane;
-      const int key = c >> 3;
-      src_off[j] = key * kIdxDim + (((c & 7) ^ ((key >> 1) & 7)) << 4);
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int gr = min(wr0 + rr, nr - 1);  // clamp: rows past the group reuse a valid row, never written
+    const size_t row = row0 + gr;
+    const float head_scale = load_query<QFP8>(a, row, n, g, A[rr]);
+    // head weights with the head's scale folded in: w_s[row][head]
+    if (g == 0) {
+      const float wv = __uint_as_float((uint32_t)a.w[row * kIdxHeads + n] << 16);
+      w_s[wr0 + rr][n] = wv * head_scale;
     }
-    __syncthreads();  // tbl_s and w_s ready
-    auto issue = [&](int i) {
-      const int slot = i % kRing;
-      const size_t page = (size_t)tbl_s[i];
-      const uint8_t* pg = a.key_fp8 + page * kKeyBytes;
+  }
+  __syncthreads();  // tbl_s and w_s ready
+  // the 16 heads this lane reduces (rows 8*(i/4) + 4g + i%4 of the 32x32 tile);
+  // kept in VGPRs for one row per wave, read from LDS otherwise
+  float wv[16];
 #pragma unroll
-      for (int j = 0; j < kCopies - 1; ++j) copy16_to_lds(pg + src_off[j], key_s[slot] + 1024 * j);
-      copy4_to_lds(a.key_scale + page * kBlock + lane, ks_s[slot]);
-    };
-    for (int i = 0; i < kRing - 1 && i < n_my; ++i) issue(i);
-    for (int i = 0; i < n_my; ++i) {
-      // pages issued after page i: min(kRing - 2, n_my - 1 - i)
-      if (i + kRing - 2 < n_my) wait_vmcnt<kCopies * (kRing - 2)>();
-      else wait_vmcnt<0>();
-      lds_barrier();  // page i is in LDS; the slot of page i - 1 is free
-      if (i + kRing - 1 < n_my) issue(i + kRing - 1);
-    }
-  } else {
-    // ---- compute waves: wave w owns rows w*RPW .. w*RPW + RPW - 1 of the group
-    const int wr0 = wave * RPW;
-    i32x8 A[RPW][NT][2];
+  for (int i = 0; i < 16; ++i) wv[i] = w_s[wr0][8 * (i >> 2) + 4 * g + (i & 3)];
+
+  // Score stores go through one buffer descriptor per row whose size is the
+  // row's visible prefix (positions 0 .. pos): the hardware drops any store
+  // at or past it, which is the causal mask, and lanes that hold no row's
+  // total store at an offset past every prefix. Stores are branch-free.
+  auto row_rsrc = [&](int gr) {
+    const int gv = min(gr, nr - 1);
+    const int bytes = gr < nr ? 4 * (pos0 + gr + 1) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(a.scores + (row0 + gv) * a.ld, (short)0, bytes, 0x00020000);
+  };
+  __amdgpu_buffer_rsrc_t rs[ROWS];  // used by the storing wave
 #pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const int gr = min(wr0 + rr, nr - 1);  // clamp: rows past the group reuse a valid row, never written
-      const size_t row = row0 + gr;
-      const float head_scale = load_query<QFP8>(a, row, n, g, A[rr]);
-      // head weights with the head's scale folded in: w_s[row][head]
-      if (g == 0) {
-        const float wv = __uint_as_float((uint32_t)a.w[row * kIdxHeads + n] << 16);
-        w_s[wr0 + rr][n] = wv * head_scale;
+  for (int gr = 0; gr < ROWS; ++gr) rs[gr] = row_rsrc(gr);
+  constexpr int HALF = (RPW + 1) / 2;  // lanes < 32 total row j, lanes >= 32 row j + HALF
+
+  // Copy j of a page moves LDS chunks 64j .. 64j+63 of the page's swizzled
+  // layout: lane l fetches the global chunk that belongs at LDS chunk 64j + l.
+  // The last copy moves the page's 64 scales. Wave w issues copies
+  // w*kCopiesPerWave .. w*kCopiesPerWave + kCopiesPerWave - 1.
+  auto issue = [&](int i) {
+    const int slot = i % kRing;
+    const size_t page = (size_t)tbl_s[i];
+    const uint8_t* pg = a.key_fp8 + page * kKeyBytes;
+#pragma unroll
+    for (int jj = 0; jj < kCopiesPerWave; ++jj) {
+      const int j = wave * kCopiesPerWave + jj;
+      if (j < kCopies - 1) {
+        const int c = 64 * j + lane;
+        const int key = c >> 3;
+        copy16_to_lds(pg + key * kIdxDim + (((c & 7) ^ ((key >> 1) & 7)) << 4), key_s[slot] + 1024 * j);
+      } else {
+        copy4_to_lds(a.key_scale + page * kBlock + lane, ks_s[slot]);
       }
     }
-    __syncthreads();  // tbl_s and w_s ready
-    // the 16 heads this lane reduces (rows 8*(i/4) + 4g + i%4 of the 32x32 tile);
-    // kept in VGPRs for one row per wave, read from LDS otherwise
-    constexpr int WREG = 1;
-    float wv[WREG][16];
-#pragma unroll
-    for (int rr = 0; rr < WREG; ++rr)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) wv[rr][i] = w_s[wr0 + rr][8 * (i >> 2) + 4 * g + (i & 3)];
+  };
 
-    // Score stores go through one buffer descriptor per row whose size is
-    // the row's visible prefix (positions 0 .. pos): the hardware drops any
-    // store at or past it, which is the causal mask, and lanes that hold no
-    // row's total store at an offset past every prefix. The epilogue is
-    // therefore branch-free.
-    __amdgpu_buffer_rsrc_t rs[RPW];
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const int gr = wr0 + rr;
-      const int gv = min(gr, nr - 1);
-      const int bytes = gr < nr ? 4 * (pos0 + gr + 1) : 0;
-      rs[rr] = __builtin_amdgcn_make_buffer_rsrc(a.scores + (row0 + gv) * a.ld, (short)0, bytes, 0x00020000);
-    }
-    constexpr int HALF = (RPW + 1) / 2;  // lanes < 32 total row j, lanes >= 32 row j + HALF
-    // head-weighted ReLU sum of one 32-key half for all rows of the wave,
-    // and its stores (keys 32h .. 32h+31 of page blk)
-    auto epilogue = [&](const f32x16 (&acc)[RPW], float ks, int blk, int h) {
+  auto run = [&](auto role_tag) {
+    constexpr WaveRole role = decltype(role_tag)::value;
+    // head-weighted ReLU sum of one 32-key half (keys 32h .. 32h+31 of the
+    // i-th page, block blk) for all rows of the wave, and its stores
+    auto epilogue = [&](const f32x16(&acc)[RPW], float ks, int i, int blk, int h) {
       float p[RPW];
 #pragma unroll
       for (int rr = 0; rr < RPW; ++rr) {
         float sum = 0.f;
         if constexpr (RPW == 1) {
 #pragma unroll
-          for (int i2 = 0; i2 < 16; ++i2) sum = __builtin_fmaf(wv[rr][i2], relu(acc[rr][i2]), sum);
+          for (int i2 = 0; i2 < 16; ++i2) sum = __builtin_fmaf(wv[i2], relu(acc[rr][i2]), sum);
         } else {
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
@@ -241,16 +256,22 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
         }
         p[rr] = sum;
       }
-      const uint32_t off = 4u * (uint32_t)(blk * kBlock + 32 * h + n);  // blk < 0: past every prefix
-#pragma unroll
+  #pragma unroll
       for (int j = 0; j < HALF; ++j) {
         const float v = halves_sum_pair(p[j], (j + HALF < RPW) ? p[j + HALF] : p[j]) * ks;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs[j], g == 0 ? off : kPastEnd, 0, 0);
-        if (j + HALF < RPW)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs[j + HALF], g == 1 ? off : kPastEnd, 0, 0);
+        // both lane halves write; with one row per wave they write the same value
+        const int rr = RPW == 1 ? 0 : j + g * HALF;
+        if (i >= 0) sc_s[i % (LAG + 1)][wr0 + rr][32 * h + n] = v;
       }
     };
-    auto mfma_half = [&](f32x16 (&acc)[RPW], const i32x8 (&Bh)[2]) {
+    // wave 3: store the group's scores of page i (complete once barrier i + LAG passed)
+    auto flush = [&](int i) {
+      const uint32_t off = 4u * (uint32_t)(((int)blockIdx.x + i * stride) * kBlock + lane);
+#pragma unroll
+      for (int gr = 0; gr < ROWS; ++gr)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_s[i % (LAG + 1)][gr][lane]), rs[gr], off, 0, 0);
+    };
+    auto mfma_half = [&](f32x16(&acc)[RPW], const i32x8(&Bh)[2]) {
 #pragma unroll
       for (int rr = 0; rr < RPW; ++rr) {
         acc[rr] = f32x16{};
@@ -262,101 +283,146 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
                                                                       127);
       }
     };
-    // Software pipeline over 32-key halves: the MFMAs of one half run while
-    // the VALU epilogue of the previous half (of this page or the previous
-    // one) is issued between them. With four rows per wave the second set of
-    // accumulators does not fit beside the queries; those waves take the
-    // halves one after the other and rely on the other waves of the SIMD to
-    // fill the matrix cores.
-    if constexpr (RPW > 2) {
+    auto load_b = [&](const uint8_t* kbuf, int h, i32x8(&Bh)[2]) {
+      const int key = 32 * h + n;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s));
+        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s + 1));
+        Bh[s] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                      (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+      }
+    };
+    // kRing - 1 pages are in flight. A copier's only vector-memory
+    // operations in the loop are its copies, so its vmcnt counts exactly
+    // its copies of the pages after page i.
+    auto wait_page = [&](int i) {
+      if constexpr (role == kCopier) {
+        if (i + kRing - 2 < n_my) wait_vmcnt<kCopiesPerWave * (kRing - 2)>();
+        else wait_vmcnt<0>();
+      }
+    };
+    if constexpr (role == kCopier) {
+      wait_vmcnt<0>();  // nothing but the copies is outstanding from here on
+      for (int i = 0; i < kRing - 1 && i < n_my; ++i) issue(i);
+    }
+
+    if constexpr (!PIPE) {
       for (int i = 0; i < n_my; ++i) {
-        lds_barrier();  // page i is in LDS
+        wait_page(i);
+        lds_barrier();  // page i is in LDS; the slot of page i - 1 is free
+        if constexpr (role == kCopier) {
+          if (i + kRing - 1 < n_my) issue(i + kRing - 1);
+        }
+        if constexpr (role == kFlusher) {
+          if (i >= LAG) flush(i - LAG);
+        }
         const uint8_t* kbuf = key_s[i % kRing];
         const float* ksb = ks_s[i % kRing];
         const int blk = (int)blockIdx.x + i * stride;
 #pragma unroll 1
         for (int h = 0; h < 2; ++h) {
-          const int key = 32 * h + n;
           i32x8 B[2];
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s));
-            const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s + 1));
-            B[s] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                         (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-          }
+          load_b(kbuf, h, B);
           f32x16 acc[RPW];
           mfma_half(acc, B);
-          epilogue(acc, ksb[key], blk, h);
+          epilogue(acc, ksb[32 * h + n], i, blk, h);
         }
       }
-      return;
-    }
-    f32x16 acc0[RPW], acc1[RPW];
+    } else {
+      // Software pipeline over 32-key halves: the MFMAs of one half run
+      // while the VALU epilogue of the previous half (of this page or the
+      // previous one) is issued between them.
+      f32x16 acc0[RPW], acc1[RPW];
 #pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) acc1[rr] = f32x16{};
-    float ks1 = 0.f;
-    int blk_prev = -1;
-    for (int i = 0; i < n_my; ++i) {
-      lds_barrier();  // page i is in LDS
-      const uint8_t* kbuf = key_s[i % kRing];
-      const float* ksb = ks_s[i % kRing];
-      const int blk = (int)blockIdx.x + i * stride;
-      i32x8 B[2][2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = 32 * h + n;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s));
-          const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s + 1));
-          B[h][s] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                          (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+      for (int rr = 0; rr < RPW; ++rr) acc1[rr] = f32x16{};
+      float ks1 = 0.f;
+      int blk_prev = -1;
+      for (int i = 0; i < n_my; ++i) {
+        wait_page(i);
+        lds_barrier();  // page i is in LDS; the slot of page i - 1 is free
+        if constexpr (role == kCopier) {
+          if (i + kRing - 1 < n_my) issue(i + kRing - 1);
         }
+        if constexpr (role == kFlusher) {
+          if (i >= LAG) flush(i - LAG);
+        }
+        const uint8_t* kbuf = key_s[i % kRing];
+        const float* ksb = ks_s[i % kRing];
+        const int blk = (int)blockIdx.x + i * stride;
+        i32x8 B0[2], B1[2];
+        load_b(kbuf, 0, B0);
+        load_b(kbuf, 1, B1);
+        const float ks0 = ksb[n];
+        const float ks1_next = ksb[32 + n];
+        mfma_half(acc0, B0);
+        epilogue(acc1, ks1, i - 1, blk_prev, 1);  // second half of the previous page
+        mfma_half(acc1, B1);
+        epilogue(acc0, ks0, i, blk, 0);
+        ks1 = ks1_next;
+        blk_prev = blk;
       }
-      const float ks0 = ksb[n];
-      const float ks1_next = ksb[32 + n];
-      mfma_half(acc0, B[0]);
-      epilogue(acc1, ks1, blk_prev, 1);  // second half of the previous page
-      mfma_half(acc1, B[1]);
-      epilogue(acc0, ks0, blk, 0);
-      ks1 = ks1_next;
-      blk_prev = blk;
+      epilogue(acc1, ks1, n_my - 1, blk_prev, 1);
     }
-    epilogue(acc1, ks1, blk_prev, 1);
+    __syncthreads();  // the last scores are in LDS
+    if constexpr (role == kFlusher) {
+      for (int i = max(0, n_my - LAG); i < n_my; ++i) flush(i);
+    }
+  };
+  if (wave < kCopiers) run(std::integral_constant<WaveRole, kCopier>{});
+  else run(std::integral_constant<WaveRole, kFlusher>{});
+}
+
+// Workgroups of a variant that fit one CU at once (registers, LDS), from
+// the runtime's occupancy calculator; computed once per variant.
+template <int RPW, bool QFP8>
+static int resident_per_cu() {
+  static const int n = [] {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, score_kernel<RPW, QFP8>, kThreads, 0) != hipSuccess || v < 1)
+      v = 1;
+    return v;
+  }();
+  return n;
+}
+
+static int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
+  return n;
 }
 
 template <int RPW, bool QFP8>
-static void launch_variant(const ScoreArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((score_kernel<RPW, QFP8>), grid, dim3(kThreads), 0, st, a);
-}
-
-hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st) {
-  // Rows per wave: one for decode-sized requests; more when a request brings
-  // many rows (prefill chunks), so that more rows share each staged page.
-  int rpw = 1;
-  if (q_fp8 && a.R > 4) rpw = 2;
-  if (q_fp8 && a.R > 16) rpw = 4;
-  const int groups = (a.R + 4 * rpw - 1) / (4 * rpw);
+static void launch_variant(const ScoreArgs& a, int B, int max_ctx, hipStream_t st) {
+  const int groups = (a.R + 4 * RPW - 1) / (4 * RPW);
   const int max_blk = (max_ctx + kBlock - 1) / kBlock;
-  // Two workgroups per CU (their occupancy limit) in one round over the
-  // whole grid, at least 2 pages each, and no workgroup past kMaxWgPages.
-  long long per_req = (512 + (long long)B * groups - 1) / ((long long)B * groups);
-  long long cap = (max_blk + 1) / 2;
+  // One round of resident workgroups over the whole grid, at least 2 pages
+  // each, and no workgroup past kMaxWgPages.
+  const long long slots = (long long)resident_per_cu<RPW, QFP8>() * cu_count();
+  long long per_req = (slots + (long long)B * groups - 1) / ((long long)B * groups);
+  const long long cap = (max_blk + 1) / 2;
   if (per_req > cap) per_req = cap;
   if (per_req < 1) per_req = 1;
   const long long need = (max_blk + kMaxWgPages - 1) / kMaxWgPages;
   if (per_req < need) per_req = need;
-  const dim3 grid((unsigned)per_req, B, groups);
+  hipLaunchKernelGGL((score_kernel<RPW, QFP8>), dim3((unsigned)per_req, B, groups), dim3(kThreads), 0, st, a);
+}
+
+hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st) {
+  // Rows per wave: one for decode-sized requests; more when a request brings
+  // many FP8 query rows (prefill chunks), so that more rows share each page.
   if (q_fp8) {
-    switch (rpw) {
-      case 1: launch_variant<1, true>(a, grid, st); break;
-      case 2: launch_variant<2, true>(a, grid, st); break;
-      default: launch_variant<4, true>(a, grid, st); break;
-    }
+    if (a.R > 16) launch_variant<4, true>(a, B, max_ctx, st);
+    else if (a.R > 4) launch_variant<2, true>(a, B, max_ctx, st);
+    else launch_variant<1, true>(a, B, max_ctx, st);
   } else {
-    launch_variant<1, false>(a, grid, st);
+    launch_variant<1, false>(a, B, max_ctx, st);
   }
   return hipGetLastError();
 }
