@@ -99,12 +99,9 @@ size_t decode_ws_parts(int32_t rows, int64_t max_ctx, int32_t k, DecodeWs* out, 
 }
 
 int32_t run_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows, int32_t k, int32_t* idx,
-                 void* ws, bool cleared, hipStream_t st) {
+                 void* ws, hipStream_t st) {
   const TopkWs w = topk_ws_carve(ws, rows, ld);
-  int32_t r;
-  if (!cleared && (r = hip_status(launch_topk_clear(w, rows, st), "topk clear"))) return r;
-  if ((r = hip_status(launch_topk_hist(scores, ld, row_len, rows, ld, w, st), "topk hist"))) return r;
-  return hip_status(launch_topk_select(scores, ld, row_len, rows, ld, k, idx, w, st), "topk select");
+  return hip_status(launch_topk(scores, ld, const_cast<int32_t*>(row_len), rows, ld, k, idx, w, st), "topk");
 }
 
 int32_t run_mla(const dsa_batch* batch, const dsa_cache* cache, const void* q, const int32_t* idx, int32_t k,
@@ -172,7 +169,7 @@ int32_t dsa_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_
   if (ld > INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "rows longer than 2^31 scores");
   const size_t need = dsa_workspace_size(DSA_WS_TOPK, rows, ld, k, 0);
   if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "topk needs %zu workspace bytes", need);
-  return run_topk(scores, ld, row_len, rows, k, idx, ws, false, static_cast<hipStream_t>(stream));
+  return run_topk(scores, ld, row_len, rows, k, idx, ws, static_cast<hipStream_t>(stream));
 }
 
 static int32_t mla_entry(bool split, const dsa_batch* batch, const dsa_cache* cache, const void* q,
@@ -220,11 +217,7 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
   const int64_t ld = decode_ld(batch->max_ctx);
   int32_t* idx = idx_out ? idx_out : p.idx;
   const TopkWs tw = topk_ws_carve(p.topk, rows, ld);
-  // 1. clear the first-digit histograms, derive visible lengths
-  if ((r = hip_status(launch_topk_clear(tw, rows, st, p.row_len, batch->ctx_len, batch->rows_per_request),
-                      "decode clear")))
-    return r;
-  // 2. score
+  // 1. score
   ScoreArgs a;
   a.q = q_idx;
   a.q_scale = nullptr;
@@ -239,9 +232,12 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
   a.ld = ld;
   if ((r = hip_status(launch_index_score(a, batch->num_requests, batch->max_ctx, false, st), "decode score")))
     return r;
-  // 3. select: first-digit histogram, threshold, winners
-  if ((r = run_topk(p.scores, ld, p.row_len, rows, k, idx, p.topk, true, st))) return r;
-  // 4. attend
+  // 2. select (the visible lengths are derived on the way)
+  if ((r = hip_status(launch_topk(p.scores, ld, p.row_len, rows, ld, k, idx, tw, st, batch->ctx_len,
+                                  batch->rows_per_request),
+                      "decode topk")))
+    return r;
+  // 3. attend
   return run_mla(batch, cache, q_mla, idx, k, softmax_scale, out, lse, p.mla, true, st);
 }
 

@@ -25,27 +25,21 @@ struct ScoreArgs {
 hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st);
 
 struct TopkWs {
-  uint32_t* hist;   // [rows][2048] first digit of every score
-  uint32_t* hist2;  // [rows][2048] second digit of the first-digit candidates
-  uint32_t* ctr;    // [rows][4]: {emitted above the first-digit bin, candidates}
-  uint2* cand;      // [rows][cap] (ordered key, position)
+  uint32_t* thresh;  // [rows] sampled ordered-key threshold
+  uint32_t* ctr;     // [rows] candidates collected
+  uint2* cand;       // [rows][cap] (ordered key, position)
   int32_t cap;
 };
 
 size_t topk_ws_bytes(int rows, int64_t max_len);
 TopkWs topk_ws_carve(void* ws, int rows, int64_t max_len);
 
-// Zero the histogram and counters of `rows` rows. With row_len != null, also
-// writes row_len[row] = ctx_len[row / R] - R + row % R + 1 (visible tokens).
-hipError_t launch_topk_clear(const TopkWs& w, int rows, hipStream_t st, int32_t* row_len = nullptr,
-                             const int32_t* ctx_len = nullptr, int R = 1);
-// First-digit histogram of each row (skipped when the scorer already built it).
-hipError_t launch_topk_hist(const float* scores, int64_t ld, const int32_t* row_len, int rows, int64_t max_len,
-                            const TopkWs& w, hipStream_t st);
-// Selection given the histogram: emits everything above the threshold digit,
-// collects the threshold digit's candidates, then resolves them exactly.
-hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* row_len, int rows, int64_t max_len,
-                              int k, int32_t* idx, const TopkWs& w, hipStream_t st);
+// idx[row][0..k) = the k largest scores[row][0..row_len[row]) (positions,
+// unordered; -1 padding for rows shorter than k). With ctx_len != null the
+// visible lengths are derived (ctx_len[row / R] - R + row % R + 1) and
+// written to row_len first; otherwise row_len is read.
+hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int rows, int64_t max_len, int k,
+                       int32_t* idx, const TopkWs& w, hipStream_t st, const int32_t* ctx_len = nullptr, int R = 1);
 
 struct MlaArgs {
   const uint16_t* q;        // bf16 [rows][16][576]

@@ -45,7 +45,8 @@ def test_workspace_sizes(lib):
     assert lib.dsa_workspace_size(_lib.DSA_WS_TOPK, 0, 1000, 2048, 16) == 0
     t1 = lib.dsa_workspace_size(_lib.DSA_WS_TOPK, 64, 32768, 2048, 16)
     t2 = lib.dsa_workspace_size(_lib.DSA_WS_TOPK, 64, 1 << 20, 2048, 16)
-    assert 0 < t1 < t2
+    assert 0 < t1 <= t2
+    assert lib.dsa_workspace_size(_lib.DSA_WS_TOPK, 128, 32768, 2048, 16) > t1
     d = lib.dsa_workspace_size(_lib.DSA_WS_DECODE, 64, 32768, 2048, 16)
     assert d >= 64 * 32768 * 4 + 64 * 2048 * 4  # scores + selection at least
     assert lib.dsa_workspace_size(_lib.DSA_WS_MLA_PREFILL, 4096, 0, 2048, 16) == 0
