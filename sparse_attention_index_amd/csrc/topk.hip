@@ -164,6 +164,33 @@ DSA_DEV void load_bins(const uint32_t* hist, uint32_t (&c)[8]) {
 
 DSA_DEV uint64_t composite(uint32_t key, uint32_t pos) { return ((uint64_t)key << 32) | (uint64_t)(~pos); }
 
+struct MinMaxLds {
+  uint64_t lo[kT / 64];
+  uint64_t hi[kT / 64];
+};
+
+// Workgroup-wide (min, max) of one value per thread; one barrier pair.
+DSA_DEV void block_minmax(uint64_t& lo, uint64_t& hi, MinMaxLds& s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t a = __shfl_xor(lo, off), b = __shfl_xor(hi, off);
+    lo = a < lo ? a : lo;
+    hi = b > hi ? b : hi;
+  }
+  if (lane == 0) {
+    s.lo[wave] = lo;
+    s.hi[wave] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kT / 64; ++w) {
+    lo = s.lo[w] < lo ? s.lo[w] : lo;
+    hi = s.hi[w] > hi ? s.hi[w] : hi;
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------------ sample
 
 __global__ __launch_bounds__(kT) void topk_sample_kernel(const float* __restrict__ scores, int64_t ld,
@@ -305,55 +332,137 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(const float* __restrict
 
 // ------------------------------------------------------------------ final
 
+static constexpr int kBinLds = 2048;  // threshold-bin elements kept for the last steps
+
 struct FinalLds {
   ScanLds scan;
+  MinMaxLds mm;
   uint32_t emitted;
+  uint32_t nbin;
   uint32_t hist[kHistBins];
+  uint64_t bin[kBinLds];
   uint2 elems[kFinalLds];
 };
 
 // Emit the positions of the k largest composites among `count` elements
-// (comp_at(i) gives element i's composite): 11-bit radix steps from the top
-// until the threshold bin holds exactly the elements still needed.
+// (comp_at(i) gives element i's composite).
+//  1. The radix digits start below the bits every element shares (the
+//     survivors of one row have close scores: their top bits would all fall
+//     in one bin).
+//  2. One 11-bit step finds the bin b holding the k-th largest; a second
+//     pass emits everything above b and gathers b's elements into LDS.
+//  3. Further 11-bit steps over the gathered elements resolve the rest
+//     (without the gather, when b holds more than kBinLds elements).
 template <class CompAt>
 DSA_DEV void select_top(FinalLds& L, int64_t count, int k, int32_t* __restrict__ out, CompAt comp_at) {
   const int t = threadIdx.x;
+  uint64_t lo = ~0ull, hi = 0;
+  for (int64_t i = t; i < count; i += kT) {
+    const uint64_t c = comp_at(i);
+    lo = c < lo ? c : lo;
+    hi = c > hi ? c : hi;
+  }
+  block_minmax(lo, hi, L.mm);
+  if (t == 0) {
+    L.emitted = 0;
+    L.nbin = 0;
+  }
+  // the composites are distinct, so lo == hi only for a single element
+  if (lo == hi) {
+    if (t == 0) out[0] = (int32_t)~(uint32_t)hi;
+    return;
+  }
+  int shift = 64 - __clzll((long long)(lo ^ hi));  // bits below the shared prefix
+  uint64_t prefix = shift == 64 ? 0 : hi >> shift;
   uint32_t need = (uint32_t)k;
-  uint64_t prefix = 0;
-  int shift = 64;
+
+  // step over all elements
+  int width = shift < 11 ? shift : 11;
+  int lo_bit = shift - width;
+  for (int i = t; i < kHistBins; i += kT) L.hist[i] = 0;
+  __syncthreads();
+  for (int64_t i = t; i < count; i += kT)
+    atomicAdd(&L.hist[(comp_at(i) >> lo_bit) & ((1ull << width) - 1)], 1u);
+  __syncthreads();
+  uint32_t cnt[8];
+  load_bins(L.hist, cnt);
+  Thresh th = block_threshold(cnt, need, L.scan);
+  const uint64_t b = (shift == 64 ? 0 : prefix << width) | (uint64_t)th.digit;  // top (64 - b_shift) bits
+  const int b_shift = lo_bit;
+  const bool gather = th.at <= (uint32_t)kBinLds;
+  // emit everything above b; gather b
+  for (int64_t base = 0; base < count; base += kT) {
+    const int64_t i = base + t;
+    uint64_t c = 0;
+    bool above = false, at = false;
+    if (i < count) {
+      c = comp_at(i);
+      above = (c >> b_shift) > b;
+      at = gather && (c >> b_shift) == b;
+    }
+    const uint32_t slot = wave_append(&L.emitted, above);
+    if (above) out[slot] = (int32_t)~(uint32_t)c;
+    const uint32_t bslot = wave_append(&L.nbin, at);
+    if (at) L.bin[bslot] = c;
+  }
+  __syncthreads();
+  need -= th.above;
+  const uint32_t emitted0 = th.above;
+  if (th.at == need) {  // all of b is selected
+    if (gather) {
+      for (uint32_t i = t; i < th.at; i += kT) out[emitted0 + i] = (int32_t)~(uint32_t)L.bin[i];
+    } else {
+      if (t == 0) L.emitted = 0;
+      __syncthreads();
+      for (int64_t base = 0; base < count; base += kT) {
+        const int64_t i = base + t;
+        bool take = false;
+        uint64_t c = 0;
+        if (i < count) {
+          c = comp_at(i);
+          take = (c >> b_shift) == b;
+        }
+        const uint32_t slot = wave_append(&L.emitted, take);
+        if (take) out[emitted0 + slot] = (int32_t)~(uint32_t)c;
+      }
+    }
+    return;
+  }
+  // resolve within b: element j of the bin is bin_at(j)
+  const int64_t nb = gather ? (int64_t)th.at : count;
+  auto bin_at = [&](int64_t j) -> uint64_t { return gather ? L.bin[j] : comp_at(j); };
+  prefix = b;
+  shift = lo_bit;
   while (true) {
-    const int width = shift < 11 ? shift : 11;
-    const int lo = shift - width;
-    const uint64_t mask = (1ull << width) - 1;
+    width = shift < 11 ? shift : 11;
+    lo_bit = shift - width;
     for (int i = t; i < kHistBins; i += kT) L.hist[i] = 0;
     __syncthreads();
-    for (int64_t i = t; i < count; i += kT) {
-      const uint64_t c = comp_at(i);
-      if (shift == 64 || (c >> shift) == prefix) atomicAdd(&L.hist[(c >> lo) & mask], 1u);
+    for (int64_t j = t; j < nb; j += kT) {
+      const uint64_t c = bin_at(j);
+      if ((c >> shift) == prefix) atomicAdd(&L.hist[(c >> lo_bit) & ((1ull << width) - 1)], 1u);
     }
     __syncthreads();
-    uint32_t cnt[8];
     load_bins(L.hist, cnt);
-    const Thresh th = block_threshold(cnt, need, L.scan);
+    th = block_threshold(cnt, need, L.scan);
     need -= th.above;
-    prefix = (shift == 64 ? 0 : prefix << width) | (uint64_t)th.digit;
-    shift = lo;
+    prefix = (prefix << width) | (uint64_t)th.digit;
+    shift = lo_bit;
     if (th.at == need || shift == 0) break;
   }
   if (t == 0) L.emitted = 0;
   __syncthreads();
-  // every element whose top (64 - shift) bits are at least the resolved prefix
-  for (int64_t base = 0; base < count; base += kT) {
-    const int64_t i = base + t;
+  // elements of b whose top (64 - shift) bits are at least the resolved prefix
+  for (int64_t base = 0; base < nb; base += kT) {
+    const int64_t j = base + t;
     bool take = false;
-    uint32_t pos = 0;
-    if (i < count) {
-      const uint64_t c = comp_at(i);
-      take = (c >> shift) >= prefix;
-      pos = ~(uint32_t)c;
+    uint64_t c = 0;
+    if (j < nb) {
+      c = bin_at(j);
+      take = (gather || (c >> b_shift) == b) && (c >> shift) >= prefix;
     }
     const uint32_t slot = wave_append(&L.emitted, take);
-    if (take && slot < (uint32_t)k) out[slot] = (int32_t)pos;
+    if (take && emitted0 + slot < (uint32_t)k) out[emitted0 + slot] = (int32_t)~(uint32_t)c;
   }
 }
 
@@ -376,7 +485,19 @@ __global__ __launch_bounds__(kT) void topk_final_kernel(const float* __restrict_
   const uint2* gcand = w.cand + (size_t)row * w.cap;
   if (count >= (uint32_t)k && count <= (uint32_t)w.cap) {
     if (count <= (uint32_t)kFinalLds) {
-      for (uint32_t i = t; i < count; i += kT) L.elems[i] = gcand[i];
+      for (uint32_t base = 0; base < count; base += 8 * kT) {  // eight loads in flight per lane
+        uint2 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t i = base + t + j * kT;
+          v[j] = i < count ? gcand[i] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t i = base + t + j * kT;
+          if (i < count) L.elems[i] = v[j];
+        }
+      }
       __syncthreads();
       select_top(L, count, k, out, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); });
     } else {
