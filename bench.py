@@ -12,7 +12,7 @@ hit in the 256 MB Infinity Cache.
 Prints one JSON line. `value` is context tokens scanned per second (the sum
 of the requests' context lengths per step over the step time); rows/s, the
 whole-step HBM fraction, per-stage times, the roofline of the dominant kernel
-(the indexer scorer, timed over back-to-back launches with HIP events on its
+(the indexer scorer, each stage-wise launch bracketed by HIP events on its
 stream) and a float64 CPU oracle baseline are added beside it.
 
 `--workload prefill_4096_on_128k` measures a prefill chunk instead (FP8-query
@@ -129,20 +129,6 @@ def cpu_baseline(workload_name, budget_s):
     }
 
 
-def time_launches(torch, fn, n):
-    """Average time of n back-to-back calls of fn(i) on the current stream, from HIP events
-    recorded on that stream (the host stays ahead: the GPU is kept busy while it enqueues)."""
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(5e7))
-    ev0.record()
-    for i in range(n):
-        fn(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    return 1e3 * ev0.elapsed_time(ev1) / n
-
-
 def stage_times(torch, stages, n):
     """Per-stage event times when the stages run in order, repeated n times."""
     evs = {s: [] for s, _ in stages}
@@ -241,9 +227,10 @@ def run_decode(args, torch, dsa, traffic, cfg):
 
     stage_us = stage_times(torch, [("score", score), ("topk", topk), ("attend", attend)], n_stage)
 
-    # ---- dominant kernel: the indexer scorer (one kernel per dsa_index_score call; its share
-    # of the step grows with context). Average launch time of back-to-back launches.
-    score_us = time_launches(torch, score, n_stage)
+    # ---- dominant kernel: the indexer scorer (one kernel per dsa_index_score call, so the
+    # events around each stage-wise call bracket exactly that kernel; its share of the step
+    # grows with context)
+    score_us = stage_us["score"]
     dom_bytes = traffic.scorer_bytes(lens, R)
     achieved = dom_bytes / (score_us * 1e-6) / 1e9
 
@@ -337,7 +324,7 @@ def run_prefill(args, torch, dsa, traffic, cfg):
     ms_step = ev0.elapsed_time(ev1) / args.steps
     n_stage = min(args.steps, 10)
     stage_us = stage_times(torch, [("score", score), ("topk", topk), ("attend", attend)], n_stage)
-    score_us = time_launches(torch, score, n_stage)
+    score_us = stage_us["score"]
     flops = traffic.scorer_flops([L], R)
     tflops = flops / (score_us * 1e-6) / 1e12
     sec = ms_step * 1e-3

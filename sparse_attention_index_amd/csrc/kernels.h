@@ -25,9 +25,8 @@ struct ScoreArgs {
 hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st);
 
 struct TopkWs {
-  uint32_t* thresh;  // [rows] sampled ordered-key threshold
-  uint32_t* ctr;     // [rows] candidates collected
-  uint2* cand;       // [rows][cap] (ordered key, position)
+  uint32_t* cnt;  // [rows][64] candidates each filter workgroup found
+  uint2* cand;    // [rows][cap] (ordered key, position), one region per filter workgroup
   int32_t cap;
 };
 
@@ -36,8 +35,8 @@ TopkWs topk_ws_carve(void* ws, int rows, int64_t max_len);
 
 // idx[row][0..k) = the k largest scores[row][0..row_len[row]) (positions,
 // unordered; -1 padding for rows shorter than k). With ctx_len != null the
-// visible lengths are derived (ctx_len[row / R] - R + row % R + 1) and
-// written to row_len first; otherwise row_len is read.
+// visible lengths are derived (ctx_len[row / R] - R + row % R + 1) and also
+// written to row_len; otherwise row_len is read.
 hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int rows, int64_t max_len, int k,
                        int32_t* idx, const TopkWs& w, hipStream_t st, const int32_t* ctx_len = nullptr, int R = 1);
 

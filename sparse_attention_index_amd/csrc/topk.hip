@@ -10,40 +10,41 @@
 // ~position, which is unique: larger score first, then lower position. The
 // top k composites are a unique set, the same on every run.
 //
-// Kernels, all on one stream:
-//  sample  one workgroup per row reads 8,192 scores in 64 evenly spaced runs
-//          of 128 and takes a threshold T a little below the score rank that
-//          should leave ~1.25k elements of the row above it (rows of at most
-//          kTakeAll elements keep everything); it also zeroes the row's
-//          candidate counter and, in the fused decode, writes the row's
-//          visible length;
-//  filter  several workgroups per row stream the row once with 16-byte loads
-//          and compact every (key, position) with key >= T into the row's
-//          candidate buffer: LDS lists, one global atomic per workgroup;
-//  final   one workgroup per row radix-selects the k largest composites
-//          among the candidates (in LDS when they fit). The answer is exact
+// Two kernels on one stream:
+//  filter  several workgroups per row. Each first derives the same threshold
+//          T from the same sample of the row: a sixteenth of its scores
+//          (2,048 to 8,192) in evenly spaced runs of 128; T sits a little
+//          below the sampled rank that should leave ~1.25k elements of the
+//          row above it (rows of at most kTakeAll elements keep everything).
+//          It then streams its slice of the row once with 16-byte loads and
+//          compacts every (key, position) with key >= T into LDS, then into
+//          its own region of the row's candidate buffer, with its count in
+//          its own slot: no global atomics and nothing to clear first;
+//  final   one workgroup per row gathers the slices' candidates into LDS
+//          and radix-selects the k largest composites. The answer is exact
 //          whenever at least k candidates were collected, because every
 //          element of the top k is then >= T; if fewer than k or more than
-//          the buffer holds arrived, the workgroup selects over the whole row
-//          instead. The sample only decides the speed, never the result.
+//          fit arrived, the workgroup selects over the whole row instead.
+//          The sample only decides the speed, never the result.
 #include "common.h"
 #include "kernels.h"
 
 namespace dsa {
 
-static constexpr int kT = 256;           // threads per workgroup
-static constexpr int kSample = 8192;     // scores sampled per row
-static constexpr int kRuns = 64;         // ... in this many evenly spaced runs
-static constexpr int kRunLen = kSample / kRuns;
+static constexpr int kT = 256;           // threads per filter workgroup
+static constexpr int kTF = 1024;         // threads per final workgroup
+static constexpr int kSample = 8192;     // most scores sampled per row
+static constexpr int kRunLen = 128;      // ... in evenly spaced runs of this length
 static constexpr int kTakeAll = 8192;    // rows up to this length keep every element
 static constexpr int kListLds = 4096;    // candidates a filter workgroup buffers in LDS
-static constexpr int kFinalLds = 8192;   // candidates the final kernel holds in LDS
+static constexpr int kFinalLds = 12288;  // candidates the final kernel holds in LDS
+static constexpr int kMaxSlices = 64;    // filter workgroups per row at most
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Candidate slots per row: 64 MB spread over the rows, clamped to
 // [8192, 32768] (at least kTakeAll, well above the ~1.25k + margin that a
-// sampled threshold leaves).
+// sampled threshold leaves); each filter slice of a row owns cap / slices.
 static int32_t cand_cap(int rows) {
   int64_t c = (int64_t)(64ll << 20) / 8 / (rows > 0 ? rows : 1);
   if (c > 32768) c = 32768;
@@ -53,17 +54,15 @@ static int32_t cand_cap(int rows) {
 
 size_t topk_ws_bytes(int rows, int64_t max_len) {
   (void)max_len;
-  return align_up((size_t)rows * 4, 256) * 2 + align_up((size_t)rows * cand_cap(rows) * 8, 256);
+  return align_up((size_t)rows * kMaxSlices * 4, 256) + align_up((size_t)rows * cand_cap(rows) * 8, 256);
 }
 
 TopkWs topk_ws_carve(void* ws, int rows, int64_t max_len) {
   (void)max_len;
   TopkWs w;
   char* p = static_cast<char*>(ws);
-  w.thresh = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)rows * 4, 256);
-  w.ctr = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)rows * 4, 256);
+  w.cnt = reinterpret_cast<uint32_t*>(p);
+  p += align_up((size_t)rows * kMaxSlices * 4, 256);
   w.cand = reinterpret_cast<uint2*>(p);
   w.cap = cand_cap(rows);
   return w;
@@ -116,18 +115,22 @@ struct Thresh {
   uint32_t at;     // elements in that bin
 };
 
+template <int NT>
 struct ScanLds {
-  uint32_t wsum[kT / 64];
+  uint32_t wsum[NT / 64];
   uint32_t res[3];
 };
 
-// Thread t owns bins [8t, 8t+8) with counts c[]; need >= 1 and at most the
-// total. Finds d with count(bins > d) < need <= count(bins >= d). Two barriers.
-DSA_DEV Thresh block_threshold(const uint32_t (&c)[8], uint32_t need, ScanLds& s) {
+// Thread t of NT owns bins [B t, B t + B) (B = 2048 / NT) with counts c[];
+// need >= 1 and at most the total. Finds d with count(bins > d) < need <=
+// count(bins >= d). Two barriers.
+template <int NT>
+DSA_DEV Thresh block_threshold(const uint32_t (&c)[kHistBins / NT], uint32_t need, ScanLds<NT>& s) {
+  constexpr int B = kHistBins / NT;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   uint32_t mine = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) mine += c[i];
+  for (int i = 0; i < B; ++i) mine += c[i];
   uint32_t suf = mine;  // inclusive suffix sum over the wave's lanes
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -138,12 +141,12 @@ DSA_DEV Thresh block_threshold(const uint32_t (&c)[8], uint32_t need, ScanLds& s
   if (t == 0) s.res[0] = s.res[1] = s.res[2] = 0;
   __syncthreads();
   uint32_t above = suf - mine;
-  for (int w = wave + 1; w < kT / 64; ++w) above += s.wsum[w];
+  for (int w = wave + 1; w < NT / 64; ++w) above += s.wsum[w];
   if (above < need && need <= above + mine) {
 #pragma unroll
-    for (int i = 7; i >= 0; --i) {
+    for (int i = B - 1; i >= 0; --i) {
       if (above < need && need <= above + c[i]) {
-        s.res[0] = 8 * t + i;
+        s.res[0] = B * t + i;
         s.res[1] = above;
         s.res[2] = c[i];
       }
@@ -156,21 +159,25 @@ DSA_DEV Thresh block_threshold(const uint32_t (&c)[8], uint32_t need, ScanLds& s
   return r;
 }
 
-// Bins of an 11-bit digit: thread t reads its eight counters.
-DSA_DEV void load_bins(const uint32_t* hist, uint32_t (&c)[8]) {
+// Bins of an 11-bit digit: thread t reads its counters.
+template <int NT>
+DSA_DEV void load_bins(const uint32_t* hist, uint32_t (&c)[kHistBins / NT]) {
+  constexpr int B = kHistBins / NT;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = hist[8 * threadIdx.x + i];
+  for (int i = 0; i < B; ++i) c[i] = hist[B * threadIdx.x + i];
 }
 
 DSA_DEV uint64_t composite(uint32_t key, uint32_t pos) { return ((uint64_t)key << 32) | (uint64_t)(~pos); }
 
+template <int NT>
 struct MinMaxLds {
-  uint64_t lo[kT / 64];
-  uint64_t hi[kT / 64];
+  uint64_t lo[NT / 64];
+  uint64_t hi[NT / 64];
 };
 
 // Workgroup-wide (min, max) of one value per thread; one barrier pair.
-DSA_DEV void block_minmax(uint64_t& lo, uint64_t& hi, MinMaxLds& s) {
+template <int NT>
+DSA_DEV void block_minmax(uint64_t& lo, uint64_t& hi, MinMaxLds<NT>& s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -184,100 +191,106 @@ DSA_DEV void block_minmax(uint64_t& lo, uint64_t& hi, MinMaxLds& s) {
   }
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < kT / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     lo = s.lo[w] < lo ? s.lo[w] : lo;
     hi = s.hi[w] > hi ? s.hi[w] : hi;
   }
   __syncthreads();
 }
 
-// ------------------------------------------------------------------ sample
+// ------------------------------------------------------------------ filter
 
-__global__ __launch_bounds__(kT) void topk_sample_kernel(const float* __restrict__ scores, int64_t ld,
-                                                        int32_t* __restrict__ row_len, const int32_t* ctx_len,
-                                                        int R, int k, TopkWs w) {
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ ScanLds scan;
+// Visible length of a row: from row_len, or derived in the fused decode.
+DSA_DEV int64_t visible_len(const int32_t* row_len, const int32_t* ctx_len, int R, int row) {
+  return ctx_len ? (int64_t)ctx_len[row / R] - R + row % R + 1 : (int64_t)row_len[row];
+}
+
+struct FilterLds {
+  ScanLds<kT> scan;
+  uint32_t cnt;
+  union {
+    uint32_t hist[kHistBins];
+    uint2 list[kListLds];
+  } u;
+};
+
+// The ordered-key threshold of a row (the same in every workgroup of it).
+DSA_DEV uint32_t sample_threshold(const float* __restrict__ s, int64_t n, int k, FilterLds& L) {
   const int t = threadIdx.x;
-  const int row = blockIdx.x;
-  int64_t n;
-  if (ctx_len) {  // fused decode: derive and publish the visible length
-    n = ctx_len[row / R] - R + row % R + 1;
-    if (t == 0) row_len[row] = (int32_t)n;
-  } else {
-    n = row_len[row];
-  }
-  if (t == 0) w.ctr[row] = 0;
-  if (n <= kTakeAll) {  // keep every element (also covers n <= k)
-    if (t == 0) w.thresh[row] = 0u;
-    return;
-  }
-  // Sample j (thread t takes j = t + 256 i) is element (j % 128) of run j / 128.
-  const float* s = scores + (size_t)row * ld;
+  if (n <= kTakeAll) return 0u;  // keep every element
+  // ns samples (a sixteenth of the row, 2048 to 8192): sample j (thread t
+  // takes j = t + 256 i) is element (j % 128) of run j / 128, the runs
+  // evenly spaced over the row.
+  const int64_t ns_want = (n / 16) & ~(int64_t)(8 * kT - 1);
+  const int ns = ns_want < 8 * kT ? 8 * kT : (ns_want > kSample ? kSample : (int)ns_want);
+  const int runs = ns / kRunLen;
+  const int per = ns / kT;  // 8, 16, 24 or 32
   uint32_t key[kSample / kT];
 #pragma unroll
-  for (int i = 0; i < kSample / kT; ++i) {
-    const int j = t + kT * i;
-    const int64_t start = (int64_t)(j / kRunLen) * (n - kRunLen) / (kRuns - 1);
-    key[i] = ordered_key(s[start + j % kRunLen]);
+  for (int g = 0; g < kSample / kT / 8; ++g) {
+    if (8 * g < per) {
+#pragma unroll
+      for (int i = 8 * g; i < 8 * g + 8; ++i) {
+        const int j = t + kT * i;
+        const int64_t start = (int64_t)(j / kRunLen) * (n - kRunLen) / (runs - 1);
+        key[i] = ordered_key(s[start + j % kRunLen]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 8 * g; i < 8 * g + 8; ++i) key[i] = 0u;
+    }
   }
   // Rank m of the threshold among the samples: the sampled share of 1.25k,
   // plus 32 so that a sample short of the true k-th score stays very unlikely.
-  const double share = (double)kSample / (double)n;
+  const double share = (double)ns / (double)n;
   uint32_t m = (uint32_t)(1.25 * k * share) + 32u;
-  if (m > (uint32_t)kSample) m = kSample;
+  if (m > (uint32_t)ns) m = ns;
   // Two 11-bit radix steps on the keys: T is the lower edge of the 22-bit
   // prefix bin that holds the m-th largest sample.
   uint32_t prefix = 0;
   for (int step = 0; step < 2; ++step) {
     const int shift = step == 0 ? 21 : 10;
-    for (int i = t; i < kHistBins; i += kT) hist[i] = 0;
+    for (int i = t; i < kHistBins; i += kT) L.u.hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kSample / kT; ++i)
-      if (step == 0 || (key[i] >> 21) == prefix) atomicAdd(&hist[(key[i] >> shift) & (kHistBins - 1)], 1u);
+      if (i < per && (step == 0 || (key[i] >> 21) == prefix))
+        atomicAdd(&L.u.hist[(key[i] >> shift) & (kHistBins - 1)], 1u);
     __syncthreads();
-    uint32_t c[8];
-    load_bins(hist, c);
-    const Thresh th = block_threshold(c, m, scan);
+    uint32_t c[kHistBins / kT];
+    load_bins<kT>(L.u.hist, c);
+    const Thresh th = block_threshold<kT>(c, m, L.scan);
     m -= th.above;
     prefix = step == 0 ? (uint32_t)th.digit : (prefix << 11) | (uint32_t)th.digit;
   }
-  if (t == 0) w.thresh[row] = prefix << 10;
+  return prefix << 10;
 }
-
-// ------------------------------------------------------------------ filter
-
-struct FilterLds {
-  uint32_t cnt;
-  uint32_t base;
-  uint2 list[kListLds];
-};
 
 template <bool VEC>
 __global__ __launch_bounds__(kT) void topk_filter_kernel(const float* __restrict__ scores, int64_t ld,
-                                                        const int32_t* __restrict__ row_len, int slice, int k,
-                                                        TopkWs w) {
+                                                        int32_t* __restrict__ row_len, const int32_t* ctx_len,
+                                                        int R, int slice, int k, TopkWs w) {
   __shared__ FilterLds L;
   const int t = threadIdx.x;
   const int row = blockIdx.y;
-  const int64_t n = row_len[row];
+  const int64_t n = visible_len(row_len, ctx_len, R, row);
+  if (ctx_len && blockIdx.x == 0 && t == 0) row_len[row] = (int32_t)n;  // published for the caller
   if (n <= k) return;  // the final kernel emits every position
+  const float* s = scores + (size_t)row * ld;
+  const uint32_t T = sample_threshold(s, n, k, L);
   const int64_t s0 = (int64_t)blockIdx.x * slice;
   const int64_t s1 = s0 + slice < n ? s0 + slice : n;
-  const uint32_t T = w.thresh[row];
-  uint32_t* ctr = w.ctr + row;
-  uint2* gcand = w.cand + (size_t)row * w.cap;
-  const float* s = scores + (size_t)row * ld;
+  const uint32_t sub = (uint32_t)(w.cap / gridDim.x);  // this slice's share of the row's buffer
+  uint2* gcand = w.cand + (size_t)row * w.cap + (size_t)blockIdx.x * sub;
   if (t == 0) L.cnt = 0;
   __syncthreads();
 
   // Each lane classifies 16 scores per step into a bitmask; one LDS atomic
-  // per wave reserves the slots (uniform trip counts).
+  // per wave reserves the slots (uniform trip counts). The next step's
+  // scores are loaded before the current ones are classified.
   const int lane = t & 63, wave = t >> 6;
-  for (int64_t base = s0; base < s1; base += 16 * kT) {
+  auto load_step = [&](int64_t base, float (&v)[16]) {
     const int64_t wbase = base + 1024 * wave + 4 * lane;  // element (q, e): wbase + 256 q + e
-    float v[16];
     if (VEC) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -294,12 +307,19 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(const float* __restrict
         v[j] = i < s1 ? s[i] : 0.f;
       }
     }
+  };
+  float cur[16], nxt[16];
+  if (s0 < s1) load_step(s0, cur);
+  for (int64_t base = s0; base < s1; base += 16 * kT) {
+    const bool more = base + 16 * kT < s1;
+    if (more) load_step(base + 16 * kT, nxt);
+    const int64_t wbase = base + 1024 * wave + 4 * lane;
     uint32_t cmask = 0;
     uint32_t keys[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int64_t i = wbase + 256 * (j >> 2) + (j & 3);
-      keys[j] = ordered_key(v[j]);
+      keys[j] = ordered_key(cur[j]);
       cmask |= (uint32_t)(i < s1 && keys[j] >= T) << j;
     }
     uint32_t tc;
@@ -309,25 +329,22 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(const float* __restrict
     while (cmask) {
       const int j = __builtin_ctz(cmask);
       cmask &= cmask - 1;
-      const uint2 e = make_uint2(keys[j], (uint32_t)(wbase + 256 * (j >> 2) + (j & 3)));
-      if (slot < (uint32_t)kListLds) {
-        L.list[slot] = e;
-      } else {  // LDS list full: straight to the row's buffer
-        const uint32_t gs = atomicAdd(ctr, 1u);
-        if (gs < (uint32_t)w.cap) gcand[gs] = e;
-      }
+      if (slot < (uint32_t)kListLds)
+        L.u.list[slot] = make_uint2(keys[j], (uint32_t)(wbase + 256 * (j >> 2) + (j & 3)));
       ++slot;
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
     }
   }
   __syncthreads();
-  if (t == 0) {
-    const uint32_t nc = L.cnt < (uint32_t)kListLds ? L.cnt : (uint32_t)kListLds;
-    L.base = nc ? atomicAdd(ctr, nc) : 0;
-    L.cnt = nc;
-  }
-  __syncthreads();
-  for (uint32_t i = t; i < L.cnt; i += kT)
-    if (L.base + i < (uint32_t)w.cap) gcand[L.base + i] = L.list[i];
+  // The true count is published even when it overflowed the LDS list or the
+  // slice's region: the final kernel then falls back to the whole row.
+  const uint32_t nc = L.cnt;
+  const uint32_t keep = nc <= (uint32_t)kListLds && nc <= sub ? nc : 0u;
+  for (uint32_t i = t; i < keep; i += kT) gcand[i] = L.u.list[i];
+  if (t == 0) w.cnt[(size_t)row * kMaxSlices + blockIdx.x] = nc;
 }
 
 // ------------------------------------------------------------------ final
@@ -335,10 +352,13 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(const float* __restrict
 static constexpr int kBinLds = 2048;  // threshold-bin elements kept for the last steps
 
 struct FinalLds {
-  ScanLds scan;
-  MinMaxLds mm;
+  ScanLds<kTF> scan;
+  MinMaxLds<kTF> mm;
   uint32_t emitted;
   uint32_t nbin;
+  uint32_t off[kMaxSlices];
+  uint32_t total;
+  uint32_t bad;
   uint32_t hist[kHistBins];
   uint64_t bin[kBinLds];
   uint2 elems[kFinalLds];
@@ -357,12 +377,12 @@ template <class CompAt>
 DSA_DEV void select_top(FinalLds& L, int64_t count, int k, int32_t* __restrict__ out, CompAt comp_at) {
   const int t = threadIdx.x;
   uint64_t lo = ~0ull, hi = 0;
-  for (int64_t i = t; i < count; i += kT) {
+  for (int64_t i = t; i < count; i += kTF) {
     const uint64_t c = comp_at(i);
     lo = c < lo ? c : lo;
     hi = c > hi ? c : hi;
   }
-  block_minmax(lo, hi, L.mm);
+  block_minmax<kTF>(lo, hi, L.mm);
   if (t == 0) {
     L.emitted = 0;
     L.nbin = 0;
@@ -379,19 +399,19 @@ DSA_DEV void select_top(FinalLds& L, int64_t count, int k, int32_t* __restrict__
   // step over all elements
   int width = shift < 11 ? shift : 11;
   int lo_bit = shift - width;
-  for (int i = t; i < kHistBins; i += kT) L.hist[i] = 0;
+  for (int i = t; i < kHistBins; i += kTF) L.hist[i] = 0;
   __syncthreads();
-  for (int64_t i = t; i < count; i += kT)
+  for (int64_t i = t; i < count; i += kTF)
     atomicAdd(&L.hist[(comp_at(i) >> lo_bit) & ((1ull << width) - 1)], 1u);
   __syncthreads();
-  uint32_t cnt[8];
-  load_bins(L.hist, cnt);
-  Thresh th = block_threshold(cnt, need, L.scan);
+  uint32_t cnt[kHistBins / kTF];
+  load_bins<kTF>(L.hist, cnt);
+  Thresh th = block_threshold<kTF>(cnt, need, L.scan);
   const uint64_t b = (shift == 64 ? 0 : prefix << width) | (uint64_t)th.digit;  // top (64 - b_shift) bits
   const int b_shift = lo_bit;
   const bool gather = th.at <= (uint32_t)kBinLds;
   // emit everything above b; gather b
-  for (int64_t base = 0; base < count; base += kT) {
+  for (int64_t base = 0; base < count; base += kTF) {
     const int64_t i = base + t;
     uint64_t c = 0;
     bool above = false, at = false;
@@ -410,11 +430,11 @@ DSA_DEV void select_top(FinalLds& L, int64_t count, int k, int32_t* __restrict__
   const uint32_t emitted0 = th.above;
   if (th.at == need) {  // all of b is selected
     if (gather) {
-      for (uint32_t i = t; i < th.at; i += kT) out[emitted0 + i] = (int32_t)~(uint32_t)L.bin[i];
+      for (uint32_t i = t; i < th.at; i += kTF) out[emitted0 + i] = (int32_t)~(uint32_t)L.bin[i];
     } else {
       if (t == 0) L.emitted = 0;
       __syncthreads();
-      for (int64_t base = 0; base < count; base += kT) {
+      for (int64_t base = 0; base < count; base += kTF) {
         const int64_t i = base + t;
         bool take = false;
         uint64_t c = 0;
@@ -436,15 +456,15 @@ DSA_DEV void select_top(FinalLds& L, int64_t count, int k, int32_t* __restrict__
   while (true) {
     width = shift < 11 ? shift : 11;
     lo_bit = shift - width;
-    for (int i = t; i < kHistBins; i += kT) L.hist[i] = 0;
+    for (int i = t; i < kHistBins; i += kTF) L.hist[i] = 0;
     __syncthreads();
-    for (int64_t j = t; j < nb; j += kT) {
+    for (int64_t j = t; j < nb; j += kTF) {
       const uint64_t c = bin_at(j);
       if ((c >> shift) == prefix) atomicAdd(&L.hist[(c >> lo_bit) & ((1ull << width) - 1)], 1u);
     }
     __syncthreads();
-    load_bins(L.hist, cnt);
-    th = block_threshold(cnt, need, L.scan);
+    load_bins<kTF>(L.hist, cnt);
+    th = block_threshold<kTF>(cnt, need, L.scan);
     need -= th.above;
     prefix = (prefix << width) | (uint64_t)th.digit;
     shift = lo_bit;
@@ -453,7 +473,7 @@ DSA_DEV void select_top(FinalLds& L, int64_t count, int k, int32_t* __restrict__
   if (t == 0) L.emitted = 0;
   __syncthreads();
   // elements of b whose top (64 - shift) bits are at least the resolved prefix
-  for (int64_t base = 0; base < nb; base += kT) {
+  for (int64_t base = 0; base < nb; base += kTF) {
     const int64_t j = base + t;
     bool take = false;
     uint64_t c = 0;
@@ -469,43 +489,62 @@ DSA_DEV void select_top(FinalLds& L, int64_t count, int k, int32_t* __restrict__
 // One workgroup per row (a kernel boundary orders the filter's writes before
 // these reads; a device-scope fence per workgroup would write back each
 // XCD's L2).
-__global__ __launch_bounds__(kT) void topk_final_kernel(const float* __restrict__ scores, int64_t ld,
-                                                       const int32_t* __restrict__ row_len, int k,
-                                                       int32_t* __restrict__ idx, TopkWs w) {
+__global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict__ scores, int64_t ld,
+                                                       const int32_t* __restrict__ row_len, const int32_t* ctx_len,
+                                                       int R, int slices, int k, int32_t* __restrict__ idx,
+                                                       TopkWs w) {
   __shared__ FinalLds L;
   const int t = threadIdx.x;
   const int row = blockIdx.x;
-  const int64_t n = row_len[row];
+  const int64_t n = visible_len(row_len, ctx_len, R, row);
   int32_t* out = idx + (size_t)row * k;
   if (n <= k) {  // every visible position is selected; the rest is padding
-    for (int64_t i = t; i < k; i += kT) out[i] = i < n ? (int32_t)i : -1;
+    for (int64_t i = t; i < k; i += kTF) out[i] = i < n ? (int32_t)i : -1;
     return;
   }
-  const uint32_t count = w.ctr[row];
-  const uint2* gcand = w.cand + (size_t)row * w.cap;
-  if (count >= (uint32_t)k && count <= (uint32_t)w.cap) {
-    if (count <= (uint32_t)kFinalLds) {
-      for (uint32_t base = 0; base < count; base += 8 * kT) {  // eight loads in flight per lane
-        uint2 v[8];
+  // slices' counts and their offsets in LDS: lane t of wave 0 owns slice t
+  const uint32_t sub = (uint32_t)(w.cap / slices);
+  if (t < 64) {
+    const uint32_t c = t < slices ? w.cnt[(size_t)row * kMaxSlices + t] : 0u;
+    const uint64_t bad = __ballot(c > sub || c > (uint32_t)kListLds);
+    uint32_t incl = c;  // inclusive scan over the wave
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t i = base + t + j * kT;
-          v[j] = i < count ? gcand[i] : make_uint2(0u, 0u);
-        }
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t x = __shfl_up(incl, d);
+      if (t >= d) incl += x;
+    }
+    L.off[t] = incl - c;
+    if (t == 63) L.total = incl;
+    if (t == 0) L.bad = bad != 0;
+  }
+  __syncthreads();
+  const uint32_t count = L.total;
+  if (!L.bad && count >= (uint32_t)k && count <= (uint32_t)kFinalLds) {
+    // element i sits in the last slice whose offset is <= i; eight loads in
+    // flight per lane
+    const uint2* base = w.cand + (size_t)row * w.cap;
+    for (uint32_t b0 = 0; b0 < count; b0 += 8 * kTF) {
+      uint2 v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t i = base + t + j * kT;
-          if (i < count) L.elems[i] = v[j];
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t i = b0 + t + j * kTF;
+        v[j] = make_uint2(0u, 0u);
+        if (i < count) {
+          int sl = 0;
+#pragma unroll
+          for (int step = kMaxSlices / 2; step >= 1; step >>= 1)
+            if (sl + step < slices && L.off[sl + step] <= i) sl += step;
+          v[j] = base[(size_t)sl * sub + (i - L.off[sl])];
         }
       }
-      __syncthreads();
-      select_top(L, count, k, out, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); });
-    } else {
-      select_top(L, count, k, out, [&](int64_t i) {
-        const uint2 e = gcand[i];
-        return composite(e.x, e.y);
-      });
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t i = b0 + t + j * kTF;
+        if (i < count) L.elems[i] = v[j];
+      }
     }
+    __syncthreads();
+    select_top(L, count, k, out, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); });
   } else {  // the sample missed: select over the whole row
     const float* s = scores + (size_t)row * ld;
     select_top(L, n, k, out, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
@@ -520,26 +559,26 @@ static bool vec_ok(const float* scores, int64_t ld) {
 
 hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int rows, int64_t max_len, int k,
                        int32_t* idx, const TopkWs& w, hipStream_t st, const int32_t* ctx_len, int R) {
-  hipLaunchKernelGGL(topk_sample_kernel, dim3(rows), dim3(kT), 0, st, scores, ld, row_len, ctx_len, R, k, w);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // Filter: enough workgroups to cover the GPU twice, at least 4096 scores each.
+  // Filter: enough workgroups to cover the GPU twice, at least 4096 scores
+  // and at most kMaxSlices workgroups per row.
   int64_t want = (512 + rows - 1) / rows;
   const int64_t max_slices = (max_len + 4095) / 4096;
   if (want > max_slices) want = max_slices;
+  if (want > kMaxSlices) want = kMaxSlices;
   if (want < 1) want = 1;
   int64_t slice = (max_len + want - 1) / want;
   slice = (slice + 4095) / 4096 * 4096;
   const int ns = (int)((max_len + slice - 1) / slice);
   if (vec_ok(scores, ld))
-    hipLaunchKernelGGL(topk_filter_kernel<true>, dim3(ns, rows), dim3(kT), 0, st, scores, ld, row_len, (int)slice,
-                       k, w);
-  else
-    hipLaunchKernelGGL(topk_filter_kernel<false>, dim3(ns, rows), dim3(kT), 0, st, scores, ld, row_len,
+    hipLaunchKernelGGL(topk_filter_kernel<true>, dim3(ns, rows), dim3(kT), 0, st, scores, ld, row_len, ctx_len, R,
                        (int)slice, k, w);
-  e = hipGetLastError();
+  else
+    hipLaunchKernelGGL(topk_filter_kernel<false>, dim3(ns, rows), dim3(kT), 0, st, scores, ld, row_len, ctx_len,
+                       R, (int)slice, k, w);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_final_kernel, dim3(rows), dim3(kT), 0, st, scores, ld, row_len, k, idx, w);
+  hipLaunchKernelGGL(topk_final_kernel, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, ctx_len, R, ns, k, idx,
+                     w);
   return hipGetLastError();
 }
 
