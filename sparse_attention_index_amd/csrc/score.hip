@@ -78,6 +78,19 @@ DSA_DEV int key_chunk_off(int n, int j) { return n * kIdxDim + ((j ^ ((n >> 1) &
 // negative integers. The operands are finite MFMA sums.
 DSA_DEV float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// Wave priority from the workgroup's progress: 3 over its first quarter of
+// pages down to 0 over its last. Several workgroups share each SIMD and the
+// oldest wave wins ties, so without this the first workgroup placed on a CU
+// races ahead and the last one finishes the kernel alone; with it, the
+// workgroups that lag get issued first and all finish at about the same time.
+DSA_DEV void set_progress_priority(int i, int n) {
+  const int lvl = (4 * (n - i)) / (n + 1);
+  if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
+  else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Byte offset past every row's visible prefix: buffer stores there are dropped.
 static constexpr uint32_t kPastEnd = 0x80000000u;
 
@@ -309,6 +322,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
 
     if constexpr (!PIPE) {
       for (int i = 0; i < n_my; ++i) {
+        if ((i & 7) == 0) set_progress_priority(i, n_my);
         wait_page(i);
         lds_barrier();  // page i is in LDS; the slot of page i - 1 is free
         if constexpr (role == kCopier) {
@@ -339,6 +353,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
       float ks1 = 0.f;
       int blk_prev = -1;
       for (int i = 0; i < n_my; ++i) {
+        if ((i & 7) == 0) set_progress_priority(i, n_my);
         wait_page(i);
         lds_barrier();  // page i is in LDS; the slot of page i - 1 is free
         if constexpr (role == kCopier) {

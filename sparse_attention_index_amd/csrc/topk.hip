@@ -12,14 +12,15 @@
 //
 // Two kernels on one stream:
 //  filter  several workgroups per row. Each first derives the same threshold
-//          T from the same sample of the row: a sixteenth of its scores
-//          (2,048 to 8,192) in evenly spaced runs of 128; T sits a little
+//          T from the same sample of the row: 2,048 or 4,096 of its scores
+//          in evenly spaced runs of 128; T sits a little
 //          below the sampled rank that should leave ~1.25k elements of the
 //          row above it (rows of at most kTakeAll elements keep everything).
 //          It then streams its slice of the row once with 16-byte loads and
-//          compacts every (key, position) with key >= T into LDS, then into
-//          its own region of the row's candidate buffer, with its count in
-//          its own slot: no global atomics and nothing to clear first;
+//          compacts every (key, position) with key >= T into LDS (overflow
+//          straight to global), then into its own region of the row's
+//          candidate buffer, with its count in its own slot: no global
+//          atomics and nothing to clear first;
 //  final   one workgroup per row gathers the slices' candidates into LDS
 //          and radix-selects the k largest composites. The answer is exact
 //          whenever at least k candidates were collected, because every
@@ -33,7 +34,7 @@ namespace dsa {
 
 static constexpr int kT = 256;           // threads per filter workgroup
 static constexpr int kTF = 1024;         // threads per final workgroup
-static constexpr int kSample = 8192;     // most scores sampled per row
+static constexpr int kSample = 4096;     // most scores sampled per row
 static constexpr int kRunLen = 128;      // ... in evenly spaced runs of this length
 static constexpr int kTakeAll = 8192;    // rows up to this length keep every element
 static constexpr int kListLds = 4096;    // candidates a filter workgroup buffers in LDS
@@ -218,47 +219,44 @@ struct FilterLds {
 DSA_DEV uint32_t sample_threshold(const float* __restrict__ s, int64_t n, int k, FilterLds& L) {
   const int t = threadIdx.x;
   if (n <= kTakeAll) return 0u;  // keep every element
-  // ns samples (a sixteenth of the row, 2048 to 8192): sample j (thread t
-  // takes j = t + 256 i) is element (j % 128) of run j / 128, the runs
-  // evenly spaced over the row.
-  const int64_t ns_want = (n / 16) & ~(int64_t)(8 * kT - 1);
-  const int ns = ns_want < 8 * kT ? 8 * kT : (ns_want > kSample ? kSample : (int)ns_want);
+  // ns samples (2048, or 4096 past 256K elements): sample j (thread t takes
+  // j = t + 256 i) is element (j % 128) of run j / 128, the runs evenly
+  // spaced over the row.
+  const int ns = n > (1 << 18) ? 4096 : 2048;
   const int runs = ns / kRunLen;
-  const int per = ns / kT;  // 8, 16, 24 or 32
+  const int per = ns / kT;  // 8 or 16
   uint32_t key[kSample / kT];
 #pragma unroll
-  for (int g = 0; g < kSample / kT / 8; ++g) {
-    if (8 * g < per) {
-#pragma unroll
-      for (int i = 8 * g; i < 8 * g + 8; ++i) {
-        const int j = t + kT * i;
-        const int64_t start = (int64_t)(j / kRunLen) * (n - kRunLen) / (runs - 1);
-        key[i] = ordered_key(s[start + j % kRunLen]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 8 * g; i < 8 * g + 8; ++i) key[i] = 0u;
+  for (int i = 0; i < kSample / kT; ++i) {
+    key[i] = 0u;
+    if (i < 8 || per > 8) {
+      const int j = t + kT * i;
+      const int64_t start = (int64_t)(j / kRunLen) * (n - kRunLen) / (runs - 1);
+      key[i] = ordered_key(s[start + j % kRunLen]);
     }
   }
-  // Rank m of the threshold among the samples: the sampled share of 1.25k,
-  // plus 32 so that a sample short of the true k-th score stays very unlikely.
-  const double share = (double)ns / (double)n;
-  uint32_t m = (uint32_t)(1.25 * k * share) + 32u;
+  // Rank m of the threshold among the samples: the samples expected above
+  // the k-th score of the row (e = k ns / n) times 1.25, plus 3 standard
+  // deviations of that count (sqrt e) and 8, so that a threshold above the
+  // k-th score (too few candidates) stays below about one in a million.
+  const double e = (double)k * ns / (double)n;
+  uint32_t m = (uint32_t)(1.25 * e + 3.0 * __builtin_sqrt(e)) + 8u;
   if (m > (uint32_t)ns) m = ns;
   // Two 11-bit radix steps on the keys: T is the lower edge of the 22-bit
   // prefix bin that holds the m-th largest sample.
   uint32_t prefix = 0;
+  uint32_t* hist = L.u.hist;
   for (int step = 0; step < 2; ++step) {
     const int shift = step == 0 ? 21 : 10;
-    for (int i = t; i < kHistBins; i += kT) L.u.hist[i] = 0;
+    for (int i = t; i < kHistBins; i += kT) hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kSample / kT; ++i)
-      if (i < per && (step == 0 || (key[i] >> 21) == prefix))
-        atomicAdd(&L.u.hist[(key[i] >> shift) & (kHistBins - 1)], 1u);
+      if ((i < 8 || per > 8) && (step == 0 || (key[i] >> 21) == prefix))
+        atomicAdd(&hist[(key[i] >> shift) & (kHistBins - 1)], 1u);
     __syncthreads();
     uint32_t c[kHistBins / kT];
-    load_bins<kT>(L.u.hist, c);
+    load_bins<kT>(hist, c);
     const Thresh th = block_threshold<kT>(c, m, L.scan);
     m -= th.above;
     prefix = step == 0 ? (uint32_t)th.digit : (prefix << 11) | (uint32_t)th.digit;
@@ -329,8 +327,9 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(const float* __restrict
     while (cmask) {
       const int j = __builtin_ctz(cmask);
       cmask &= cmask - 1;
-      if (slot < (uint32_t)kListLds)
-        L.u.list[slot] = make_uint2(keys[j], (uint32_t)(wbase + 256 * (j >> 2) + (j & 3)));
+      const uint2 e = make_uint2(keys[j], (uint32_t)(wbase + 256 * (j >> 2) + (j & 3)));
+      if (slot < (uint32_t)kListLds) L.u.list[slot] = e;  // the rest of the region takes the overflow
+      else if (slot < sub) gcand[slot] = e;
       ++slot;
     }
     if (more) {
@@ -339,10 +338,10 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(const float* __restrict
     }
   }
   __syncthreads();
-  // The true count is published even when it overflowed the LDS list or the
-  // slice's region: the final kernel then falls back to the whole row.
+  // The true count is published even when it overflowed the slice's region:
+  // the final kernel then falls back to the whole row.
   const uint32_t nc = L.cnt;
-  const uint32_t keep = nc <= (uint32_t)kListLds && nc <= sub ? nc : 0u;
+  const uint32_t keep = nc <= sub ? (nc < (uint32_t)kListLds ? nc : (uint32_t)kListLds) : 0u;
   for (uint32_t i = t; i < keep; i += kT) gcand[i] = L.u.list[i];
   if (t == 0) w.cnt[(size_t)row * kMaxSlices + blockIdx.x] = nc;
 }
@@ -506,7 +505,7 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
   const uint32_t sub = (uint32_t)(w.cap / slices);
   if (t < 64) {
     const uint32_t c = t < slices ? w.cnt[(size_t)row * kMaxSlices + t] : 0u;
-    const uint64_t bad = __ballot(c > sub || c > (uint32_t)kListLds);
+    const uint64_t bad = __ballot(c > sub);
     uint32_t incl = c;  // inclusive scan over the wave
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
