@@ -26,6 +26,9 @@ FLAGS = [
     "-fPIC",
     # keep hipcc from forming packed fp32 math on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: accumulators parked in AGPRs cost one
+    # v_accvgpr_read per element before the scorer's epilogue can use them
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{os.path.join(ROOT, 'include')}",
     "-Wno-unused-command-line-argument",
 ]
