@@ -158,11 +158,10 @@ DSA_DEV float load_query(const ScoreArgs& a, size_t row, int n, int g, i32x8 (&A
 enum WaveRole { kCopier, kFlusher };
 
 template <int RPW, bool QFP8>
-__global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void score_kernel(ScoreArgs a) {
   constexpr int ROWS = 4 * RPW;
   constexpr int NT = QFP8 ? 1 : 2;  // E4M3 terms per query value
-  constexpr bool PIPE = RPW <= 2;   // software-pipelined halves (see below)
-  constexpr int LAG = PIPE ? 2 : 1;  // a page's scores are complete LAG barriers later
+  constexpr int LAG = 2;             // a page's scores are complete two barriers later
   __shared__ __attribute__((aligned(16))) uint8_t key_s[kRing][kKeyBytes];
   __shared__ __attribute__((aligned(16))) float ks_s[kRing][kBlock];
   __shared__ int32_t tbl_s[kMaxWgPages];
@@ -221,10 +220,6 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
     const int bytes = gr < nr ? 4 * (pos0 + gr + 1) : 0;
     return __builtin_amdgcn_make_buffer_rsrc(a.scores + (row0 + gv) * a.ld, (short)0, bytes, 0x00020000);
   };
-  __amdgpu_buffer_rsrc_t rs[ROWS];  // used by the storing wave
-#pragma unroll
-  for (int gr = 0; gr < ROWS; ++gr) rs[gr] = row_rsrc(gr);
-  constexpr int HALF = (RPW + 1) / 2;  // lanes < 32 total row j, lanes >= 32 row j + HALF
 
   // Copy j of a page moves LDS chunks 64j .. 64j+63 of the page's swizzled
   // layout: lane l fetches the global chunk that belongs at LDS chunk 64j + l.
@@ -249,51 +244,54 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
 
   auto run = [&](auto role_tag) {
     constexpr WaveRole role = decltype(role_tag)::value;
-    // head-weighted ReLU sum of one 32-key half (keys 32h .. 32h+31 of the
-    // i-th page, block blk) for all rows of the wave, and its stores
-    auto epilogue = [&](const f32x16(&acc)[RPW], float ks, int i, int blk, int h) {
-      float p[RPW];
+    // The rows of a wave are taken in groups of G (one or two): a unit of
+    // work is one 32-key half of a page for one group. Lanes < 32 end up
+    // with the group's first row, lanes >= 32 with its second.
+    constexpr int G = RPW < 2 ? RPW : 2;
+    constexpr int NG = RPW / G;
+    // head-weighted ReLU sum of one unit (keys 32h .. 32h+31 of the i-th
+    // page, rows gi*G ..) into the LDS score buffer
+    auto epilogue = [&](const f32x16(&acc)[G], float ks, int i, int h, int gi) {
+      float p[G];
 #pragma unroll
-      for (int rr = 0; rr < RPW; ++rr) {
+      for (int r = 0; r < G; ++r) {
         float sum = 0.f;
         if constexpr (RPW == 1) {
 #pragma unroll
-          for (int i2 = 0; i2 < 16; ++i2) sum = __builtin_fmaf(wv[i2], relu(acc[rr][i2]), sum);
+          for (int i2 = 0; i2 < 16; ++i2) sum = __builtin_fmaf(wv[i2], relu(acc[r][i2]), sum);
         } else {
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 w4 = *reinterpret_cast<const f32x4*>(&w_s[wr0 + rr][8 * q4 + 4 * g]);
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(&w_s[wr0 + gi * G + r][8 * q4 + 4 * g]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sum = __builtin_fmaf(w4[e], relu(acc[rr][4 * q4 + e]), sum);
+            for (int e = 0; e < 4; ++e) sum = __builtin_fmaf(w4[e], relu(acc[r][4 * q4 + e]), sum);
           }
         }
-        p[rr] = sum;
+        p[r] = sum;
       }
-  #pragma unroll
-      for (int j = 0; j < HALF; ++j) {
-        const float v = halves_sum_pair(p[j], (j + HALF < RPW) ? p[j + HALF] : p[j]) * ks;
-        // both lane halves write; with one row per wave they write the same value
-        const int rr = RPW == 1 ? 0 : j + g * HALF;
-        if (i >= 0) sc_s[i % (LAG + 1)][wr0 + rr][32 * h + n] = v;
-      }
+      const float v = halves_sum_pair(p[0], p[G - 1]) * ks;
+      // both lane halves write; with one row per group they write the same value
+      const int rr = gi * G + (G == 2 ? g : 0);
+      if (i >= 0) sc_s[i % (LAG + 1)][wr0 + rr][32 * h + n] = v;
     };
     // wave 3: store the group's scores of page i (complete once barrier i + LAG passed)
     auto flush = [&](int i) {
       const uint32_t off = 4u * (uint32_t)(((int)blockIdx.x + i * stride) * kBlock + lane);
 #pragma unroll
-      for (int gr = 0; gr < ROWS; ++gr)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_s[i % (LAG + 1)][gr][lane]), rs[gr], off, 0, 0);
+      for (int gr = 0; gr < ROWS; ++gr)  // descriptors rebuilt here: scalar work, no registers held
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_s[i % (LAG + 1)][gr][lane]), row_rsrc(gr), off, 0,
+                                              0);
     };
-    auto mfma_half = [&](f32x16(&acc)[RPW], const i32x8(&Bh)[2]) {
+    auto mfma_unit = [&](f32x16(&acc)[G], const i32x8(&Bh)[2], int gi) {
 #pragma unroll
-      for (int rr = 0; rr < RPW; ++rr) {
-        acc[rr] = f32x16{};
+      for (int r = 0; r < G; ++r) {
+        acc[r] = f32x16{};
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int s = 0; s < 2; ++s)
-            acc[rr] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[rr][t][s], Bh[s], acc[rr], 0, 0, 0, 127, 0,
-                                                                      127);
+            acc[r] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[gi * G + r][t][s], Bh[s], acc[r], 0, 0, 0,
+                                                                     127, 0, 127);
       }
     };
     auto load_b = [&](const uint8_t* kbuf, int h, i32x8(&Bh)[2]) {
@@ -320,65 +318,44 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
       for (int i = 0; i < kRing - 1 && i < n_my; ++i) issue(i);
     }
 
-    if constexpr (!PIPE) {
-      for (int i = 0; i < n_my; ++i) {
-        if ((i & 7) == 0) set_progress_priority(i, n_my);
-        wait_page(i);
-        lds_barrier();  // page i is in LDS; the slot of page i - 1 is free
-        if constexpr (role == kCopier) {
-          if (i + kRing - 1 < n_my) issue(i + kRing - 1);
-        }
-        if constexpr (role == kFlusher) {
-          if (i >= LAG) flush(i - LAG);
-        }
-        const uint8_t* kbuf = key_s[i % kRing];
-        const float* ksb = ks_s[i % kRing];
-        const int blk = (int)blockIdx.x + i * stride;
-#pragma unroll 1
-        for (int h = 0; h < 2; ++h) {
-          i32x8 B[2];
-          load_b(kbuf, h, B);
-          f32x16 acc[RPW];
-          mfma_half(acc, B);
-          epilogue(acc, ksb[32 * h + n], i, blk, h);
-        }
-      }
-    } else {
-      // Software pipeline over 32-key halves: the MFMAs of one half run
-      // while the VALU epilogue of the previous half (of this page or the
-      // previous one) is issued between them.
-      f32x16 acc0[RPW], acc1[RPW];
+    // Software pipeline over units: the MFMAs of one unit run while the
+    // VALU epilogue of the unit before it (of this page or, for the first
+    // unit, the last unit of the previous page) is issued between them.
+    f32x16 acc[2][G];
 #pragma unroll
-      for (int rr = 0; rr < RPW; ++rr) acc1[rr] = f32x16{};
-      float ks1 = 0.f;
-      int blk_prev = -1;
-      for (int i = 0; i < n_my; ++i) {
-        if ((i & 7) == 0) set_progress_priority(i, n_my);
-        wait_page(i);
-        lds_barrier();  // page i is in LDS; the slot of page i - 1 is free
-        if constexpr (role == kCopier) {
-          if (i + kRing - 1 < n_my) issue(i + kRing - 1);
-        }
-        if constexpr (role == kFlusher) {
-          if (i >= LAG) flush(i - LAG);
-        }
-        const uint8_t* kbuf = key_s[i % kRing];
-        const float* ksb = ks_s[i % kRing];
-        const int blk = (int)blockIdx.x + i * stride;
-        i32x8 B0[2], B1[2];
-        load_b(kbuf, 0, B0);
-        load_b(kbuf, 1, B1);
-        const float ks0 = ksb[n];
-        const float ks1_next = ksb[32 + n];
-        mfma_half(acc0, B0);
-        epilogue(acc1, ks1, i - 1, blk_prev, 1);  // second half of the previous page
-        mfma_half(acc1, B1);
-        epilogue(acc0, ks0, i, blk, 0);
-        ks1 = ks1_next;
-        blk_prev = blk;
+    for (int r = 0; r < G; ++r) acc[1][r] = f32x16{};
+    float ks_prev = 0.f;
+    for (int i = 0; i < n_my; ++i) {
+      if ((i & 7) == 0) set_progress_priority(i, n_my);
+      wait_page(i);
+      lds_barrier();  // page i is in LDS; the slot of page i - 1 is free
+      if constexpr (role == kCopier) {
+        if (i + kRing - 1 < n_my) issue(i + kRing - 1);
       }
-      epilogue(acc1, ks1, n_my - 1, blk_prev, 1);
+      if constexpr (role == kFlusher) {
+        if (i >= LAG) flush(i - LAG);
+      }
+      const uint8_t* kbuf = key_s[i % kRing];
+      const float* ksb = ks_s[i % kRing];
+      // keys of both halves up front for one group per half; with two
+      // groups the second half's keys are read when its first unit starts
+      i32x8 B[NG == 1 ? 2 : 1][2];
+      load_b(kbuf, 0, B[0]);
+      if constexpr (NG == 1) load_b(kbuf, 1, B[NG == 1 ? 1 : 0]);
+      const float ks[2] = {ksb[n], ksb[32 + n]};
+#pragma unroll
+      for (int u = 0; u < 2 * NG; ++u) {  // unit u: half u / NG, group u % NG
+        const int h = u / NG, gi = u % NG;
+        if constexpr (NG > 1) {
+          if (u == NG) load_b(kbuf, 1, B[0]);
+        }
+        mfma_unit(acc[u & 1], B[NG == 1 ? h : 0], gi);
+        if (u == 0) epilogue(acc[1], ks_prev, i - 1, 1, NG - 1);  // last unit of the previous page
+        else epilogue(acc[(u - 1) & 1], ks[(u - 1) / NG], i, (u - 1) / NG, (u - 1) % NG);
+      }
+      ks_prev = ks[1];
     }
+    epilogue(acc[1], ks_prev, n_my - 1, 1, NG - 1);
     __syncthreads();  // the last scores are in LDS
     if constexpr (role == kFlusher) {
       for (int i = max(0, n_my - LAG); i < n_my; ++i) flush(i);
