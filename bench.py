@@ -130,21 +130,18 @@ def cpu_baseline(workload_name, budget_s):
 
 
 def kernel_time(torch, fn, nsets, n=20):
-    """Average launch time of a one-kernel entry point: n launches (rotating over the input
-    sets) captured in a HIP graph, replayed between two events on the replay stream."""
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(n):
-            fn(i % nsets)
+    """Average launch time of a one-kernel entry point: n launches back to back on the current
+    stream (rotating over the input sets) between two events. A GPU-side sleep ahead of them
+    lets the host enqueue all n first, so no host gap falls inside the timed span. Stream order
+    serialises the launches, as inside the decode step."""
+    fn(0)  # untimed
     torch.cuda.synchronize()
-    graph.replay()  # untimed
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        graph.replay()
-        ev1.record(stream)
+    torch.cuda._sleep(int(2e8))
+    ev0.record()
+    for i in range(n):
+        fn(i % nsets)
+    ev1.record()
     torch.cuda.synchronize()
     return 1e3 * ev0.elapsed_time(ev1) / n
 

@@ -71,6 +71,77 @@ TopkWs topk_ws_carve(void* ws, int rows, int64_t max_len) {
 
 // ------------------------------------------------------------------ helpers
 
+// Cross-lane moves through DPP (a VALU operand modifier, a few cycles) rather
+// than ds_bpermute (an LDS round trip of ~300 cycles): lanes whose source is
+// outside the pattern, or whose row is masked off, read 0.
+template <int CTRL, int ROW_MASK = 0xf>
+DSA_DEV uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, true);
+}
+constexpr int kDppXor1 = 0xb1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4e;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane 7 - i within each 8
+constexpr int kDppMirror = 0x140;      // lane 15 - i within each 16
+constexpr int kDppShr1 = 0x111;        // row_shr:n = 0x110 + n
+constexpr int kDppBcast15 = 0x142;     // lane 15 of each row -> the next row
+constexpr int kDppBcast31 = 0x143;     // lane 31 -> rows 2 and 3
+
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele inside rows of 16,
+// then the row totals carried across with the row broadcasts).
+DSA_DEV uint32_t wave_incl_sum(uint32_t x) {
+  x += dpp<kDppShr1>(x);
+  x += dpp<kDppShr1 + 1>(x);
+  x += dpp<kDppShr1 + 3>(x);
+  x += dpp<kDppShr1 + 7>(x);
+  x += dpp<kDppBcast15, 0xa>(x);
+  x += dpp<kDppBcast31, 0xc>(x);
+  return x;
+}
+
+// 64-bit value of lane ^ 1, ^ 2 or the mirrored lane, one DPP move per half.
+template <int CTRL>
+DSA_DEV uint64_t dpp64(uint64_t v) {
+  return ((uint64_t)dpp<CTRL>((uint32_t)(v >> 32)) << 32) | dpp<CTRL>((uint32_t)v);
+}
+
+// Max over the wave, returned in every lane (uniform).
+DSA_DEV uint32_t wave_max32(uint32_t v) {
+  v = max(v, dpp<kDppXor1>(v));
+  v = max(v, dpp<kDppXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));
+  v = max(v, dpp<kDppMirror>(v));
+  return max(max((uint32_t)__builtin_amdgcn_readlane(v, 0), (uint32_t)__builtin_amdgcn_readlane(v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane(v, 32), (uint32_t)__builtin_amdgcn_readlane(v, 48)));
+}
+
+// Min and max over the wave, returned in every lane (uniform).
+DSA_DEV void wave_minmax64(uint64_t& lo, uint64_t& hi) {
+#define DSA_MINMAX_STEP(CTRL)                       \
+  {                                                 \
+    const uint64_t a = dpp64<CTRL>(lo), b = dpp64<CTRL>(hi); \
+    lo = a < lo ? a : lo;                           \
+    hi = b > hi ? b : hi;                           \
+  }
+  DSA_MINMAX_STEP(kDppXor1)
+  DSA_MINMAX_STEP(kDppXor2)
+  DSA_MINMAX_STEP(kDppHalfMirror)
+  DSA_MINMAX_STEP(kDppMirror)
+#undef DSA_MINMAX_STEP
+  // every lane of a row now holds the row's result; combine the four rows
+  uint64_t l = ~0ull, h = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t a = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(lo >> 32), 16 * r) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((uint32_t)lo, 16 * r);
+    const uint64_t b = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(hi >> 32), 16 * r) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((uint32_t)hi, 16 * r);
+    l = a < l ? a : l;
+    h = b > h ? b : h;
+  }
+  lo = l;
+  hi = h;
+}
+
 // Append the predicated lanes of a wave to a counter (LDS or global); returns
 // each predicated lane's slot. One atomic per wave.
 DSA_DEV uint32_t wave_append(uint32_t* counter, bool pred) {
@@ -80,18 +151,19 @@ DSA_DEV uint32_t wave_append(uint32_t* counter, bool pred) {
   const int leader = __ffsll((unsigned long long)mask) - 1;
   uint32_t base = 0;
   if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-  base = __shfl(base, leader);
+  base = __builtin_amdgcn_readlane(base, leader);
   const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
   return base + below;
 }
 
-// Exclusive prefix of small per-lane counts (0..31) over the wave, from five
-// bit-sliced ballots (no LDS traffic); total is the wave sum.
+// Exclusive prefix of small per-lane counts (below 2^BITS) over the wave,
+// from BITS bit-sliced ballots (no LDS traffic); total is the wave sum.
+template <int BITS = 5>
 DSA_DEV uint32_t wave_prefix_small(uint32_t cnt, uint32_t& total) {
   uint32_t pre = 0, tot = 0;
 #pragma unroll
-  for (int bit = 0; bit < 5; ++bit) {
+  for (int bit = 0; bit < BITS; ++bit) {
     const uint64_t m = __ballot((cnt >> bit) & 1u);
     pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << bit;
     tot += (uint32_t)__popcll(m) << bit;
@@ -132,17 +204,15 @@ DSA_DEV Thresh block_threshold(const uint32_t (&c)[kHistBins / NT], uint32_t nee
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < B; ++i) mine += c[i];
-  uint32_t suf = mine;  // inclusive suffix sum over the wave's lanes
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t v = __shfl_down(suf, off);
-    if (lane + off < 64) suf += v;
-  }
-  if (lane == 0) s.wsum[wave] = suf;
+  const uint32_t pre = wave_incl_sum(mine);
+  const uint32_t wtot = __builtin_amdgcn_readlane(pre, 63);
+  if (lane == 0) s.wsum[wave] = wtot;
   if (t == 0) s.res[0] = s.res[1] = s.res[2] = 0;
   __syncthreads();
-  uint32_t above = suf - mine;
-  for (int w = wave + 1; w < NT / 64; ++w) above += s.wsum[w];
+  // bins of the later lanes of this wave, plus the later waves' totals (lane
+  // w < NT / 64 reads wave w's total: one LDS read per lane)
+  const uint32_t later = (lane < NT / 64 && lane > wave) ? s.wsum[lane] : 0u;
+  uint32_t above = wtot - pre + __builtin_amdgcn_readlane(wave_incl_sum(later), 63);
   if (above < need && need <= above + mine) {
 #pragma unroll
     for (int i = B - 1; i >= 0; --i) {
@@ -155,9 +225,9 @@ DSA_DEV Thresh block_threshold(const uint32_t (&c)[kHistBins / NT], uint32_t nee
     }
   }
   __syncthreads();
-  Thresh r{(int)s.res[0], s.res[1], s.res[2]};
-  __syncthreads();
-  return r;
+  // No barrier after this read: every caller passes at least two more
+  // barriers before the next call clears res.
+  return Thresh{(int)s.res[0], s.res[1], s.res[2]};
 }
 
 // Bins of an 11-bit digit: thread t reads its counters.
@@ -180,30 +250,27 @@ struct MinMaxLds {
 template <int NT>
 DSA_DEV void block_minmax(uint64_t& lo, uint64_t& hi, MinMaxLds<NT>& s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t a = __shfl_xor(lo, off), b = __shfl_xor(hi, off);
-    lo = a < lo ? a : lo;
-    hi = b > hi ? b : hi;
-  }
+  wave_minmax64(lo, hi);
   if (lane == 0) {
     s.lo[wave] = lo;
     s.hi[wave] = hi;
   }
   __syncthreads();
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    lo = s.lo[w] < lo ? s.lo[w] : lo;
-    hi = s.hi[w] > hi ? s.hi[w] : hi;
-  }
+  // lane w < NT / 64 takes wave w's result; one more wave reduction
+  lo = lane < NT / 64 ? s.lo[lane] : ~0ull;
+  hi = lane < NT / 64 ? s.hi[lane] : 0ull;
+  wave_minmax64(lo, hi);
   __syncthreads();
 }
 
 // ------------------------------------------------------------------ filter
 
 // Visible length of a row: from row_len, or derived in the fused decode.
-DSA_DEV int64_t visible_len(const int32_t* row_len, const int32_t* ctx_len, int R, int row) {
-  return ctx_len ? (int64_t)ctx_len[row / R] - R + row % R + 1 : (int64_t)row_len[row];
+// Clamped to [0, ld], so that a length beyond the row's storage never turns
+// into an out-of-bounds read.
+DSA_DEV int64_t visible_len(const int32_t* row_len, const int32_t* ctx_len, int R, int row, int64_t ld) {
+  const int64_t n = ctx_len ? (int64_t)ctx_len[row / R] - R + row % R + 1 : (int64_t)row_len[row];
+  return n < 0 ? 0 : (n > ld ? ld : n);
 }
 
 struct FilterLds {
@@ -215,26 +282,37 @@ struct FilterLds {
   } u;
 };
 
-// The ordered-key threshold of a row (the same in every workgroup of it).
-DSA_DEV uint32_t sample_threshold(const float* __restrict__ s, int64_t n, int k, FilterLds& L) {
+// Sampled threshold of a row (the same in every workgroup of it), in two
+// parts so that a caller can issue other loads in between.
+// sample_load: ns samples (2048, or 4096 past 256K elements); sample j
+// (thread t of NT takes j = t + NT i) is element (j % 128) of run j / 128, the
+// runs evenly spaced over the row.
+template <int NT>
+DSA_DEV void sample_load(const float* __restrict__ s, int64_t n, uint32_t (&key)[kSample / NT]) {
   const int t = threadIdx.x;
-  if (n <= kTakeAll) return 0u;  // keep every element
-  // ns samples (2048, or 4096 past 256K elements): sample j (thread t takes
-  // j = t + 256 i) is element (j % 128) of run j / 128, the runs evenly
-  // spaced over the row.
   const int ns = n > (1 << 18) ? 4096 : 2048;
   const int runs = ns / kRunLen;
-  const int per = ns / kT;  // 8 or 16
-  uint32_t key[kSample / kT];
+  const int per = ns / NT;
 #pragma unroll
-  for (int i = 0; i < kSample / kT; ++i) {
+  for (int i = 0; i < kSample / NT; ++i) {
     key[i] = 0u;
-    if (i < 8 || per > 8) {
-      const int j = t + kT * i;
+    if (n > kTakeAll && i < per) {
+      const int j = t + NT * i;
       const int64_t start = (int64_t)(j / kRunLen) * (n - kRunLen) / (runs - 1);
       key[i] = ordered_key(s[start + j % kRunLen]);
     }
   }
+}
+
+// sample_select: the ordered-key threshold T from the samples; every element
+// is kept (T = 0) for rows of at most kTakeAll elements.
+template <int NT>
+DSA_DEV uint32_t sample_select(const uint32_t (&key)[kSample / NT], int64_t n, int k, uint32_t* hist,
+                               ScanLds<NT>& scan) {
+  const int t = threadIdx.x;
+  if (n <= kTakeAll) return 0u;
+  const int ns = n > (1 << 18) ? 4096 : 2048;
+  const int per = ns / NT;
   // Rank m of the threshold among the samples: the samples expected above
   // the k-th score of the row (e = k ns / n) times 1.25, plus 3 standard
   // deviations of that count (sqrt e) and 8, so that a threshold above the
@@ -245,19 +323,18 @@ DSA_DEV uint32_t sample_threshold(const float* __restrict__ s, int64_t n, int k,
   // Two 11-bit radix steps on the keys: T is the lower edge of the 22-bit
   // prefix bin that holds the m-th largest sample.
   uint32_t prefix = 0;
-  uint32_t* hist = L.u.hist;
   for (int step = 0; step < 2; ++step) {
     const int shift = step == 0 ? 21 : 10;
-    for (int i = t; i < kHistBins; i += kT) hist[i] = 0;
+    for (int i = t; i < kHistBins; i += NT) hist[i] = 0;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kSample / kT; ++i)
-      if ((i < 8 || per > 8) && (step == 0 || (key[i] >> 21) == prefix))
+    for (int i = 0; i < kSample / NT; ++i)
+      if (i < per && (step == 0 || (key[i] >> 21) == prefix))
         atomicAdd(&hist[(key[i] >> shift) & (kHistBins - 1)], 1u);
     __syncthreads();
-    uint32_t c[kHistBins / kT];
-    load_bins<kT>(hist, c);
-    const Thresh th = block_threshold<kT>(c, m, L.scan);
+    uint32_t c[kHistBins / NT];
+    load_bins<NT>(hist, c);
+    const Thresh th = block_threshold<NT>(c, m, scan);
     m -= th.above;
     prefix = step == 0 ? (uint32_t)th.digit : (prefix << 11) | (uint32_t)th.digit;
   }
@@ -271,11 +348,13 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(const float* __restrict
   __shared__ FilterLds L;
   const int t = threadIdx.x;
   const int row = blockIdx.y;
-  const int64_t n = visible_len(row_len, ctx_len, R, row);
+  const int64_t n = visible_len(row_len, ctx_len, R, row, ld);
   if (ctx_len && blockIdx.x == 0 && t == 0) row_len[row] = (int32_t)n;  // published for the caller
   if (n <= k) return;  // the final kernel emits every position
   const float* s = scores + (size_t)row * ld;
-  const uint32_t T = sample_threshold(s, n, k, L);
+  uint32_t skey[kSample / kT];
+  sample_load<kT>(s, n, skey);
+  const uint32_t T = sample_select<kT>(skey, n, k, L.u.hist, L.scan);
   const int64_t s0 = (int64_t)blockIdx.x * slice;
   const int64_t s1 = s0 + slice < n ? s0 + slice : n;
   const uint32_t sub = (uint32_t)(w.cap / gridDim.x);  // this slice's share of the row's buffer
@@ -350,16 +429,21 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(const float* __restrict
 
 static constexpr int kBinLds = 2048;  // threshold-bin elements kept for the last steps
 
-struct FinalLds {
+// LDS of select_top (one workgroup of kTF threads).
+struct SelectLds {
   ScanLds<kTF> scan;
   MinMaxLds<kTF> mm;
   uint32_t emitted;
   uint32_t nbin;
+  uint32_t hist[kHistBins];
+  uint64_t bin[kBinLds];
+};
+
+struct FinalLds {
+  SelectLds s;
   uint32_t off[kMaxSlices];
   uint32_t total;
   uint32_t bad;
-  uint32_t hist[kHistBins];
-  uint64_t bin[kBinLds];
   uint2 elems[kFinalLds];
 };
 
@@ -372,16 +456,23 @@ struct FinalLds {
 //     pass emits everything above b and gathers b's elements into LDS.
 //  3. Further 11-bit steps over the gathered elements resolve the rest
 //     (without the gather, when b holds more than kBinLds elements).
+// With have_bounds, [lo0, hi0] is given to hold every composite (the pass
+// that finds the exact extremes is skipped).
 template <class CompAt>
-DSA_DEV void select_top(FinalLds& L, int64_t count, int k, int32_t* __restrict__ out, CompAt comp_at) {
+DSA_DEV void select_top(SelectLds& L, int64_t count, int k, int32_t* __restrict__ out, CompAt comp_at,
+                        bool have_bounds = false, uint64_t lo0 = 0, uint64_t hi0 = 0) {
   const int t = threadIdx.x;
-  uint64_t lo = ~0ull, hi = 0;
-  for (int64_t i = t; i < count; i += kTF) {
-    const uint64_t c = comp_at(i);
-    lo = c < lo ? c : lo;
-    hi = c > hi ? c : hi;
+  uint64_t lo = lo0, hi = hi0;
+  if (!have_bounds) {
+    lo = ~0ull;
+    hi = 0;
+    for (int64_t i = t; i < count; i += kTF) {
+      const uint64_t c = comp_at(i);
+      lo = c < lo ? c : lo;
+      hi = c > hi ? c : hi;
+    }
+    block_minmax<kTF>(lo, hi, L.mm);
   }
-  block_minmax<kTF>(lo, hi, L.mm);
   if (t == 0) {
     L.emitted = 0;
     L.nbin = 0;
@@ -420,16 +511,17 @@ DSA_DEV void select_top(FinalLds& L, int64_t count, int k, int32_t* __restrict__
       at = gather && (c >> b_shift) == b;
     }
     const uint32_t slot = wave_append(&L.emitted, above);
-    if (above) out[slot] = (int32_t)~(uint32_t)c;
+    if (above && slot < (uint32_t)k) out[slot] = (int32_t)~(uint32_t)c;
     const uint32_t bslot = wave_append(&L.nbin, at);
-    if (at) L.bin[bslot] = c;
+    if (at && bslot < (uint32_t)kBinLds) L.bin[bslot] = c;
   }
   __syncthreads();
   need -= th.above;
   const uint32_t emitted0 = th.above;
   if (th.at == need) {  // all of b is selected
     if (gather) {
-      for (uint32_t i = t; i < th.at; i += kTF) out[emitted0 + i] = (int32_t)~(uint32_t)L.bin[i];
+      for (uint32_t i = t; i < th.at && emitted0 + i < (uint32_t)k; i += kTF)
+        out[emitted0 + i] = (int32_t)~(uint32_t)L.bin[i];
     } else {
       if (t == 0) L.emitted = 0;
       __syncthreads();
@@ -442,7 +534,7 @@ DSA_DEV void select_top(FinalLds& L, int64_t count, int k, int32_t* __restrict__
           take = (c >> b_shift) == b;
         }
         const uint32_t slot = wave_append(&L.emitted, take);
-        if (take) out[emitted0 + slot] = (int32_t)~(uint32_t)c;
+        if (take && emitted0 + slot < (uint32_t)k) out[emitted0 + slot] = (int32_t)~(uint32_t)c;
       }
     }
     return;
@@ -495,7 +587,7 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
   __shared__ FinalLds L;
   const int t = threadIdx.x;
   const int row = blockIdx.x;
-  const int64_t n = visible_len(row_len, ctx_len, R, row);
+  const int64_t n = visible_len(row_len, ctx_len, R, row, ld);
   int32_t* out = idx + (size_t)row * k;
   if (n <= k) {  // every visible position is selected; the rest is padding
     for (int64_t i = t; i < k; i += kTF) out[i] = i < n ? (int32_t)i : -1;
@@ -506,12 +598,7 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
   if (t < 64) {
     const uint32_t c = t < slices ? w.cnt[(size_t)row * kMaxSlices + t] : 0u;
     const uint64_t bad = __ballot(c > sub);
-    uint32_t incl = c;  // inclusive scan over the wave
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t x = __shfl_up(incl, d);
-      if (t >= d) incl += x;
-    }
+    const uint32_t incl = wave_incl_sum(c);
     L.off[t] = incl - c;
     if (t == 63) L.total = incl;
     if (t == 0) L.bad = bad != 0;
@@ -543,11 +630,125 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
       }
     }
     __syncthreads();
-    select_top(L, count, k, out, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); });
+    select_top(L.s, count, k, out, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); });
   } else {  // the sample missed: select over the whole row
     const float* s = scores + (size_t)row * ld;
-    select_top(L, n, k, out, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
+    select_top(L.s, n, k, out, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
   }
+}
+
+// ------------------------------------------------------------------ short rows
+
+// Rows of at most kShortMax scores: one workgroup per row holds the whole row
+// in registers (element 4096 q + 4 t + e of the row is key[4 q + e] of thread
+// t), so threshold, filter and selection run in one kernel with no global
+// round trip. Same sample, threshold and exactness argument as above; the
+// survivors go to LDS and select_top picks the k largest.
+static constexpr int kShortPer = 40;                // scores per thread
+static constexpr int kShortMax = kShortPer * kTF;   // 40,960
+
+struct ShortLds {
+  SelectLds f;
+  uint32_t cnt;
+  uint32_t wmax[kTF / 64];
+  uint2 elems[kFinalLds + 1];  // survivors, plus one spare entry taking overflow writes
+};
+
+template <bool VEC>
+__global__ __launch_bounds__(kTF) void topk_short_kernel(const float* __restrict__ scores, int64_t ld,
+                                                       int32_t* __restrict__ row_len, const int32_t* ctx_len, int R,
+                                                       int k, int32_t* __restrict__ idx) {
+  __shared__ ShortLds L;
+  const int t = threadIdx.x;
+  const int row = blockIdx.x;
+  const int n = (int)visible_len(row_len, ctx_len, R, row, ld);  // <= ld <= kShortMax
+  if (ctx_len && t == 0) row_len[row] = n;  // published for the caller
+  int32_t* out = idx + (size_t)row * k;
+  if (n <= k) {
+    for (int i = t; i < k; i += kTF) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* s = scores + (size_t)row * ld;
+  uint32_t skey[kSample / kTF];
+  sample_load<kTF>(s, n, skey);
+  // The row through a buffer descriptor of n scores (one VGPR offset per
+  // lane); groups of 4 (one load) that start past n are not loaded. Scores
+  // at positions >= n become NaN, which no comparison keeps.
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s), (short)0, 4 * n, 0x00020000);
+  float x[kShortPer];
+#pragma unroll
+  for (int q = 0; q < kShortPer / 4; ++q) {
+    if (4096 * q < n) {  // uniform
+      if (VEC) {
+        const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * t, 16384 * q, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[4 * q + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, 16 * t + 4 * e, 16384 * q, 0));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * q + e] = __builtin_nanf("");
+    }
+  }
+  if (t == 0) L.cnt = 0;
+  lds_barrier();  // the counter is cleared before any wave reserves (the row loads stay in flight)
+  const uint32_t T = sample_select<kTF>(skey, n, k, L.f.hist, L.f.scan);
+  // The group holding position n: NaN past n, and with 16-byte loads the
+  // scores of a partial vector read again one by one (the buffer load of a
+  // vector that crosses the end may return zeros).
+#pragma unroll
+  for (int q = 0; q < kShortPer / 4; ++q) {
+    if (4096 * q < n && n < 4096 * q + 4096) {  // uniform
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4096 * q + 4 * t + e;
+        if (i >= n) x[4 * q + e] = __builtin_nanf("");
+        else if (VEC && i >= (n & ~3)) x[4 * q + e] = s[i];
+      }
+    }
+  }
+  // key >= T as a float comparison (scores are not NaN): T is the lower edge
+  // of a bin holding a sampled score, so its float is a number unless T lies
+  // below every number's key, where every score passes.
+  const float Tf = T <= ordered_key(-INFINITY) ? -INFINITY
+                                                : __uint_as_float((T & 0x80000000u) ? (T & 0x7fffffffu) : ~T);
+
+  // survivors -> LDS as (score bits, position): one reservation per wave;
+  // slots past the buffer all land on its spare last entry. The row maximum
+  // bounds the survivors from above for the selection.
+  uint32_t mine = 0;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j) {
+    mine += (uint32_t)(x[j] >= Tf);
+    mx = fmaxf(mx, x[j]);  // NaN operands are ignored
+  }
+  const int lane = t & 63, wave = t >> 6;
+  const uint32_t wmax = wave_max32(ordered_key(mx));
+  if (lane == 0) L.wmax[wave] = wmax;
+  uint32_t total;
+  const uint32_t pre = wave_prefix_small<6>(mine, total);
+  uint32_t slot = wave_reserve(&L.cnt, total) + pre;
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j) {
+    const bool kp = x[j] >= Tf;
+    if (kp) L.elems[slot < (uint32_t)kFinalLds ? slot : (uint32_t)kFinalLds] =
+        make_uint2(__float_as_uint(x[j]), (uint32_t)(4096 * (j >> 2) + 4 * t + (j & 3)));
+    slot += kp;
+  }
+  __syncthreads();
+  const uint32_t count = L.cnt;
+  const uint32_t kmax = wave_max32(lane < kTF / 64 ? L.wmax[lane] : 0u);
+  if (count >= (uint32_t)k && count <= (uint32_t)kFinalLds)
+    select_top(
+        L.f, count, k, out,
+        [&](int64_t i) { return composite(ordered_key(__uint_as_float(L.elems[i].x)), L.elems[i].y); }, true,
+        (uint64_t)T << 32, ((uint64_t)kmax << 32) | 0xffffffffull);
+  else  // the sample missed: select over the whole row
+    select_top(L.f, n, k, out, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
 }
 
 // ------------------------------------------------------------------ launcher
@@ -558,6 +759,15 @@ static bool vec_ok(const float* scores, int64_t ld) {
 
 hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int rows, int64_t max_len, int k,
                        int32_t* idx, const TopkWs& w, hipStream_t st, const int32_t* ctx_len, int R) {
+  if (max_len <= kShortMax) {
+    if (vec_ok(scores, ld))
+      hipLaunchKernelGGL(topk_short_kernel<true>, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, ctx_len, R, k,
+                         idx);
+    else
+      hipLaunchKernelGGL(topk_short_kernel<false>, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, ctx_len, R, k,
+                         idx);
+    return hipGetLastError();
+  }
   // Filter: enough workgroups to cover the GPU twice, at least 4096 scores
   // and at most kMaxSlices workgroups per row.
   int64_t want = (512 + rows - 1) / rows;

@@ -69,8 +69,13 @@ def test_topk_within_band_of_oracle_scores(gpu, name):
         check_topk_band(idx[row], oracle.row_scores(case, row), case.topk, f"{name} row {row}")
 
 
-def _rows_tensor(rows):
-    L = max(len(r) for r in rows) or 1
+# Rows of at most this many scores are selected by the one-kernel path (whole
+# row in registers); longer rows by the filter + final kernels.
+SHORT_MAX = 40960
+
+
+def _rows_tensor(rows, min_ld=0):
+    L = max(max(len(r) for r in rows), min_ld, 1)
     ld = (L + 63) // 64 * 64
     t = torch.zeros((len(rows), ld), dtype=torch.float32)
     for i, r in enumerate(rows):
@@ -78,7 +83,8 @@ def _rows_tensor(rows):
     return t.cuda(), torch.tensor([len(r) for r in rows], dtype=torch.int32).cuda()
 
 
-def test_topk_edge_cases(gpu):
+@pytest.mark.parametrize("path", ["short", "long"])
+def test_topk_edge_cases(gpu, path):
     rng = np.random.default_rng(7)
     rows = [
         np.zeros(10000),  # one bin, more ties than the candidate buffer: full-row path
@@ -91,8 +97,11 @@ def test_topk_edge_cases(gpu):
         np.full(4096, 3.25),  # exactly 2k ties
         np.where(rng.random(300000) < 0.01, 5.0 + rng.random(300000), rng.random(300000)),  # planted cluster
     ]
-    print("\n[case] topk edge rows", [len(r) for r in rows], flush=True)
-    scores, row_len = _rows_tensor(rows)
+    if path == "short":
+        rows = [r[:SHORT_MAX] for r in rows] + [rng.standard_normal(SHORT_MAX - 3)]  # partial last vector
+    print(f"\n[case] topk edge rows ({path})", [len(r) for r in rows], flush=True)
+    scores, row_len = _rows_tensor(rows, min_ld=0 if path == "short" else 2 * SHORT_MAX)
+    assert (scores.shape[1] <= SHORT_MAX) == (path == "short")
     for k in (2048, 1, 1000):
         idx = gpu_topk(scores, row_len, k).cpu().numpy()
         s32 = scores.cpu().numpy()
@@ -100,8 +109,28 @@ def test_topk_edge_cases(gpu):
             check_topk_exact(idx[i], s32[i, : len(r)], k, f"edge row {i} k {k}")
 
 
-def test_topk_all_ties_pick_lowest_positions(gpu):
-    scores, row_len = _rows_tensor([np.ones(9000), np.ones(2500)])
+@pytest.mark.parametrize("L", [SHORT_MAX - 3, 3 * SHORT_MAX + 5])
+def test_topk_unaligned_rows(gpu, L):
+    """Rows that start off a 16-byte boundary, with an odd row stride (the scalar-load variants)."""
+    rng = np.random.default_rng(L)
+    rows = 3
+    base = torch.as_tensor(rng.standard_normal((rows, L + 2)), dtype=torch.float32).cuda()
+    scores = base[:, 1 : L + 1]  # stride L + 2, first element 4 bytes past the allocation start
+    lens = [L, L - 1, 3000]
+    row_len = torch.tensor(lens, dtype=torch.int32).cuda()
+    print(f"\n[case] topk unaligned L={L} stride={scores.stride(0)}", flush=True)
+    for k in (2048, 7):
+        ws = dsa.workspace(dsa.dsa_workspace_size(dsa.DSA_WS_TOPK, rows, scores.stride(0), k))
+        idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+        dsa.dsa_topk(scores, row_len, k, idx, ws)
+        idx_h, s = idx.cpu().numpy(), scores.cpu().numpy()
+        for i, n in enumerate(lens):
+            check_topk_exact(idx_h[i], s[i, :n], k, f"unaligned L {L} row {i} k {k}")
+
+
+@pytest.mark.parametrize("min_ld", [0, 2 * SHORT_MAX])
+def test_topk_all_ties_pick_lowest_positions(gpu, min_ld):
+    scores, row_len = _rows_tensor([np.ones(9000), np.ones(2500)], min_ld=min_ld)
     idx = gpu_topk(scores, row_len, 2048).cpu().numpy()
     assert sorted(idx[0].tolist()) == list(range(2048))
     assert sorted(idx[1].tolist()) == list(range(2048))
