@@ -25,8 +25,10 @@ struct ScoreArgs {
 hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st);
 
 struct TopkWs {
-  uint32_t* cnt;  // [rows][64] candidates each filter workgroup found
-  uint2* cand;    // [rows][cap] (ordered key, position), one region per filter workgroup
+  uint32_t* cnt;   // [rows][64] survivors each slice workgroup found
+  uint32_t* tmax;  // [rows][64] largest ordered key each slice workgroup saw
+  uint32_t* thr;   // [rows] the row's sampled threshold (ordered key)
+  uint2* cand;     // [rows][cap] (ordered key, position), one region per slice workgroup
   int32_t cap;
 };
 

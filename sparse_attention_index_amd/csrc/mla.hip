@@ -291,41 +291,59 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
 }
 
 // Merge split partials: out = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}.
-// Grid (8, rows): workgroup x handles dims [64x, 64x + 64) of all 16 heads.
+// Grid (8, rows): workgroup x handles dims [64x, 64x + 64) of all 16 heads;
+// thread t owns head h = t / 16 and dims 64x + 4 (t % 16) + [0, 4). Every
+// global load is issued up front (the first 8 splits' partial outputs, and
+// the (max, sum) pairs of splits t % 16 + 16 u), so the merge costs one memory
+// round trip; the 16 lanes of a head reduce with DPP.
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaPart part, uint16_t* out_bits, float* lse) {
   __shared__ float wgt_s[64][kMlaHeads];  // per split, per head weight e^{m_s - M} / L
   const int row = blockIdx.y;
-  const int S = part.splits;
-  const float* ml = part.ml + (size_t)row * S * kMlaHeads * 2;
-  if (threadIdx.x < kMlaHeads) {
-    const int h = threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(s * kMlaHeads + h) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float m = ml[(s * kMlaHeads + h) * 2];
-      L += (m == -INFINITY) ? 0.f : ml[(s * kMlaHeads + h) * 2 + 1] * __expf(m - M);
-    }
-    for (int s = 0; s < S; ++s) {
-      const float m = ml[(s * kMlaHeads + h) * 2];
-      wgt_s[s][h] = (L > 0.f && m != -INFINITY) ? __expf(m - M) / L : 0.f;
-    }
-    if (lse && blockIdx.x == 0) lse[(size_t)row * kMlaHeads + h] = L > 0.f ? M + __logf(L) : -INFINITY;
-  }
-  __syncthreads();
-  __bf16* out = reinterpret_cast<__bf16*>(out_bits) + (size_t)row * kMlaHeads * kV;
-  const float* po = part.o + (size_t)row * S * kMlaHeads * kV;
-  // 16 heads x 64 dims = 1024 outputs, 4 per thread (one float4 per split)
-  const int h = threadIdx.x >> 4;
-  const int d = 64 * blockIdx.x + 4 * (threadIdx.x & 15);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(po + ((size_t)s * kMlaHeads + h) * kV + d);
-    const float wgt = wgt_s[s][h];
-    acc += v * wgt;
-  }
+  const int S = part.splits;  // <= 64
+  const int h = threadIdx.x >> 4, j = threadIdx.x & 15;
+  const int d = 64 * blockIdx.x + 4 * j;
+  const float* po = part.o + (size_t)row * S * kMlaHeads * kV + h * kV + d;
+  constexpr size_t kSplitStride = (size_t)kMlaHeads * kV;
+  f32x4 v[8];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) out[h * kV + d + e] = (__bf16)acc[e];
+  for (int u = 0; u < 8; ++u)
+    v[u] = u < S ? *reinterpret_cast<const f32x4*>(po + u * kSplitStride) : f32x4{0.f, 0.f, 0.f, 0.f};
+  const float2* ml = reinterpret_cast<const float2*>(part.ml) + (size_t)row * S * kMlaHeads;
+  float m[4], l[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int s = j + 16 * u;
+    const float2 x = s < S ? ml[s * kMlaHeads + h] : make_float2(-INFINITY, 0.f);
+    m[u] = x.x;
+    l[u] = x.y;
+  }
+  const float M = row_max16(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])));
+  float L = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) L += m[u] == -INFINITY ? 0.f : l[u] * __expf(m[u] - M);
+  L = row_sum16(L);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int s = j + 16 * u;
+    if (s < S) wgt_s[s][h] = (L > 0.f && m[u] != -INFINITY) ? __expf(m[u] - M) / L : 0.f;
+  }
+  if (lse && blockIdx.x == 0 && j == 0) lse[(size_t)row * kMlaHeads + h] = L > 0.f ? M + __logf(L) : -INFINITY;
+  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (u < S) acc += v[u] * wgt_s[u][h];
+  for (int s0 = 8; s0 < S; s0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = s0 + u < S ? *reinterpret_cast<const f32x4*>(po + (s0 + u) * kSplitStride) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) acc += v[u] * wgt_s[s0 + u][h];
+  }
+  __bf16* out = reinterpret_cast<__bf16*>(out_bits) + ((size_t)row * kMlaHeads + h) * kV + d;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = (__bf16)acc[e];
 }
 
 static int splits_for(int rows, int k) {

@@ -32,12 +32,10 @@
 
 namespace dsa {
 
-static constexpr int kT = 256;           // threads per filter workgroup
 static constexpr int kTF = 1024;         // threads per final workgroup
 static constexpr int kSample = 4096;     // most scores sampled per row
 static constexpr int kRunLen = 128;      // ... in evenly spaced runs of this length
 static constexpr int kTakeAll = 8192;    // rows up to this length keep every element
-static constexpr int kListLds = 4096;    // candidates a filter workgroup buffers in LDS
 static constexpr int kFinalLds = 12288;  // candidates the final kernel holds in LDS
 static constexpr int kMaxSlices = 64;    // filter workgroups per row at most
 
@@ -53,9 +51,12 @@ static int32_t cand_cap(int rows) {
   return (int32_t)(c / 64 * 64);
 }
 
+// Workspace: per (row, slice) count and largest key, per row threshold, then
+// the candidate regions.
 size_t topk_ws_bytes(int rows, int64_t max_len) {
   (void)max_len;
-  return align_up((size_t)rows * kMaxSlices * 4, 256) + align_up((size_t)rows * cand_cap(rows) * 8, 256);
+  return 2 * align_up((size_t)rows * kMaxSlices * 4, 256) + align_up((size_t)rows * 4, 256) +
+         align_up((size_t)rows * cand_cap(rows) * 8, 256);
 }
 
 TopkWs topk_ws_carve(void* ws, int rows, int64_t max_len) {
@@ -64,6 +65,10 @@ TopkWs topk_ws_carve(void* ws, int rows, int64_t max_len) {
   char* p = static_cast<char*>(ws);
   w.cnt = reinterpret_cast<uint32_t*>(p);
   p += align_up((size_t)rows * kMaxSlices * 4, 256);
+  w.tmax = reinterpret_cast<uint32_t*>(p);
+  p += align_up((size_t)rows * kMaxSlices * 4, 256);
+  w.thr = reinterpret_cast<uint32_t*>(p);
+  p += align_up((size_t)rows * 4, 256);
   w.cand = reinterpret_cast<uint2*>(p);
   w.cap = cand_cap(rows);
   return w;
@@ -273,46 +278,51 @@ DSA_DEV int64_t visible_len(const int32_t* row_len, const int32_t* ctx_len, int 
   return n < 0 ? 0 : (n > ld ? ld : n);
 }
 
-struct FilterLds {
-  ScanLds<kT> scan;
-  uint32_t cnt;
-  union {
-    uint32_t hist[kHistBins];
-    uint2 list[kListLds];
-  } u;
-};
-
 // Sampled threshold of a row (the same in every workgroup of it), in two
 // parts so that a caller can issue other loads in between.
 // sample_load: ns samples (2048, or 4096 past 256K elements); sample j
 // (thread t of NT takes j = t + NT i) is element (j % 128) of run j / 128, the
 // runs evenly spaced over the row.
 template <int NT>
-DSA_DEV void sample_load(const float* __restrict__ s, int64_t n, uint32_t (&key)[kSample / NT]) {
+DSA_DEV void sample_load(const float* __restrict__ s, int64_t n, uint32_t (&raw)[kSample / NT]) {
   const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kSample / NT; ++i) raw[i] = 0u;
+  if (n <= kTakeAll) return;  // no samples needed (uniform)
   const int ns = n > (1 << 18) ? 4096 : 2048;
-  const int runs = ns / kRunLen;
   const int per = ns / NT;
+  // Run r starts at floor(r span / d), span = n - 128, d = runs - 1 (31 or
+  // 15) = r q + floor(r rem / d) with q, rem = span divided by d, computed
+  // once; r rem < d^2 takes a constant-divisor 32-bit division (a 64-bit
+  // division by a variable would be a long software routine per sample).
+  // Every load is issued before any is used: the raw bits are converted to
+  // keys where they are first needed.
+  const uint32_t span = (uint32_t)(n - kRunLen);  // rows are shorter than 2^31
+  const bool wide = ns == 4096;
+  const uint32_t q = wide ? span / 31u : span / 15u;
+  const uint32_t rem = span - q * (wide ? 31u : 15u);
 #pragma unroll
   for (int i = 0; i < kSample / NT; ++i) {
-    key[i] = 0u;
-    if (n > kTakeAll && i < per) {
-      const int j = t + NT * i;
-      const int64_t start = (int64_t)(j / kRunLen) * (n - kRunLen) / (runs - 1);
-      key[i] = ordered_key(s[start + j % kRunLen]);
-    }
+    const uint32_t j = (uint32_t)(t + NT * i);
+    const uint32_t r = j / kRunLen;
+    const uint32_t start = r * q + (wide ? (r * rem) / 31u : (r * rem) / 15u);
+    const size_t pos = i < per ? (size_t)start + j % kRunLen : 0;  // extra slots re-read position 0
+    raw[i] = __float_as_uint(s[pos]);
   }
 }
 
 // sample_select: the ordered-key threshold T from the samples; every element
 // is kept (T = 0) for rows of at most kTakeAll elements.
 template <int NT>
-DSA_DEV uint32_t sample_select(const uint32_t (&key)[kSample / NT], int64_t n, int k, uint32_t* hist,
+DSA_DEV uint32_t sample_select(const uint32_t (&raw)[kSample / NT], int64_t n, int k, uint32_t* hist,
                                ScanLds<NT>& scan) {
   const int t = threadIdx.x;
   if (n <= kTakeAll) return 0u;
   const int ns = n > (1 << 18) ? 4096 : 2048;
   const int per = ns / NT;
+  uint32_t key[kSample / NT];
+#pragma unroll
+  for (int i = 0; i < kSample / NT; ++i) key[i] = ordered_key(__uint_as_float(raw[i]));
   // Rank m of the threshold among the samples: the samples expected above
   // the k-th score of the row (e = k ns / n) times 1.25, plus 3 standard
   // deviations of that count (sqrt e) and 8, so that a threshold above the
@@ -320,109 +330,51 @@ DSA_DEV uint32_t sample_select(const uint32_t (&key)[kSample / NT], int64_t n, i
   const double e = (double)k * ns / (double)n;
   uint32_t m = (uint32_t)(1.25 * e + 3.0 * __builtin_sqrt(e)) + 8u;
   if (m > (uint32_t)ns) m = ns;
-  // Two 11-bit radix steps on the keys: T is the lower edge of the 22-bit
-  // prefix bin that holds the m-th largest sample.
-  uint32_t prefix = 0;
-  for (int step = 0; step < 2; ++step) {
-    const int shift = step == 0 ? 21 : 10;
+  // 11-bit radix steps that start just below the prefix every sample shares
+  // (from their min and max, so that the first step spreads over its bins):
+  // T is the lower edge of the bin that holds the m-th largest sample, once
+  // the bin is at most 2^10 keys wide.
+  const int lane = t & 63, wave = t >> 6;
+  uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < kSample / NT; ++i)
+    if (i < per) {
+      lo = min(lo, key[i]);
+      hi = max(hi, key[i]);
+    }
+  lo = ~wave_max32(~lo);
+  hi = wave_max32(hi);
+  if (lane == 0) {
+    hist[wave] = lo;
+    hist[NT / 64 + wave] = hi;
+  }
+  __syncthreads();
+  lo = ~wave_max32(lane < NT / 64 ? ~hist[lane] : 0u);
+  hi = wave_max32(lane < NT / 64 ? hist[NT / 64 + lane] : 0u);
+  __syncthreads();  // the extremes are read before the histogram is cleared
+  if (lo == hi) return hi;  // every sample has the same key (uniform branch)
+  int shift = 32 - __clz((int)(lo ^ hi));  // bits below the shared prefix
+  uint32_t prefix = shift == 32 ? 0u : hi >> shift;
+  while (true) {  // uniform trip count
+    const int width = shift < 11 ? shift : 11;
+    const int lo_bit = shift - width;
     for (int i = t; i < kHistBins; i += NT) hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kSample / NT; ++i)
-      if (i < per && (step == 0 || (key[i] >> 21) == prefix))
-        atomicAdd(&hist[(key[i] >> shift) & (kHistBins - 1)], 1u);
+      if (i < per && (shift == 32 || (key[i] >> shift) == prefix))
+        atomicAdd(&hist[(key[i] >> lo_bit) & ((1u << width) - 1)], 1u);
     __syncthreads();
     uint32_t c[kHistBins / NT];
     load_bins<NT>(hist, c);
     const Thresh th = block_threshold<NT>(c, m, scan);
     m -= th.above;
-    prefix = step == 0 ? (uint32_t)th.digit : (prefix << 11) | (uint32_t)th.digit;
+    prefix = (shift == 32 ? 0u : prefix << width) | (uint32_t)th.digit;
+    shift = lo_bit;
+    if (shift <= 10) return prefix << shift;
+    // (every thread read its bins before block_threshold's first barrier, so
+    // the next clear is safe)
   }
-  return prefix << 10;
-}
-
-template <bool VEC>
-__global__ __launch_bounds__(kT) void topk_filter_kernel(const float* __restrict__ scores, int64_t ld,
-                                                        int32_t* __restrict__ row_len, const int32_t* ctx_len,
-                                                        int R, int slice, int k, TopkWs w) {
-  __shared__ FilterLds L;
-  const int t = threadIdx.x;
-  const int row = blockIdx.y;
-  const int64_t n = visible_len(row_len, ctx_len, R, row, ld);
-  if (ctx_len && blockIdx.x == 0 && t == 0) row_len[row] = (int32_t)n;  // published for the caller
-  if (n <= k) return;  // the final kernel emits every position
-  const float* s = scores + (size_t)row * ld;
-  uint32_t skey[kSample / kT];
-  sample_load<kT>(s, n, skey);
-  const uint32_t T = sample_select<kT>(skey, n, k, L.u.hist, L.scan);
-  const int64_t s0 = (int64_t)blockIdx.x * slice;
-  const int64_t s1 = s0 + slice < n ? s0 + slice : n;
-  const uint32_t sub = (uint32_t)(w.cap / gridDim.x);  // this slice's share of the row's buffer
-  uint2* gcand = w.cand + (size_t)row * w.cap + (size_t)blockIdx.x * sub;
-  if (t == 0) L.cnt = 0;
-  __syncthreads();
-
-  // Each lane classifies 16 scores per step into a bitmask; one LDS atomic
-  // per wave reserves the slots (uniform trip counts). The next step's
-  // scores are loaded before the current ones are classified.
-  const int lane = t & 63, wave = t >> 6;
-  auto load_step = [&](int64_t base, float (&v)[16]) {
-    const int64_t wbase = base + 1024 * wave + 4 * lane;  // element (q, e): wbase + 256 q + e
-    if (VEC) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t i = wbase + 256 * q;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (i < s1) x = *reinterpret_cast<const f32x4*>(s + i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t i = wbase + 256 * (j >> 2) + (j & 3);
-        v[j] = i < s1 ? s[i] : 0.f;
-      }
-    }
-  };
-  float cur[16], nxt[16];
-  if (s0 < s1) load_step(s0, cur);
-  for (int64_t base = s0; base < s1; base += 16 * kT) {
-    const bool more = base + 16 * kT < s1;
-    if (more) load_step(base + 16 * kT, nxt);
-    const int64_t wbase = base + 1024 * wave + 4 * lane;
-    uint32_t cmask = 0;
-    uint32_t keys[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int64_t i = wbase + 256 * (j >> 2) + (j & 3);
-      keys[j] = ordered_key(cur[j]);
-      cmask |= (uint32_t)(i < s1 && keys[j] >= T) << j;
-    }
-    uint32_t tc;
-    const uint32_t pc = wave_prefix_small((uint32_t)__popc(cmask), tc);
-    const uint32_t bc = wave_reserve(&L.cnt, tc);
-    uint32_t slot = bc + pc;
-    while (cmask) {
-      const int j = __builtin_ctz(cmask);
-      cmask &= cmask - 1;
-      const uint2 e = make_uint2(keys[j], (uint32_t)(wbase + 256 * (j >> 2) + (j & 3)));
-      if (slot < (uint32_t)kListLds) L.u.list[slot] = e;  // the rest of the region takes the overflow
-      else if (slot < sub) gcand[slot] = e;
-      ++slot;
-    }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
-    }
-  }
-  __syncthreads();
-  // The true count is published even when it overflowed the slice's region:
-  // the final kernel then falls back to the whole row.
-  const uint32_t nc = L.cnt;
-  const uint32_t keep = nc <= sub ? (nc < (uint32_t)kListLds ? nc : (uint32_t)kListLds) : 0u;
-  for (uint32_t i = t; i < keep; i += kT) gcand[i] = L.u.list[i];
-  if (t == 0) w.cnt[(size_t)row * kMaxSlices + blockIdx.x] = nc;
 }
 
 // ------------------------------------------------------------------ final
@@ -577,17 +529,253 @@ DSA_DEV void select_top(SelectLds& L, int64_t count, int k, int32_t* __restrict_
   }
 }
 
-// One workgroup per row (a kernel boundary orders the filter's writes before
-// these reads; a device-scope fence per workgroup would write back each
-// XCD's L2).
+// ------------------------------------------------------------------ short rows
+
+// Rows of at most kShortMax scores: one workgroup of kTF threads per row
+// holds the whole row in registers (score 4096 q + 4 t + e is x[4 q + e] of
+// thread t), keeps every score >= T in LDS and selects the k largest there:
+// one kernel, no global round trip. The samples and the row are loaded
+// together, so the threshold is found while the row is in flight.
+static constexpr int kShortPer = 40;                // scores per thread
+static constexpr int kShortMax = kTF * kShortPer;   // 40,960
+
+struct ShortLds {
+  SelectLds f;
+  uint32_t cnt;
+  uint32_t wmax[kTF / 64];
+  uint2 elems[kFinalLds + 1];  // survivors, plus one spare entry taking overflow writes
+};
+
+// key >= T as a float comparison (scores are not NaN): T is the lower edge of
+// a bin holding a sampled score, so its float is a number unless T lies below
+// every number's key, where every score passes.
+DSA_DEV float key_threshold_float(uint32_t T) {
+  return T <= ordered_key(-INFINITY) ? -INFINITY : __uint_as_float((T & 0x80000000u) ? (T & 0x7fffffffu) : ~T);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kTF) void topk_short_kernel(const float* __restrict__ scores, int64_t ld,
+                                                       int32_t* __restrict__ row_len, const int32_t* ctx_len, int R,
+                                                       int k, int32_t* __restrict__ idx) {
+  constexpr int G = kShortPer / 4;  // 16-byte groups per thread
+  __shared__ ShortLds L;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int row = blockIdx.x;
+  const int n = (int)visible_len(row_len, ctx_len, R, row, ld);  // <= ld <= kShortMax
+  if (ctx_len && t == 0) row_len[row] = n;  // published for the caller
+  int32_t* out = idx + (size_t)row * k;
+  if (n <= k) {  // every visible position is selected; the rest is padding
+    for (int i = t; i < k; i += kTF) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* s = scores + (size_t)row * ld;
+  uint32_t skey[kSample / kTF];
+  sample_load<kTF>(s, n, skey);
+  // The row through a buffer descriptor of n scores (one VGPR offset per
+  // lane); groups that start past n are not loaded.
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s), (short)0, 4 * n, 0x00020000);
+  float x[kShortPer];
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    if (4096 * q < n) {  // uniform
+      if (VEC) {
+        const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * t, 16384 * q, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[4 * q + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, 16 * t + 4 * e, 16384 * q, 0));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * q + e] = __builtin_nanf("");
+    }
+  }
+  if (t == 0) L.cnt = 0;
+  lds_barrier();  // the counter is cleared before any wave reserves (the row loads stay in flight)
+  const uint32_t T = sample_select<kTF>(skey, n, k, L.f.hist, L.f.scan);
+  const float Tf = key_threshold_float(T);
+  // The group holding position n - 1 (index qb): NaN past n, and with
+  // 16-byte loads the scores of a partial vector read again one by one (the
+  // buffer load of a vector that crosses the end may return zeros). NaN is
+  // never kept.
+  {
+    const int qb = (n - 1) / 4096;  // uniform
+    float y[4];
+    bool past[4], reread[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4096 * qb + 4 * t + e;
+      past[e] = i >= n;
+      reread[e] = VEC && !past[e] && i >= (n & ~3);
+      y[e] = reread[e] ? s[i] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      if (q == qb) {  // uniform
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * q + e] = past[e] ? __builtin_nanf("") : (reread[e] ? y[e] : x[4 * q + e]);
+      }
+    }
+  }
+  // survivors -> LDS as (score bits, position), in batches of 8 scores: one
+  // reservation per wave and batch; slots past the buffer all land on its
+  // spare last entry. The row maximum bounds the survivors from above.
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j) mx = fmaxf(mx, x[j]);  // NaN operands are ignored
+  uint32_t pbase = (uint32_t)(4 * t);
+  asm volatile("" : "+v"(pbase));  // keeps the compiler from precomputing every position
+#pragma unroll
+  for (int b = 0; b < kShortPer; b += 8) {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = b; j < b + 8; ++j) mine += (uint32_t)(x[j] >= Tf);
+    uint32_t total;
+    const uint32_t pre = wave_prefix_small<4>(mine, total);
+    uint32_t slot = wave_reserve(&L.cnt, total) + pre;
+#pragma unroll
+    for (int j = b; j < b + 8; ++j) {
+      const bool kp = x[j] >= Tf;
+      if (kp)
+        L.elems[slot < (uint32_t)kFinalLds ? slot : (uint32_t)kFinalLds] =
+            make_uint2(__float_as_uint(x[j]), pbase + (uint32_t)(4096 * (j >> 2) + (j & 3)));
+      slot += kp;
+    }
+  }
+  const uint32_t wm = wave_max32(ordered_key(mx));
+  if (lane == 0) L.wmax[wave] = wm;
+  __syncthreads();
+  const uint32_t count = L.cnt;
+  const uint32_t kmax = wave_max32(lane < kTF / 64 ? L.wmax[lane] : 0u);
+  if (count >= (uint32_t)k && count <= (uint32_t)kFinalLds)
+    select_top(
+        L.f, count, k, out,
+        [&](int64_t i) { return composite(ordered_key(__uint_as_float(L.elems[i].x)), L.elems[i].y); }, true,
+        (uint64_t)T << 32, ((uint64_t)kmax << 32) | 0xffffffffull);
+  else  // the sample missed: select over the whole row
+    select_top(L.f, n, k, out, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
+}
+
+// ------------------------------------------------------------------ long rows
+
+// Grid (slices, rows), kT threads: workgroup x streams its slice of the row
+// (16 scores per lane and step, the next step in flight) and writes every
+// score >= T, as (ordered key, position), to its own region of the row's
+// candidate buffer; then its true count, its largest key and (slice 0) T go
+// to slots of its own: no global atomics, nothing to clear first. The first
+// two steps are issued once the samples have arrived, so the threshold is
+// found while they are in flight.
+static constexpr int kT = 256;
+
+struct SliceLds {
+  ScanLds<kT> scan;
+  uint32_t hist[kHistBins];
+  uint32_t cnt;
+  uint32_t wmax[kT / 64];
+};
+
+template <bool VEC>
+__global__ __launch_bounds__(kT) void topk_slice_kernel(const float* __restrict__ scores, int64_t ld,
+                                                       int32_t* __restrict__ row_len, const int32_t* ctx_len, int R,
+                                                       int slice, int k, TopkWs w) {
+  __shared__ SliceLds L;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int row = blockIdx.y;
+  const int64_t n = visible_len(row_len, ctx_len, R, row, ld);
+  if (ctx_len && blockIdx.x == 0 && t == 0) row_len[row] = (int32_t)n;  // published for the caller
+  if (n <= k) return;  // the final kernel emits every position
+  const float* s = scores + (size_t)row * ld;
+  const int64_t s0 = (int64_t)blockIdx.x * slice;
+  const int64_t s1 = s0 + slice < n ? s0 + slice : n;
+  const uint32_t sub = (uint32_t)(w.cap / gridDim.x);  // this slice's share of the row's buffer
+  uint2* gcand = w.cand + (size_t)row * w.cap + (size_t)blockIdx.x * sub;
+
+  // Step of 4096 scores at base: lane element (q, e) is position
+  // base + 1024 wave + 4 lane + 256 q + e, read through a buffer descriptor
+  // of the slice (past its end the loads return 0 and no branch is needed,
+  // so the compiler keeps several steps' loads in flight).
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s + s0), (short)0,
+                                                      (int)(4 * (s1 > s0 ? s1 - s0 : 0)), 0x00020000);
+  auto load_step = [&](int64_t base, float (&v)[16]) {
+    const int off = (int)(4 * (base - s0)) + 16 * (256 * wave + lane);
+    if (VEC) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 1024 * q, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, off + 4 * (j & 3), 1024 * (j >> 2), 0));
+    }
+  };
+  // The samples travel alone (the slice loads of every workgroup would delay
+  // them); the first two steps of the slice are in flight while the
+  // threshold is computed.
+  uint32_t skey[kSample / kT];
+  sample_load<kT>(s, n, skey);
+  wait_vmcnt<0>();
+  float cur[16], nxt[16];
+  if (s0 < s1) load_step(s0, cur);
+  if (s0 + 4096 < s1) load_step(s0 + 4096, nxt);
+  if (t == 0) L.cnt = 0;
+  lds_barrier();  // the counter is cleared before any wave reserves (the loads stay in flight)
+  const uint32_t T = sample_select<kT>(skey, n, k, L.hist, L.scan);
+  const float Tf = key_threshold_float(T);
+
+  float mx = -INFINITY;
+  for (int64_t base = s0; base < s1; base += 4096) {
+    const bool whole = base + 4096 <= s1;  // uniform: no position test needed
+    const int64_t wbase = base + 1024 * wave + 4 * lane;
+    uint32_t cmask = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool in = whole || wbase + 256 * (j >> 2) + (j & 3) < s1;
+      cmask |= (uint32_t)(in && cur[j] >= Tf) << j;
+      if (in) mx = fmaxf(mx, cur[j]);
+    }
+    uint32_t tc;
+    const uint32_t pc = wave_prefix_small<5>((uint32_t)__popc(cmask), tc);
+    uint32_t slot = wave_reserve(&L.cnt, tc) + pc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (cmask & (1u << j)) {
+        if (slot < sub) gcand[slot] = make_uint2(ordered_key(cur[j]), (uint32_t)(wbase + 256 * (j >> 2) + (j & 3)));
+        ++slot;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
+    if (base + 8192 < s1) load_step(base + 8192, nxt);
+  }
+  const uint32_t wm = wave_max32(ordered_key(mx));
+  if (lane == 0) L.wmax[wave] = wm;
+  __syncthreads();
+  if (t == 0) {
+    // the true count, also when it overflowed the region: the final kernel
+    // then selects over the whole row
+    w.cnt[(size_t)row * kMaxSlices + blockIdx.x] = L.cnt;
+    w.tmax[(size_t)row * kMaxSlices + blockIdx.x] = max(max(L.wmax[0], L.wmax[1]), max(L.wmax[2], L.wmax[3]));
+    if (blockIdx.x == 0) w.thr[row] = T;
+  }
+}
+
+// One workgroup per row gathers the slices' survivors (a kernel boundary
+// orders the slice workgroups' writes before these reads; a device-scope fence
+// per workgroup would write back each XCD's L2). Every survivor lies in
+// [T << 32, (largest key << 32) | ~0], which saves select_top a pass.
 __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict__ scores, int64_t ld,
-                                                       const int32_t* __restrict__ row_len, const int32_t* ctx_len,
-                                                       int R, int slices, int k, int32_t* __restrict__ idx,
-                                                       TopkWs w) {
+                                                       const int32_t* __restrict__ row_len, int slices, int k,
+                                                       int32_t* __restrict__ idx, TopkWs w) {
   __shared__ FinalLds L;
+  __shared__ uint32_t kmax_s;
   const int t = threadIdx.x;
   const int row = blockIdx.x;
-  const int64_t n = visible_len(row_len, ctx_len, R, row, ld);
+  const int64_t n = visible_len(row_len, nullptr, 1, row, ld);  // published by the slice pass
   int32_t* out = idx + (size_t)row * k;
   if (n <= k) {  // every visible position is selected; the rest is padding
     for (int64_t i = t; i < k; i += kTF) out[i] = i < n ? (int32_t)i : -1;
@@ -597,12 +785,18 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
   const uint32_t sub = (uint32_t)(w.cap / slices);
   if (t < 64) {
     const uint32_t c = t < slices ? w.cnt[(size_t)row * kMaxSlices + t] : 0u;
+    const uint32_t km = t < slices ? w.tmax[(size_t)row * kMaxSlices + t] : 0u;
     const uint64_t bad = __ballot(c > sub);
     const uint32_t incl = wave_incl_sum(c);
+    const uint32_t kmax = wave_max32(km);
     L.off[t] = incl - c;
     if (t == 63) L.total = incl;
-    if (t == 0) L.bad = bad != 0;
+    if (t == 0) {
+      L.bad = bad != 0;
+      kmax_s = kmax;
+    }
   }
+  const uint32_t T = w.thr[row];
   __syncthreads();
   const uint32_t count = L.total;
   if (!L.bad && count >= (uint32_t)k && count <= (uint32_t)kFinalLds) {
@@ -630,125 +824,13 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
       }
     }
     __syncthreads();
-    select_top(L.s, count, k, out, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); });
+    select_top(
+        L.s, count, k, out, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); }, true,
+        (uint64_t)T << 32, ((uint64_t)kmax_s << 32) | 0xffffffffull);
   } else {  // the sample missed: select over the whole row
     const float* s = scores + (size_t)row * ld;
     select_top(L.s, n, k, out, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
   }
-}
-
-// ------------------------------------------------------------------ short rows
-
-// Rows of at most kShortMax scores: one workgroup per row holds the whole row
-// in registers (element 4096 q + 4 t + e of the row is key[4 q + e] of thread
-// t), so threshold, filter and selection run in one kernel with no global
-// round trip. Same sample, threshold and exactness argument as above; the
-// survivors go to LDS and select_top picks the k largest.
-static constexpr int kShortPer = 40;                // scores per thread
-static constexpr int kShortMax = kShortPer * kTF;   // 40,960
-
-struct ShortLds {
-  SelectLds f;
-  uint32_t cnt;
-  uint32_t wmax[kTF / 64];
-  uint2 elems[kFinalLds + 1];  // survivors, plus one spare entry taking overflow writes
-};
-
-template <bool VEC>
-__global__ __launch_bounds__(kTF) void topk_short_kernel(const float* __restrict__ scores, int64_t ld,
-                                                       int32_t* __restrict__ row_len, const int32_t* ctx_len, int R,
-                                                       int k, int32_t* __restrict__ idx) {
-  __shared__ ShortLds L;
-  const int t = threadIdx.x;
-  const int row = blockIdx.x;
-  const int n = (int)visible_len(row_len, ctx_len, R, row, ld);  // <= ld <= kShortMax
-  if (ctx_len && t == 0) row_len[row] = n;  // published for the caller
-  int32_t* out = idx + (size_t)row * k;
-  if (n <= k) {
-    for (int i = t; i < k; i += kTF) out[i] = i < n ? i : -1;
-    return;
-  }
-  const float* s = scores + (size_t)row * ld;
-  uint32_t skey[kSample / kTF];
-  sample_load<kTF>(s, n, skey);
-  // The row through a buffer descriptor of n scores (one VGPR offset per
-  // lane); groups of 4 (one load) that start past n are not loaded. Scores
-  // at positions >= n become NaN, which no comparison keeps.
-  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s), (short)0, 4 * n, 0x00020000);
-  float x[kShortPer];
-#pragma unroll
-  for (int q = 0; q < kShortPer / 4; ++q) {
-    if (4096 * q < n) {  // uniform
-      if (VEC) {
-        const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * t, 16384 * q, 0));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          x[4 * q + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, 16 * t + 4 * e, 16384 * q, 0));
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * q + e] = __builtin_nanf("");
-    }
-  }
-  if (t == 0) L.cnt = 0;
-  lds_barrier();  // the counter is cleared before any wave reserves (the row loads stay in flight)
-  const uint32_t T = sample_select<kTF>(skey, n, k, L.f.hist, L.f.scan);
-  // The group holding position n: NaN past n, and with 16-byte loads the
-  // scores of a partial vector read again one by one (the buffer load of a
-  // vector that crosses the end may return zeros).
-#pragma unroll
-  for (int q = 0; q < kShortPer / 4; ++q) {
-    if (4096 * q < n && n < 4096 * q + 4096) {  // uniform
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4096 * q + 4 * t + e;
-        if (i >= n) x[4 * q + e] = __builtin_nanf("");
-        else if (VEC && i >= (n & ~3)) x[4 * q + e] = s[i];
-      }
-    }
-  }
-  // key >= T as a float comparison (scores are not NaN): T is the lower edge
-  // of a bin holding a sampled score, so its float is a number unless T lies
-  // below every number's key, where every score passes.
-  const float Tf = T <= ordered_key(-INFINITY) ? -INFINITY
-                                                : __uint_as_float((T & 0x80000000u) ? (T & 0x7fffffffu) : ~T);
-
-  // survivors -> LDS as (score bits, position): one reservation per wave;
-  // slots past the buffer all land on its spare last entry. The row maximum
-  // bounds the survivors from above for the selection.
-  uint32_t mine = 0;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < kShortPer; ++j) {
-    mine += (uint32_t)(x[j] >= Tf);
-    mx = fmaxf(mx, x[j]);  // NaN operands are ignored
-  }
-  const int lane = t & 63, wave = t >> 6;
-  const uint32_t wmax = wave_max32(ordered_key(mx));
-  if (lane == 0) L.wmax[wave] = wmax;
-  uint32_t total;
-  const uint32_t pre = wave_prefix_small<6>(mine, total);
-  uint32_t slot = wave_reserve(&L.cnt, total) + pre;
-#pragma unroll
-  for (int j = 0; j < kShortPer; ++j) {
-    const bool kp = x[j] >= Tf;
-    if (kp) L.elems[slot < (uint32_t)kFinalLds ? slot : (uint32_t)kFinalLds] =
-        make_uint2(__float_as_uint(x[j]), (uint32_t)(4096 * (j >> 2) + 4 * t + (j & 3)));
-    slot += kp;
-  }
-  __syncthreads();
-  const uint32_t count = L.cnt;
-  const uint32_t kmax = wave_max32(lane < kTF / 64 ? L.wmax[lane] : 0u);
-  if (count >= (uint32_t)k && count <= (uint32_t)kFinalLds)
-    select_top(
-        L.f, count, k, out,
-        [&](int64_t i) { return composite(ordered_key(__uint_as_float(L.elems[i].x)), L.elems[i].y); }, true,
-        (uint64_t)T << 32, ((uint64_t)kmax << 32) | 0xffffffffull);
-  else  // the sample missed: select over the whole row
-    select_top(L.f, n, k, out, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
 }
 
 // ------------------------------------------------------------------ launcher
@@ -759,8 +841,9 @@ static bool vec_ok(const float* scores, int64_t ld) {
 
 hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int rows, int64_t max_len, int k,
                        int32_t* idx, const TopkWs& w, hipStream_t st, const int32_t* ctx_len, int R) {
+  const bool vec = vec_ok(scores, ld);
   if (max_len <= kShortMax) {
-    if (vec_ok(scores, ld))
+    if (vec)
       hipLaunchKernelGGL(topk_short_kernel<true>, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, ctx_len, R, k,
                          idx);
     else
@@ -768,7 +851,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int ro
                          idx);
     return hipGetLastError();
   }
-  // Filter: enough workgroups to cover the GPU twice, at least 4096 scores
+  // Slices: enough workgroups to cover the GPU twice, at least 4096 scores
   // and at most kMaxSlices workgroups per row.
   int64_t want = (512 + rows - 1) / rows;
   const int64_t max_slices = (max_len + 4095) / 4096;
@@ -778,16 +861,15 @@ hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int ro
   int64_t slice = (max_len + want - 1) / want;
   slice = (slice + 4095) / 4096 * 4096;
   const int ns = (int)((max_len + slice - 1) / slice);
-  if (vec_ok(scores, ld))
-    hipLaunchKernelGGL(topk_filter_kernel<true>, dim3(ns, rows), dim3(kT), 0, st, scores, ld, row_len, ctx_len, R,
+  if (vec)
+    hipLaunchKernelGGL(topk_slice_kernel<true>, dim3(ns, rows), dim3(kT), 0, st, scores, ld, row_len, ctx_len, R,
                        (int)slice, k, w);
   else
-    hipLaunchKernelGGL(topk_filter_kernel<false>, dim3(ns, rows), dim3(kT), 0, st, scores, ld, row_len, ctx_len,
-                       R, (int)slice, k, w);
+    hipLaunchKernelGGL(topk_slice_kernel<false>, dim3(ns, rows), dim3(kT), 0, st, scores, ld, row_len, ctx_len, R,
+                       (int)slice, k, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_final_kernel, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, ctx_len, R, ns, k, idx,
-                     w);
+  hipLaunchKernelGGL(topk_final_kernel, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, ns, k, idx, w);
   return hipGetLastError();
 }
 
