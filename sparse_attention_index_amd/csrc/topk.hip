@@ -452,20 +452,29 @@ DSA_DEV void select_top(SelectLds& L, int64_t count, int k, int32_t* __restrict_
   const uint64_t b = (shift == 64 ? 0 : prefix << width) | (uint64_t)th.digit;  // top (64 - b_shift) bits
   const int b_shift = lo_bit;
   const bool gather = th.at <= (uint32_t)kBinLds;
-  // emit everything above b; gather b
-  for (int64_t base = 0; base < count; base += kTF) {
-    const int64_t i = base + t;
-    uint64_t c = 0;
-    bool above = false, at = false;
-    if (i < count) {
-      c = comp_at(i);
-      above = (c >> b_shift) > b;
-      at = gather && (c >> b_shift) == b;
+  // emit everything above b; gather b. Each thread counts its elements of
+  // both kinds first, so that a wave reserves its slots with one atomic per
+  // kind instead of one per pass over 1024 elements.
+  {
+    uint32_t na = 0, nb = 0;
+    for (int64_t i = t; i < count; i += kTF) {
+      const uint64_t c = comp_at(i);
+      na += (uint32_t)((c >> b_shift) > b);
+      nb += (uint32_t)(gather && (c >> b_shift) == b);
     }
-    const uint32_t slot = wave_append(&L.emitted, above);
-    if (above && slot < (uint32_t)k) out[slot] = (int32_t)~(uint32_t)c;
-    const uint32_t bslot = wave_append(&L.nbin, at);
-    if (at && bslot < (uint32_t)kBinLds) L.bin[bslot] = c;
+    const uint32_t ia = wave_incl_sum(na), ib = wave_incl_sum(nb);
+    uint32_t sa = wave_reserve(&L.emitted, __builtin_amdgcn_readlane(ia, 63)) + ia - na;
+    uint32_t sb = wave_reserve(&L.nbin, __builtin_amdgcn_readlane(ib, 63)) + ib - nb;
+    for (int64_t i = t; i < count; i += kTF) {
+      const uint64_t c = comp_at(i);
+      if ((c >> b_shift) > b) {
+        if (sa < (uint32_t)k) out[sa] = (int32_t)~(uint32_t)c;
+        ++sa;
+      } else if (gather && (c >> b_shift) == b) {
+        if (sb < (uint32_t)kBinLds) L.bin[sb] = c;
+        ++sb;
+      }
+    }
   }
   __syncthreads();
   need -= th.above;
