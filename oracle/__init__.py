@@ -20,7 +20,9 @@ this package; the product path never does.
 Parity status of each function (see the pins in tests/test_oracle_pins.py):
 e4m3_table, gather_tokens, index_scores, topk_positions, attend, dsa_rows and
 dsa_bytes are pinned against closed forms, library routines or the pages'
-printed numbers.
+printed numbers; key_write's layer_norm, e4m3_encode, quantize_rows and
+write_slots against torch's layer_norm and float8 cast, closed forms and the
+workloads' own quantiser.
 """
 
 from .fp8 import e4m3_table, e4m3_decode  # noqa: F401
@@ -35,3 +37,11 @@ from .dsa import (  # noqa: F401
     topk_positions,
 )
 from .traffic import dsa_bytes, dense_mla_bytes, counted_bytes  # noqa: F401
+from .key_write import (  # noqa: F401
+    e4m3_encode,
+    index_key_write,
+    layer_norm,
+    quantize_rows,
+    scatter_rows,
+    write_slots,
+)
