@@ -7,7 +7,7 @@
  * Write the new token's FP8 index key, Score every cached key with the
  * indexer's 32 heads, Select the 2,048 highest-scoring positions per query
  * row, and Attend with MLA over only those latent rows. This library covers
- * Score, Select and Attend.
+ * all four.
  *
  * Conventions shared by every entry point
  *  - Pointers are device pointers unless a comment says "host". `stream` is a
@@ -97,6 +97,28 @@ typedef struct {
   int32_t max_blocks;
   int32_t max_ctx;
 } dsa_batch;
+
+/*
+ * Write: the new tokens' index keys into the cache ("TokenSpeed Kimi K3.1",
+ * section "Integrating sparse attention with the K3 stack", step 1: the new
+ * token's index key is normalised, quantised to FP8 with a single scale and
+ * written into the cache; LayerNorm is the only key normalisation the loader
+ * accepts). For row = b * rows_per_request + r, at position
+ * p = ctx_len[b] - rows_per_request + r:
+ *   y = LayerNorm(k[row]) over its 128 dims (biased variance, eps added to
+ *       the variance) * ln_weight + ln_bias, computed in fp32;
+ *   scale = max |y| / 448 (1 for an all-zero row);
+ *   key_fp8[slot][0..127] = E4M3(y / scale) (round to nearest even),
+ *   key_scale[slot] = scale, with slot = block_table[b][p / 64] * 64 + p % 64.
+ *   k          bf16 [rows][128] (4-byte aligned)
+ *   ln_weight, ln_bias  fp32 [128] (8-byte aligned)
+ *   key_fp8    [num_blocks][64][128] E4M3, written; key_scale [num_blocks][64]
+ * A row whose position is negative or whose page id lies outside
+ * [0, num_blocks) is skipped (nothing is written for it). Only the new rows'
+ * slots are written. eps must be positive and finite.
+ */
+int32_t dsa_index_key_write(const dsa_batch* batch, const void* k, const float* ln_weight, const float* ln_bias,
+                            float eps, uint8_t* key_fp8, float* key_scale, int32_t num_blocks, void* stream);
 
 /*
  * Score: the lightning indexer. For every row and every token s the row sees,

@@ -145,6 +145,27 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def dsa_index_key_write(batch: Batch, k, ln_weight, ln_bias, key_fp8, key_scale, eps: float = 1e-6, stream=None):
+    """Write the batch's new rows' index keys into the cache planes: LayerNorm
+    of k (bf16 [rows, 128]) with ln_weight / ln_bias (fp32 [128]), E4M3
+    quantisation with one absmax scale per row, paged by the batch's tables.
+    key_fp8 (uint8 [nb, 64, 128]) and key_scale (fp32 [nb, 64]) are written in place."""
+    rows = batch.rows
+    _need(k, "k", _BF16, rows * 128)
+    _need(ln_weight, "ln_weight", _F32, 128)
+    _need(ln_bias, "ln_bias", _F32, 128)
+    _need(key_fp8, "key_fp8", _CODES)
+    if key_fp8.dim() != 3 or tuple(key_fp8.shape[1:]) != (64, 128):
+        raise ValueError("key_fp8 must be [num_blocks, 64, 128]")
+    nb = int(key_fp8.shape[0])
+    _need(key_scale, "key_scale", _F32, nb * 64)
+    st = load().dsa_index_key_write(
+        ctypes.byref(batch.c), _ptr(k), _ptr(ln_weight), _ptr(ln_bias), float(eps), _ptr(key_fp8), _ptr(key_scale),
+        nb, _stream(stream),
+    )
+    _check(st, "dsa_index_key_write")
+
+
 def dsa_index_score(batch: Batch, cache: Cache, q, w, scores, q_scale=None, stream=None):
     """scores[row, s] for every visible token s (fp32 [rows, ld])."""
     q_dtype = DSA_Q_FP8 if q_scale is not None else DSA_Q_BF16

@@ -21,6 +21,7 @@ DSA_WS_MLA_PREFILL = 3
 DSA_WS_DECODE = 4
 
 EXPORTS = (
+    "dsa_index_key_write",
     "dsa_index_score",
     "dsa_topk",
     "dsa_sparse_mla_decode",
@@ -77,6 +78,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     BP = ctypes.POINTER(DsaBatchC)
     CP = ctypes.POINTER(DsaCacheC)
     sig = {
+        "dsa_index_key_write": (I32, [BP, P, P, P, F, P, P, I32, P]),
         "dsa_index_score": (I32, [BP, CP, P, I32, P, P, P, I64, P]),
         "dsa_topk": (I32, [P, I64, P, I32, I32, P, P, SZ, P]),
         "dsa_sparse_mla_decode": (I32, [BP, CP, P, I32, P, I32, F, P, P, P, SZ, P]),

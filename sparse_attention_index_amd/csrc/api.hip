@@ -1,5 +1,6 @@
 // C ABI of libdsa: host-side argument checks, workspace carving and launch
 // sequencing. Declarations and semantics are in include/dsa.h.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -159,6 +160,33 @@ int32_t dsa_index_score(const dsa_batch* batch, const dsa_cache* cache, const vo
                     "index score");
 }
 
+int32_t dsa_index_key_write(const dsa_batch* batch, const void* k, const float* ln_weight, const float* ln_bias,
+                            float eps, uint8_t* key_fp8, float* key_scale, int32_t num_blocks, void* stream) {
+  g_err[0] = 0;
+  int32_t r = check_batch(batch);
+  if (r) return r;
+  if (!k || !ln_weight || !ln_bias || !key_fp8 || !key_scale)
+    return fail(DSA_ERR_INVALID_ARG, "k, ln_weight, ln_bias, key_fp8 or key_scale is null");
+  if (num_blocks < 1) return fail(DSA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (!(eps > 0.f) || !(eps < INFINITY)) return fail(DSA_ERR_INVALID_ARG, "eps must be positive and finite");
+  if (!aligned(k, 4) || !aligned(ln_weight, 8) || !aligned(ln_bias, 8) || !aligned(key_fp8, 2))
+    return fail(DSA_ERR_INVALID_ARG, "k, ln_weight, ln_bias or key_fp8 is misaligned");
+  KeyWriteArgs a;
+  a.k = static_cast<const uint16_t*>(k);
+  a.ln_weight = ln_weight;
+  a.ln_bias = ln_bias;
+  a.eps = eps;
+  a.ctx_len = batch->ctx_len;
+  a.block_table = batch->block_table;
+  a.max_blocks = batch->max_blocks;
+  a.R = batch->rows_per_request;
+  a.rows = batch->num_requests * batch->rows_per_request;
+  a.key_fp8 = key_fp8;
+  a.key_scale = key_scale;
+  a.num_blocks = num_blocks;
+  return hip_status(launch_index_key_write(a, static_cast<hipStream_t>(stream)), "index key write");
+}
+
 int32_t dsa_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows, int32_t k, int32_t* idx,
                  void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
@@ -271,6 +299,6 @@ const char* dsa_status_string(int32_t status) {
 
 const char* dsa_last_error(void) { return g_err; }
 
-int32_t dsa_version(void) { return 100; }
+int32_t dsa_version(void) { return 200; }
 
 }  // extern "C"

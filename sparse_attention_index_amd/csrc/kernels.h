@@ -61,4 +61,21 @@ size_t mla_ws_bytes(int rows, int k, bool split);
 // merges the partial results by log-sum-exp; false gives each row one workgroup.
 hipError_t launch_sparse_mla(const MlaArgs& a, int rows, bool split, void* ws, hipStream_t st);
 
+struct KeyWriteArgs {
+  const uint16_t* k;         // bf16 [rows][128] new index keys
+  const float* ln_weight;    // fp32 [128]
+  const float* ln_bias;      // fp32 [128]
+  float eps;
+  const int32_t* ctx_len;    // [B]
+  const int32_t* block_table;  // [B][max_blocks]
+  int32_t max_blocks;
+  int32_t R;                 // rows per request
+  int32_t rows;              // B * R
+  uint8_t* key_fp8;          // [num_blocks][64][128]
+  float* key_scale;          // [num_blocks][64]
+  int32_t num_blocks;
+};
+// LayerNorm + E4M3 absmax quantisation + paged write of each new row's key.
+hipError_t launch_index_key_write(const KeyWriteArgs& a, hipStream_t st);
+
 }  // namespace dsa

@@ -98,6 +98,14 @@ def test_argument_errors_are_reported_before_any_launch(lib):
             _lib.DSA_ERR_INVALID_ARG
         assert fn(ctypes.byref(b), ctypes.byref(c), P + 2, 16, P, 64, 0.1, P, None, P, 1 << 30, None) == \
             _lib.DSA_ERR_INVALID_ARG
+    # index-key write
+    kw = lib.dsa_index_key_write
+    assert kw(None, P, P, P, 1e-6, P, P, 1, None) == _lib.DSA_ERR_INVALID_ARG
+    assert kw(ctypes.byref(b), None, P, P, 1e-6, P, P, 1, None) == _lib.DSA_ERR_INVALID_ARG
+    assert kw(ctypes.byref(b), P, P, P, 0.0, P, P, 1, None) == _lib.DSA_ERR_INVALID_ARG
+    assert kw(ctypes.byref(b), P, P, P, float("nan"), P, P, 1, None) == _lib.DSA_ERR_INVALID_ARG
+    assert kw(ctypes.byref(b), P, P, P, 1e-6, P, P, 0, None) == _lib.DSA_ERR_INVALID_ARG
+    assert kw(ctypes.byref(b), P + 2, P, P, 1e-6, P, P, 1, None) == _lib.DSA_ERR_INVALID_ARG
     # fused decode
     assert lib.dsa_decode(ctypes.byref(b), ctypes.byref(c), P, P, P, 16, 2048, 0.1, P, None, None, P, 16, None) == \
         _lib.DSA_ERR_WORKSPACE
