@@ -375,6 +375,99 @@ def run_prefill(args, torch, dsa, traffic, cfg):
     }
 
 
+KEY_WRITE = {
+    # name: (requests, new rows per request, context of each request)
+    "index_key_write_4096": (1, 4096, 135168),   # the prefill chunk's new keys
+    "index_key_write_16x4": (16, 4, 32768),      # one decode step's new keys
+}
+KEY_WRITE_ROW_BYTES = 256 + 128 + 4 + 4  # bf16 key in, E4M3 codes + scale out, page id
+
+
+def run_key_write(args, torch, dsa):
+    """The index-key write step alone: LayerNorm + E4M3 absmax quantisation +
+    paged write of every new row's key (device-resident inputs)."""
+    B, R, L = KEY_WRITE[args.workload]
+    nb = B * ((L + 63) // 64)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20260100)
+    ctx = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    table = torch.randperm(nb, generator=g, device="cuda").to(torch.int32).reshape(B, -1)
+    batch = dsa.Batch(R, ctx, table, L)
+    nsets = 4
+    ks = [torch.randn((B * R, 128), generator=g, device="cuda").to(torch.bfloat16) for _ in range(nsets)]
+    w = (1.0 + 0.1 * torch.randn(128, generator=g, device="cuda")).float()
+    b = (0.1 * torch.randn(128, generator=g, device="cuda")).float()
+    key_fp8 = torch.zeros((nb, 64, 128), dtype=torch.uint8, device="cuda")
+    key_scale = torch.ones((nb, 64), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        dsa.dsa_index_key_write(batch, ks[i % nsets], w, b, key_fp8, key_scale)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(1e8))  # the host queues every launch before the GPU reaches them
+    ev0.record()
+    for i in range(n):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * ev0.elapsed_time(ev1) / n
+    rows = B * R
+    achieved = rows * KEY_WRITE_ROW_BYTES / (us * 1e-6) / 1e9
+    return {
+        "metric": "DSA index-key write: new rows/s; % of HBM roofline",
+        "value": rows / (us * 1e-6),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": args.warmup,
+        "ms_per_step": us * 1e-3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "requests": B, "rows_per_request": R, "context": L,
+                   "launch": "eager, back to back"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "index_key_write_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes": rows * KEY_WRITE_ROW_BYTES,
+            "avg_launch_us": us,
+        },
+    }
+
+
+def key_write_cpu_baseline(workload_name, budget_s):
+    """The oracle's key write on the same number of rows (host numpy)."""
+    import numpy as np
+
+    import oracle
+
+    B, R, L = KEY_WRITE[workload_name]
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((B * R, 128)).astype(np.float32)
+    w, b = np.ones(128), np.zeros(128)
+    reps, spent = 0, 0.0
+    while spent < budget_s or reps == 0:
+        t0 = time.perf_counter()
+        oracle.index_key_write(k, w, b, 1e-6)
+        spent += time.perf_counter() - t0
+        reps += 1
+        if reps >= 50:
+            break
+    return {"value": reps * B * R / spent, "unit": "rows/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"{reps} x {B * R} rows, LayerNorm + quantisation, numpy on the host, {spent:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -390,6 +483,12 @@ def main():
 
     dsa.load()
     torch.cuda.set_device(0)
+    if args.workload in KEY_WRITE:
+        result = run_key_write(args, torch, dsa)
+        if args.cpu_seconds > 0:
+            result["cpu_baseline"] = key_write_cpu_baseline(args.workload, min(args.cpu_seconds, 5.0))
+        print(json.dumps(result), flush=True)
+        return
     cfg = case_config(args.workload)
     if cfg["R"] > 64:
         result = run_prefill(args, torch, dsa, traffic, cfg)
