@@ -70,6 +70,7 @@ struct DecodeWs {
   float* scores;
   int32_t* row_len;
   int32_t* idx;
+  int32_t* slots;  // physical cache rows of the selection
   void* topk;
   void* mla;
 };
@@ -80,6 +81,7 @@ size_t decode_ws_parts(int32_t rows, int64_t max_ctx, int32_t k, DecodeWs* out, 
   const size_t s_scores = align256((size_t)rows * ld * sizeof(float));
   const size_t s_len = align256((size_t)rows * sizeof(int32_t));
   const size_t s_idx = align256((size_t)rows * k * sizeof(int32_t));
+  const size_t s_slots = s_idx;
   const size_t s_topk = align256(topk_ws_bytes(rows, ld));
   const size_t s_mla = align256(mla_ws_bytes(rows, k, true));
   if (out) {
@@ -90,13 +92,15 @@ size_t decode_ws_parts(int32_t rows, int64_t max_ctx, int32_t k, DecodeWs* out, 
     off += s_len;
     out->idx = reinterpret_cast<int32_t*>(p + off);
     off += s_idx;
+    out->slots = reinterpret_cast<int32_t*>(p + off);
+    off += s_slots;
     out->topk = p + off;
     off += s_topk;
     out->mla = s_mla ? p + off : nullptr;
     off += s_mla;
     return off;
   }
-  return s_scores + s_len + s_idx + s_topk + s_mla;
+  return s_scores + s_len + s_idx + s_slots + s_topk + s_mla;
 }
 
 int32_t run_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows, int32_t k, int32_t* idx,
@@ -106,10 +110,12 @@ int32_t run_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_
 }
 
 int32_t run_mla(const dsa_batch* batch, const dsa_cache* cache, const void* q, const int32_t* idx, int32_t k,
-                float softmax_scale, void* out, float* lse, void* ws, bool split, hipStream_t st) {
+                float softmax_scale, void* out, float* lse, void* ws, bool split, hipStream_t st,
+                const int32_t* slots = nullptr) {
   MlaArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.idx = idx;
+  a.slots = slots;
   a.lat_fp8 = cache->lat_fp8;
   a.lat_scale = cache->lat_scale;
   a.block_table = batch->block_table;
@@ -260,13 +266,18 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
   a.ld = ld;
   if ((r = hip_status(launch_index_score(a, batch->num_requests, batch->max_ctx, false, st), "decode score")))
     return r;
-  // 2. select (the visible lengths are derived on the way)
+  // 2. select (the visible lengths are derived on the way), also writing the
+  //    cache rows of the selection so that attention reads no block table
+  SlotOut so;
+  so.slots = p.slots;
+  so.block_table = batch->block_table;
+  so.max_blocks = batch->max_blocks;
   if ((r = hip_status(launch_topk(p.scores, ld, p.row_len, rows, ld, k, idx, tw, st, batch->ctx_len,
-                                  batch->rows_per_request),
+                                  batch->rows_per_request, so),
                       "decode topk")))
     return r;
   // 3. attend
-  return run_mla(batch, cache, q_mla, idx, k, softmax_scale, out, lse, p.mla, true, st);
+  return run_mla(batch, cache, q_mla, idx, k, softmax_scale, out, lse, p.mla, true, st, p.slots);
 }
 
 size_t dsa_workspace_size(int32_t kind, int32_t rows, int64_t max_ctx, int32_t k, int32_t num_heads) {

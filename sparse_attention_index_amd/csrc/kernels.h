@@ -35,16 +35,26 @@ struct TopkWs {
 size_t topk_ws_bytes(int rows, int64_t max_len);
 TopkWs topk_ws_carve(void* ws, int rows, int64_t max_len);
 
+// Physical cache slots of a selection (page id * 64 + offset, -1 for
+// padding), for rows laid out request-major with R rows per request.
+struct SlotOut {
+  int32_t* slots = nullptr;              // [rows][k], or null: not emitted
+  const int32_t* block_table = nullptr;  // [B][max_blocks]
+  int32_t max_blocks = 0;
+};
 // idx[row][0..k) = the k largest scores[row][0..row_len[row]) (positions,
 // unordered; -1 padding for rows shorter than k). With ctx_len != null the
 // visible lengths are derived (ctx_len[row / R] - R + row % R + 1) and also
-// written to row_len; otherwise row_len is read.
+// written to row_len; otherwise row_len is read. With so.slots set, the
+// selection's physical slots are written too.
 hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int rows, int64_t max_len, int k,
-                       int32_t* idx, const TopkWs& w, hipStream_t st, const int32_t* ctx_len = nullptr, int R = 1);
+                       int32_t* idx, const TopkWs& w, hipStream_t st, const int32_t* ctx_len = nullptr, int R = 1,
+                       const SlotOut& so = SlotOut{});
 
 struct MlaArgs {
   const uint16_t* q;        // bf16 [rows][16][576]
   const int32_t* idx;       // [rows][k]
+  const int32_t* slots = nullptr;  // [rows][k] physical slots of idx, or null (then idx goes through block_table)
   const uint8_t* lat_fp8;   // [num_blocks][64][576]
   const float* lat_scale;   // [num_blocks][64]
   const int32_t* block_table;

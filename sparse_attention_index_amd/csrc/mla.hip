@@ -109,13 +109,18 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
 
   // Resolve every selected position of this split to a cache row up front
   // (-1: skipped; also the padding of the last tile).
-  for (int j = tid; j < ntiles * TK; j += 512) {
-    int32_t ra = -1;
-    if (j < nkeys) {
-      const int pos = sel[kbeg + j];
-      if (pos >= 0 && pos < a.max_blocks * kBlock) ra = table[pos >> 6] * kBlock + (pos & 63);
+  if (a.slots) {  // the selection arrives as cache rows already
+    const int32_t* sl = a.slots + (size_t)row * a.k;
+    for (int j = tid; j < ntiles * TK; j += 512) rowaddr_s[j] = j < nkeys ? sl[kbeg + j] : -1;
+  } else {
+    for (int j = tid; j < ntiles * TK; j += 512) {
+      int32_t ra = -1;
+      if (j < nkeys) {
+        const int pos = sel[kbeg + j];
+        if (pos >= 0 && pos < a.max_blocks * kBlock) ra = table[pos >> 6] * kBlock + (pos & 63);
+      }
+      rowaddr_s[j] = ra;
     }
-    rowaddr_s[j] = ra;
   }
   // Query fragments: lane holds head n, dims 32s + 8g + [0,8) for step s.
   bf16x8 qa[18];

@@ -408,10 +408,22 @@ struct FinalLds {
 //     pass emits everything above b and gathers b's elements into LDS.
 //  3. Further 11-bit steps over the gathered elements resolve the rest
 //     (without the gather, when b holds more than kBinLds elements).
+// Where the i-th selected position goes: out[i], and with a page table also
+// its physical cache slot (page id * 64 + offset) to slots[i].
+struct Emit {
+  int32_t* out;
+  int32_t* slots;      // or null
+  const int32_t* tbl;  // page ids of the row's request (LDS), when slots is set
+  DSA_DEV void operator()(uint32_t i, uint32_t pos) const {
+    out[i] = (int32_t)pos;
+    if (slots) slots[i] = tbl[pos >> 6] * kBlock + (int32_t)(pos & 63);
+  }
+};
+
 // With have_bounds, [lo0, hi0] is given to hold every composite (the pass
 // that finds the exact extremes is skipped).
 template <class CompAt>
-DSA_DEV void select_top(SelectLds& L, int64_t count, int k, int32_t* __restrict__ out, CompAt comp_at,
+DSA_DEV void select_top(SelectLds& L, int64_t count, int k, const Emit& out, CompAt comp_at,
                         bool have_bounds = false, uint64_t lo0 = 0, uint64_t hi0 = 0) {
   const int t = threadIdx.x;
   uint64_t lo = lo0, hi = hi0;
@@ -431,7 +443,7 @@ DSA_DEV void select_top(SelectLds& L, int64_t count, int k, int32_t* __restrict_
   }
   // the composites are distinct, so lo == hi only for a single element
   if (lo == hi) {
-    if (t == 0) out[0] = (int32_t)~(uint32_t)hi;
+    if (t == 0) out(0, ~(uint32_t)hi);
     return;
   }
   int shift = 64 - __clzll((long long)(lo ^ hi));  // bits below the shared prefix
@@ -468,7 +480,7 @@ DSA_DEV void select_top(SelectLds& L, int64_t count, int k, int32_t* __restrict_
     for (int64_t i = t; i < count; i += kTF) {
       const uint64_t c = comp_at(i);
       if ((c >> b_shift) > b) {
-        if (sa < (uint32_t)k) out[sa] = (int32_t)~(uint32_t)c;
+        if (sa < (uint32_t)k) out(sa, ~(uint32_t)c);
         ++sa;
       } else if (gather && (c >> b_shift) == b) {
         if (sb < (uint32_t)kBinLds) L.bin[sb] = c;
@@ -482,7 +494,7 @@ DSA_DEV void select_top(SelectLds& L, int64_t count, int k, int32_t* __restrict_
   if (th.at == need) {  // all of b is selected
     if (gather) {
       for (uint32_t i = t; i < th.at && emitted0 + i < (uint32_t)k; i += kTF)
-        out[emitted0 + i] = (int32_t)~(uint32_t)L.bin[i];
+        out(emitted0 + i, ~(uint32_t)L.bin[i]);
     } else {
       if (t == 0) L.emitted = 0;
       __syncthreads();
@@ -495,7 +507,7 @@ DSA_DEV void select_top(SelectLds& L, int64_t count, int k, int32_t* __restrict_
           take = (c >> b_shift) == b;
         }
         const uint32_t slot = wave_append(&L.emitted, take);
-        if (take && emitted0 + slot < (uint32_t)k) out[emitted0 + slot] = (int32_t)~(uint32_t)c;
+        if (take && emitted0 + slot < (uint32_t)k) out(emitted0 + slot, ~(uint32_t)c);
       }
     }
     return;
@@ -534,7 +546,7 @@ DSA_DEV void select_top(SelectLds& L, int64_t count, int k, int32_t* __restrict_
       take = (gather || (c >> b_shift) == b) && (c >> shift) >= prefix;
     }
     const uint32_t slot = wave_append(&L.emitted, take);
-    if (take && emitted0 + slot < (uint32_t)k) out[emitted0 + slot] = (int32_t)~(uint32_t)c;
+    if (take && emitted0 + slot < (uint32_t)k) out(emitted0 + slot, ~(uint32_t)c);
   }
 }
 
@@ -552,7 +564,8 @@ struct ShortLds {
   SelectLds f;
   uint32_t cnt;
   uint32_t wmax[kTF / 64];
-  uint2 elems[kFinalLds + 1];  // survivors, plus one spare entry taking overflow writes
+  int32_t tbl[kShortMax / kBlock];  // page ids of the row's request (when slots are emitted)
+  uint2 elems[kFinalLds + 1];       // survivors, plus one spare entry taking overflow writes
 };
 
 // key >= T as a float comparison (scores are not NaN): T is the lower edge of
@@ -565,7 +578,7 @@ DSA_DEV float key_threshold_float(uint32_t T) {
 template <bool VEC>
 __global__ __launch_bounds__(kTF) void topk_short_kernel(const float* __restrict__ scores, int64_t ld,
                                                        int32_t* __restrict__ row_len, const int32_t* ctx_len, int R,
-                                                       int k, int32_t* __restrict__ idx) {
+                                                       int k, int32_t* __restrict__ idx, SlotOut so) {
   constexpr int G = kShortPer / 4;  // 16-byte groups per thread
   __shared__ ShortLds L;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -573,10 +586,19 @@ __global__ __launch_bounds__(kTF) void topk_short_kernel(const float* __restrict
   const int n = (int)visible_len(row_len, ctx_len, R, row, ld);  // <= ld <= kShortMax
   if (ctx_len && t == 0) row_len[row] = n;  // published for the caller
   int32_t* out = idx + (size_t)row * k;
+  int32_t* slots = so.slots ? so.slots + (size_t)row * k : nullptr;
+  const int32_t* table = so.slots ? so.block_table + (size_t)(row / R) * so.max_blocks : nullptr;
   if (n <= k) {  // every visible position is selected; the rest is padding
-    for (int i = t; i < k; i += kTF) out[i] = i < n ? i : -1;
+    for (int i = t; i < k; i += kTF) {
+      out[i] = i < n ? i : -1;
+      if (slots) slots[i] = i < n && (i >> 6) < so.max_blocks ? table[i >> 6] * kBlock + (i & 63) : -1;
+    }
     return;
   }
+  // the request's page ids, loaded first so that waiting for them waits for nothing else
+  int32_t tv = 0;
+  const int npages = (n + kBlock - 1) / kBlock;
+  if (slots && t < npages) tv = t < so.max_blocks ? table[t] : -1;
   const float* s = scores + (size_t)row * ld;
   uint32_t skey[kSample / kTF];
   sample_load<kTF>(s, n, skey);
@@ -602,6 +624,7 @@ __global__ __launch_bounds__(kTF) void topk_short_kernel(const float* __restrict
     }
   }
   if (t == 0) L.cnt = 0;
+  if (slots && t < npages) L.tbl[t] = tv;  // read after the barriers below
   lds_barrier();  // the counter is cleared before any wave reserves (the row loads stay in flight)
   const uint32_t T = sample_select<kTF>(skey, n, k, L.f.hist, L.f.scan);
   const float Tf = key_threshold_float(T);
@@ -658,13 +681,14 @@ __global__ __launch_bounds__(kTF) void topk_short_kernel(const float* __restrict
   __syncthreads();
   const uint32_t count = L.cnt;
   const uint32_t kmax = wave_max32(lane < kTF / 64 ? L.wmax[lane] : 0u);
+  const Emit emit{out, slots, L.tbl};
   if (count >= (uint32_t)k && count <= (uint32_t)kFinalLds)
     select_top(
-        L.f, count, k, out,
+        L.f, count, k, emit,
         [&](int64_t i) { return composite(ordered_key(__uint_as_float(L.elems[i].x)), L.elems[i].y); }, true,
         (uint64_t)T << 32, ((uint64_t)kmax << 32) | 0xffffffffull);
   else  // the sample missed: select over the whole row
-    select_top(L.f, n, k, out, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
+    select_top(L.f, n, k, emit, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
 }
 
 // ------------------------------------------------------------------ long rows
@@ -778,8 +802,8 @@ __global__ __launch_bounds__(kT) void topk_slice_kernel(const float* __restrict_
 // per workgroup would write back each XCD's L2). Every survivor lies in
 // [T << 32, (largest key << 32) | ~0], which saves select_top a pass.
 __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict__ scores, int64_t ld,
-                                                       const int32_t* __restrict__ row_len, int slices, int k,
-                                                       int32_t* __restrict__ idx, TopkWs w) {
+                                                       const int32_t* __restrict__ row_len, int R, int slices, int k,
+                                                       int32_t* __restrict__ idx, TopkWs w, SlotOut so) {
   __shared__ FinalLds L;
   __shared__ uint32_t kmax_s;
   const int t = threadIdx.x;
@@ -788,8 +812,14 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
   int32_t* out = idx + (size_t)row * k;
   if (n <= k) {  // every visible position is selected; the rest is padding
     for (int64_t i = t; i < k; i += kTF) out[i] = i < n ? (int32_t)i : -1;
+    if (so.slots) {
+      const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
+      for (int i = t; i < k; i += kTF)
+        so.slots[(size_t)row * k + i] = i < n && (i >> 6) < so.max_blocks ? table[i >> 6] * kBlock + (i & 63) : -1;
+    }
     return;
   }
+  const Emit emit{out, nullptr, nullptr};
   // slices' counts and their offsets in LDS: lane t of wave 0 owns slice t
   const uint32_t sub = (uint32_t)(w.cap / slices);
   if (t < 64) {
@@ -834,11 +864,32 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
     }
     __syncthreads();
     select_top(
-        L.s, count, k, out, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); }, true,
+        L.s, count, k, emit, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); }, true,
         (uint64_t)T << 32, ((uint64_t)kmax_s << 32) | 0xffffffffull);
   } else {  // the sample missed: select over the whole row
     const float* s = scores + (size_t)row * ld;
-    select_top(L.s, n, k, out, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
+    select_top(L.s, n, k, emit, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
+  }
+  // physical slots of the selection (rows of this length have too many pages
+  // to stage their table in LDS): every thread translates its entries with
+  // all its loads in flight
+  if (so.slots) {
+    __syncthreads();  // the selection is written (workgroup-visible)
+    const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
+    constexpr int kPer = (kMaxTopk + kTF - 1) / kTF;
+    int32_t pos[kPer], page[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = t + j * kTF;
+      pos[j] = i < k ? out[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) page[j] = pos[j] >= 0 && (pos[j] >> 6) < so.max_blocks ? table[pos[j] >> 6] : -1;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = t + j * kTF;
+      if (i < k) so.slots[(size_t)row * k + i] = page[j] >= 0 ? page[j] * kBlock + (pos[j] & 63) : -1;
+    }
   }
 }
 
@@ -849,15 +900,16 @@ static bool vec_ok(const float* scores, int64_t ld) {
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int rows, int64_t max_len, int k,
-                       int32_t* idx, const TopkWs& w, hipStream_t st, const int32_t* ctx_len, int R) {
+                       int32_t* idx, const TopkWs& w, hipStream_t st, const int32_t* ctx_len, int R,
+                       const SlotOut& so) {
   const bool vec = vec_ok(scores, ld);
   if (max_len <= kShortMax) {
     if (vec)
       hipLaunchKernelGGL(topk_short_kernel<true>, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, ctx_len, R, k,
-                         idx);
+                         idx, so);
     else
       hipLaunchKernelGGL(topk_short_kernel<false>, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, ctx_len, R, k,
-                         idx);
+                         idx, so);
     return hipGetLastError();
   }
   // Slices: enough workgroups to cover the GPU twice, at least 4096 scores
@@ -878,7 +930,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int ro
                        (int)slice, k, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_final_kernel, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, ns, k, idx, w);
+  hipLaunchKernelGGL(topk_final_kernel, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, R, ns, k, idx, w, so);
   return hipGetLastError();
 }
 

@@ -29,9 +29,15 @@ CASES = {
     "fp8q_2x7": dict(B=2, R=7, lengths=[5000, 3333], seed=108, fp8_query=True, permute_blocks=True),
 }
 
+# fused decode only: rows past the single-workgroup top-k path (sliced
+# selection), with a row shorter than k, over permuted pages
+FUSED_ONLY = {
+    "2x2_long_perm": dict(B=2, R=2, lengths=[50000, 1500], seed=109, permute_blocks=True),
+}
+
 
 def _case(name, **over):
-    kw = dict(CASES[name])
+    kw = dict({**CASES, **FUSED_ONLY}[name])
     kw.update(over)
     print(f"\n[case] {name} {kw}", flush=True)
     return make_case(name=name, **kw).to("cuda")
@@ -184,7 +190,7 @@ def test_sparse_mla_skips_invalid_entries(gpu):
         assert np.all(out[3] == 0) and np.all(np.isneginf(lse[3]))
 
 
-@pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "3x3_short_perm", "1x8"])
+@pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "3x3_short_perm", "1x8", "2x2_long_perm"])
 def test_fused_decode_matches_oracle_and_stages(gpu, name):
     case = _case(name)
     out, lse, idx = gpu_decode(case)
