@@ -414,7 +414,9 @@ hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8
     else if (a.R > 4) launch_variant<2, true>(a, B, max_ctx, st);
     else launch_variant<1, true>(a, B, max_ctx, st);
   } else {
-    launch_variant<1, false>(a, B, max_ctx, st);
+    // up to 8 verification rows read each page once
+    if (a.R > 4) launch_variant<2, false>(a, B, max_ctx, st);
+    else launch_variant<1, false>(a, B, max_ctx, st);
   }
   return hipGetLastError();
 }

@@ -26,7 +26,8 @@ from workloads import case_config, make_case
 
 pytestmark = pytest.mark.gpu
 
-DECODE = ["decode_1x1_8k", "decode_16x4_32k", "decode_16x4_ragged_128k_256k", "decode_4x4_1m_planted"]
+DECODE = ["decode_1x1_8k", "decode_16x4_32k", "decode_16x8_32k", "decode_16x4_ragged_128k_256k",
+          "decode_4x4_1m_planted"]
 
 
 def _make(name):

@@ -24,6 +24,8 @@ CASES = {
     "3x3_short_perm": dict(B=3, R=3, lengths=[700, 64, 4099], seed=103, permute_blocks=True),
     "1x8": dict(B=1, R=8, lengths=[2500], seed=104),
     "2x5": dict(B=2, R=5, lengths=[1000, 1300], seed=105),
+    "2x7_perm": dict(B=2, R=7, lengths=[2900, 4100], seed=111, permute_blocks=True),
+    "1x12": dict(B=1, R=12, lengths=[3100], seed=112),
     "1x2_tiny": dict(B=1, R=2, lengths=[130], seed=106),
     "fp8q_1x64": dict(B=1, R=64, lengths=[2048 + 64], seed=107, fp8_query=True),
     "fp8q_2x7": dict(B=2, R=7, lengths=[5000, 3333], seed=108, fp8_query=True, permute_blocks=True),

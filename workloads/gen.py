@@ -217,12 +217,13 @@ def make_case(
     )
 
 
-# The five workloads the path is measured and checked on. Seeds are fixed per
+# The workloads the path is measured and checked on. Seeds are fixed per
 # workload so every run regenerates the same bytes on the same device.
 WORKLOADS = {
     "decode_1x1_8k": dict(B=1, R=1, lengths=[8192], seed=20260001),
     "decode_16x4_32k": dict(B=16, R=4, lengths=[32768] * 16, seed=20260002),
     "decode_16x4_ragged_128k_256k": dict(B=16, R=4, lengths=None, seed=20260003, permute_blocks=True),
+    "decode_16x8_32k": dict(B=16, R=8, lengths=[32768] * 16, seed=20260006),
     "decode_4x4_1m_planted": dict(B=4, R=4, lengths=[1 << 20] * 4, seed=20260004, plant_frac=0.01),
     "prefill_4096_on_128k": dict(B=1, R=4096, lengths=[131072 + 4096], seed=20260005, fp8_query=True),
 }
