@@ -18,10 +18,13 @@
 //  2. QK: wave w computes the logits of 16 heads x 16 tokens [16w, 16w+16)
 //     with 18 v_mfma_f32_16x16x32_bf16 steps (queries bf16 in VGPRs for the
 //     whole call, latent E4M3 widened to bf16 exactly);
-//  3. online softmax: per-head tile maxima (DPP row reductions over the 16
-//     tokens a lane group holds) are combined across the 8 waves in LDS so
-//     that every wave rescales identically; row sums stay per wave and are
-//     combined once at the end;
+//  3. online softmax against a per-head reference shared by all waves: p =
+//     exp(logit - reference). The reference only moves when a logit of the
+//     tile exceeds it by more than kSlack (always on the first tile with a
+//     valid token); only then do the waves exchange tile maxima (DPP row
+//     reductions, then LDS) and rescale the partial output and sums, so the
+//     common tile needs one barrier for the softmax instead of two. Row sums
+//     stay per lane and are combined once at the end;
 //  4. PV: probabilities (times the token's latent scale) go to LDS as bf16;
 //     wave w accumulates out dims [64w, 64w+64) with 16x16x32 bf16 MFMA.
 //     The V operand needs 8 consecutive tokens of one dim per lane; it comes
@@ -45,6 +48,7 @@ static constexpr int TILE_B = TK * kLat;             // 73,728 bytes
 static constexpr int kWaves = 8;
 static constexpr int kPer = TK * kChunks / (64 * kWaves);  // chunk copies per lane per tile (9)
 static constexpr int PP = TK + 8;                    // LDS bf16 per probability row (padded)
+static constexpr float kSlack = 8.f;                 // p stays below e^8 against a lagging reference
 
 struct MlaPart {
   float* o;   // [rows][splits][16][512]
@@ -89,6 +93,7 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
   __shared__ __attribute__((aligned(16))) float scl_r[NBUF][TK];
   __shared__ __attribute__((aligned(16))) __bf16 p_s[kMlaHeads * PP];
   __shared__ float mx_s[kWaves][kMlaHeads];
+  __shared__ __attribute__((aligned(8))) uint8_t flag_s[kWaves];  // per wave: a logit passed the reference
   __shared__ int32_t rowaddr_s[kMaxTopk];
   __shared__ uint32_t tile_bad[kMaxTopk / TK];
 
@@ -150,16 +155,21 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
   }
   // Copy tile t into ring slot t % 2 (skipped rows read row 0 and are zeroed
   // after arrival). Waves 0 and 1 also copy the tile's 128 scales.
-  auto issue = [&](int t) {
+  // Copies i0 .. i1-1 of this wave for tile t; the part ending at kPer also
+  // takes the scales. A tile's copies go out in three parts spread over the
+  // previous tile's compute: a wave issuing many gathers at once stalls on
+  // the full memory queue while the others wait for it at the next barrier.
+  auto issue = [&](int t, int i0, int i1) {
     uint8_t* dst = ring[t % NBUF];
     const int rb = t * TK;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
+      if (i < i0 || i >= i1) continue;
       const int ra = rowaddr_s[rb + cr[i]];
       const uint8_t* src = a.lat_fp8 + (size_t)(ra >= 0 ? ra : 0) * kLat + cj[i] * 16;
       copy16_to_lds(src, dst + 1024 * (kPer * wave + i));
     }
-    if (wave < 2) {
+    if (i1 == kPer && wave < 2) {
       const int ra = rowaddr_s[rb + 64 * wave + lane];
       copy4_to_lds(a.lat_scale + (ra >= 0 ? ra : 0), &scl_r[t % NBUF][64 * wave]);
     }
@@ -168,6 +178,10 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
   f32x4 o[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // m_run: the softmax reference of each head, the same in every wave; it is
+  // the running maximum except that it only moves when a logit exceeds it by
+  // more than kSlack (then p <= e^kSlack). l_run: this lane's partial sum of
+  // p over the tokens it held, relative to m_run.
   float m_run[4], l_run[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -175,7 +189,7 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
     l_run[i] = 0.f;
   }
   wait_vmcnt<0>();  // query fragments in VGPRs before any copy is counted
-  if (ntiles > 0) issue(0);
+  if (ntiles > 0) issue(0, 0, kPer);
 
   for (int t = 0; t < ntiles; ++t) {
     uint8_t* tile = ring[t % NBUF];
@@ -190,7 +204,8 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
       if (wave < 2 && rowaddr_s[rb + 64 * wave + lane] < 0) scl[64 * wave + lane] = 0.f;
     }
     lds_barrier();  // tile t complete in LDS for all waves; tile t-1 fully consumed
-    if (t + 1 < ntiles) issue(t + 1);  // into the slot tile t-1 used
+    const bool more = t + 1 < ntiles;  // tile t + 1 goes into the slot tile t - 1 used
+    if (more) issue(t + 1, 0, 3);
 
     // QK: logits for tokens 16*wave + n, heads 4g + i
     const int tok = 16 * wave + n;
@@ -207,38 +222,59 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
         if (jp >= kChunks) jp -= kChunks;
       }
     }
+    if (more) issue(t + 1, 3, 6);
+    // Softmax against the current reference. Only if some logit of the tile
+    // exceeds it by more than kSlack (always on the first tile with a valid
+    // token) do the waves exchange tile maxima and move the reference, which
+    // rescales the partial output and sums; the result is the same either way.
     const bool valid = rowaddr_s[t * TK + tok] >= 0;
     const float sc = scl[tok];
     const float f = a.sm_scale * sc;
-    float x[4];
+    float x[4], p[4];
+    bool over = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[i] = valid ? sacc[i] * f : -INFINITY;
-      const float mx = row_max16(x[i]);
-      if (n == 0) mx_s[wave][4 * g + i] = mx;
+      over |= x[i] > m_run[i] + kSlack;
+      p[i] = (x[i] == -INFINITY) ? 0.f : __expf(x[i] - m_run[i]);
+      p_s[(4 * g + i) * PP + tok] = (__bf16)(p[i] * sc);
     }
+    const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;  // all lanes take part
+    if (lane == 0) flag_s[wave] = wave_over ? 1 : 0;
     lds_barrier();
-    float alpha[4];
+    const uint64_t flags = *reinterpret_cast<const uint64_t*>(flag_s);
+    if (flags != 0) {  // every wave reads the same flags: a uniform branch
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * g + i;
-      float tmax = mx_s[0][h];
+      for (int i = 0; i < 4; ++i) {
+        const float mx = row_max16(x[i]);
+        if (n == 0) mx_s[wave][4 * g + i] = mx;
+      }
+      lds_barrier();
+      float alpha[4];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) tmax = fmaxf(tmax, mx_s[w][h]);
-      const float mnew = fmaxf(m_run[i], tmax);
-      alpha[i] = (mnew == -INFINITY) ? 1.f : __expf(m_run[i] - mnew);
-      const float p = (x[i] == -INFINITY) ? 0.f : __expf(x[i] - mnew);
-      m_run[i] = mnew;
-      p_s[h * PP + tok] = (__bf16)(p * sc);
-      l_run[i] = l_run[i] * alpha[i] + row_sum16(p);
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * g + i;
+        float tmax = mx_s[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) tmax = fmaxf(tmax, mx_s[w][h]);
+        const float mnew = fmaxf(m_run[i], tmax);
+        alpha[i] = (mnew == -INFINITY) ? 1.f : __expf(m_run[i] - mnew);
+        p[i] = (x[i] == -INFINITY) ? 0.f : __expf(x[i] - mnew);
+        m_run[i] = mnew;
+        p_s[h * PP + tok] = (__bf16)(p[i] * sc);
+        l_run[i] *= alpha[i];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
+      lds_barrier();
     }
-    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l_run[i] += p[i];
+    if (more) issue(t + 1, 6, kPer);
 
     // PV: out[:, 64w .. 64w+64) += P . V over the tile's 128 tokens
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
 #pragma unroll
     for (int s = 0; s < TK / 32; ++s) {
       const bf16x8 pa = *reinterpret_cast<const bf16x8*>(p_s + n * PP + 32 * s + 8 * g);
@@ -252,7 +288,9 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
     }
   }
 
-  // Row sums: every wave holds the part of its own tokens.
+  // Row sums: every lane holds the part of its own tokens.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l_run[i] = row_sum16(l_run[i]);
   __syncthreads();
   if (n == 0)
 #pragma unroll
