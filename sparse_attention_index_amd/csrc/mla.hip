@@ -16,8 +16,9 @@
 //     stored unpadded with their 16-byte chunks rotated by the row index,
 //     which spreads both read patterns below over distinct LDS banks;
 //  2. QK: wave w computes the logits of 16 heads x 16 tokens [16w, 16w+16)
-//     with 18 v_mfma_f32_16x16x32_bf16 steps (queries bf16 in VGPRs for the
-//     whole call, latent E4M3 widened to bf16 exactly);
+//     with FP8 MFMAs on the raw E4M3 latent (no conversion): the bf16 query
+//     is split exactly into two E4M3 terms with a power-of-two block scale
+//     per head, once per workgroup, and stays in VGPRs for the whole call;
 //  3. online softmax against a per-head reference shared by all waves: p =
 //     exp(logit - reference). The reference only moves when a logit of the
 //     tile exceeds it by more than kSlack (always on the first tile with a
@@ -127,13 +128,14 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
       rowaddr_s[j] = ra;
     }
   }
-  // Query fragments: lane holds head n, dims 32s + 8g + [0,8) for step s.
-  bf16x8 qa[18];
+  // This thread's share of the query for the split below: head tid / 32,
+  // dims 18 (tid % 32) + [0, 18), as 9 pairs of bf16.
+  uint32_t qpair[9];
   {
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) +
-                                                       ((size_t)row * kMlaHeads + n) * kLat + 8 * g);
+    const uint32_t* qp = reinterpret_cast<const uint32_t*>(a.q) +
+                         (((size_t)row * kMlaHeads + (tid >> 5)) * kLat + 18 * (tid & 31)) / 2;
 #pragma unroll
-    for (int s = 0; s < 18; ++s) qa[s] = qp[4 * s];
+    for (int j = 0; j < 9; ++j) qpair[j] = qp[j];
   }
   __syncthreads();  // rowaddr_s complete
   if (tid < ntiles) {
@@ -188,8 +190,65 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
     m_run[i] = -INFINITY;
     l_run[i] = 0.f;
   }
-  wait_vmcnt<0>();  // query fragments in VGPRs before any copy is counted
+  wait_vmcnt<0>();  // nothing but the copies is outstanding from here on
   if (ntiles > 0) issue(0, 0, kPer);
+
+  // Query as the A operand of 16x16x128 FP8 MFMAs. Each bf16 value is split
+  // exactly into two E4M3 terms, q 2^e = hi + lo, with a power of two 2^e
+  // per head that puts the head's largest magnitude in (224, 448]; 2^-e goes
+  // back in through the MFMA's A-operand block scale. (bf16 carries 8
+  // significant bits, each E4M3 term 4; only elements ~2^10 below the head
+  // maximum lose low bits, to E4M3's subnormal step.) The workgroup splits
+  // the query once, each thread 18 values, into [head][640] byte planes
+  // staged in ring slot 1 (dims 576-639 zero), which tile 1's copies only
+  // overwrite after the loop's first barrier; lane (g, n) then reads head
+  // n, dims 128s + 32g + [0, 32) of step s.
+  i32x8 qh[5], ql[5];
+  int qscale;  // E8M0 exponent of 2^-e for this lane's head
+  {
+    constexpr int kQRow = 640;
+    uint8_t* qhi = ring[1];
+    uint8_t* qlo = ring[1] + kMlaHeads * kQRow;
+    int* ex_s = reinterpret_cast<int*>(ring[1] + 2 * kMlaHeads * kQRow);
+    const int hq = tid >> 5, kq = tid & 31;
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 9; ++j)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(qpair[j] << 16)), fabsf(__uint_as_float(qpair[j] & 0xffff0000u))));
+    amax = row_max16(amax);
+    amax = fmaxf(amax, __shfl_xor(amax, 16));  // the 32 threads of a head
+    int ex = 0;
+    if (amax > 0.f) {
+      int e2;
+      const float fr = frexpf(amax, &e2);  // amax = fr 2^e2, fr in [0.5, 1)
+      ex = max(min((fr <= 0.875f ? 9 : 8) - e2, 127), -127);
+    }
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      const float x0 = ldexpf(__uint_as_float(qpair[j] << 16), ex);
+      const float x1 = ldexpf(__uint_as_float(qpair[j] & 0xffff0000u), ex);
+      const uint32_t hb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false) & 0xffffu;
+      const auto hf = __builtin_amdgcn_cvt_pk_f32_fp8(hb, false);
+      const uint32_t lb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0 - hf[0], x1 - hf[1], 0, false) & 0xffffu;
+      *reinterpret_cast<uint16_t*>(qhi + hq * kQRow + 18 * kq + 2 * j) = (uint16_t)hb;
+      *reinterpret_cast<uint16_t*>(qlo + hq * kQRow + 18 * kq + 2 * j) = (uint16_t)lb;
+    }
+    if (kq < 16) {
+      *reinterpret_cast<uint32_t*>(qhi + hq * kQRow + kLat + 4 * kq) = 0u;
+      *reinterpret_cast<uint32_t*>(qlo + hq * kQRow + kLat + 4 * kq) = 0u;
+    }
+    if (kq == 0) ex_s[hq] = ex;
+    lds_barrier();  // staged (the tile-0 copies stay in flight)
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+      const u32x4* ph = reinterpret_cast<const u32x4*>(qhi + n * kQRow + 128 * s + 32 * g);
+      const u32x4* pl = reinterpret_cast<const u32x4*>(qlo + n * kQRow + 128 * s + 32 * g);
+      const u32x4 h0 = ph[0], h1 = ph[1], l0 = pl[0], l1 = pl[1];
+      qh[s] = i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+      ql[s] = i32x8{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+    }
+    qscale = 127 - ex_s[n];
+  }
 
   for (int t = 0; t < ntiles; ++t) {
     uint8_t* tile = ring[t % NBUF];
@@ -207,20 +266,33 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
     const bool more = t + 1 < ntiles;  // tile t + 1 goes into the slot tile t - 1 used
     if (more) issue(t + 1, 0, 3);
 
-    // QK: logits for tokens 16*wave + n, heads 4g + i
+    // QK: logits for tokens 16*wave + n, heads 4g + i (D layout); lane
+    // (g, n) supplies token n's dims 128s + 32g + [0, 32) as the B operand,
+    // two 16-byte chunks of its row with no conversion (step 4, groups 2-3:
+    // a repeat of valid chunks, multiplied by zero queries)
     const int tok = 16 * wave + n;
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sacc;
     {
-      int jp = (g >> 1) + (tok % kChunks);
-      if (jp >= kChunks) jp -= kChunks;
-      const uint8_t* kr = tile + tok * kLat + 8 * (g & 1);
+      f32x4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+      int tk = tok;
+      asm volatile("" : "+v"(tk));  // offsets recomputed per tile rather than held in registers
+      const uint8_t* kr = tile + tk * kLat;
+      const int rot = tk % kChunks;
 #pragma unroll
-      for (int s = 0; s < 18; ++s) {
-        const uint2 v = *reinterpret_cast<const uint2*>(kr + 16 * jp);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], e4m3x8_bf16(v.x, v.y), sacc, 0, 0, 0);
-        jp += 2;
-        if (jp >= kChunks) jp -= kChunks;
+      for (int s = 0; s < 5; ++s) {
+        int c = 8 * s + 2 * g;
+        if (c >= kChunks) c -= 4;
+        int c0 = c + rot, c1 = c + 1 + rot;
+        if (c0 >= kChunks) c0 -= kChunks;
+        if (c1 >= kChunks) c1 -= kChunks;
+        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kr + 16 * c0);
+        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kr + 16 * c1);
+        const i32x8 bk = {(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                          (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+        ah = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qh[s], bk, ah, 0, 0, 0, qscale, 0, 127);
+        al = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ql[s], bk, al, 0, 0, 0, qscale, 0, 127);
       }
+      sacc = ah + al;
     }
     if (more) issue(t + 1, 3, 6);
     // Softmax against the current reference. Only if some logit of the tile
