@@ -37,6 +37,7 @@ from .dsa import (  # noqa: F401
     topk_positions,
 )
 from .traffic import dsa_bytes, dense_mla_bytes, counted_bytes  # noqa: F401
+from .mxfp4 import e2m1_table, mxfp4_decode, mxfp4_encode  # noqa: F401
 from .key_write import (  # noqa: F401
     e4m3_encode,
     index_key_write,

@@ -10,8 +10,9 @@ Readings where the pages are silent (each is listed in the design doc):
 * a row at position p sees tokens 0..p, its own token included (the Write
   step runs before Score, so the row's key is already cached);
 * the score of token s is sum_h w_h * ReLU(q_h . khat_s) with khat_s the
-  dequantised key (E4M3 value times the token's fp32 scale); no other
-  constant is applied;
+  dequantised key (E4M3 value times the token's fp32 scale, or for MXFP4
+  keys each E2M1 value times its block's power of two); no other constant
+  is applied;
 * selection keeps min(k, visible) positions, ranked by score descending,
   ties broken by the lower position;
 * attention uses softmax over scale * q . chat_s on all 576 dims, values are
@@ -23,6 +24,7 @@ from __future__ import annotations
 import numpy as np
 
 from .fp8 import e4m3_decode
+from .mxfp4 import mxfp4_decode
 
 BLOCK = 64
 
@@ -107,8 +109,12 @@ def row_scores(case, row, positions=None, q_rows=None):
     positions = np.asarray(positions, dtype=np.int64)
     assert positions.size == 0 or positions.max() <= pos, "score requested for an unseen token"
     table = _np(case.block_table)[b]
-    keys_hat = dequant(gather_tokens(_np(case.key_fp8), table, positions),
-                       gather_tokens(_np(case.key_scale), table, positions))
+    if getattr(case, "key_format", "fp8") == "mxfp4":
+        keys_hat = mxfp4_decode(gather_tokens(_np(case.key_fp4), table, positions),
+                                gather_tokens(_np(case.key_e8m0), table, positions))
+    else:
+        keys_hat = dequant(gather_tokens(_np(case.key_fp8), table, positions),
+                           gather_tokens(_np(case.key_scale), table, positions))
     q = (q_rows if q_rows is not None else _query_rows(case))[row]
     return index_scores(q, _np(case.w)[row].astype(np.float64), keys_hat)
 

@@ -56,6 +56,9 @@ class DsaCase:
     sm_scale: float
     topk: int = TOPK
     planted: Optional[torch.Tensor] = None  # bool [B, max_ctx] planted tokens (structure record)
+    key_format: str = "fp8"  # "fp8" or "mxfp4"
+    key_fp4: Optional[torch.Tensor] = None  # uint8 [num_blocks, 64, 64] E2M1 pairs (mxfp4 keys)
+    key_e8m0: Optional[torch.Tensor] = None  # uint8 [num_blocks, 64, 4] E8M0 block scales (mxfp4 keys)
 
     @property
     def rows(self) -> int:
@@ -71,7 +74,7 @@ class DsaCase:
 
     @property
     def num_blocks(self) -> int:
-        return int(self.key_fp8.shape[0])
+        return int(self.lat_fp8.shape[0])
 
     def positions(self) -> torch.Tensor:
         """int64 [rows]: the position of each query row."""
@@ -119,6 +122,7 @@ def make_case(
     topk: int = TOPK,
     name: str = "custom",
     extra_blocks: int = 0,
+    key_format: str = "fp8",
 ) -> DsaCase:
     """Build one batch.
 
@@ -128,7 +132,13 @@ def make_case(
     tokens gets plant_sigma added along the unit vector of the request's
     head-weighted query sum before quantisation. fp8_query stores the indexer
     queries as E4M3 codes with one fp32 scale per query row (prefill chunks).
+    key_format "mxfp4" stores the index keys as MXFP4 instead (68 B per token:
+    64 bytes of E2M1 pairs and four E8M0 block scales), drawn directly in
+    that format: uniform random codes and block scales 2^-2 .. 2^1 (no
+    planted structure).
     """
+    assert key_format in ("fp8", "mxfp4")
+    assert not (key_format == "mxfp4" and plant_frac > 0), "planted keys are FP8 only"
     device = torch.device(device)
     lengths = [int(x) for x in lengths]
     assert len(lengths) == B and all(L >= R for L in lengths)
@@ -164,12 +174,20 @@ def make_case(
     w = torch.rand((rows, H_IDX), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
     q_mla = _bf16_normal((rows, H_MLA, D_LAT), gen, device)
 
-    key_fp8 = torch.empty((num_blocks, BLOCK, D_IDX), dtype=torch.uint8, device=device)
-    key_scale = torch.ones((num_blocks, BLOCK), dtype=torch.float32, device=device)
+    f4 = key_format == "mxfp4"
+    if f4:
+        key_fp8 = key_scale = None
+        key_fp4 = torch.zeros((num_blocks, BLOCK, D_IDX // 2), dtype=torch.uint8, device=device)
+        key_e8m0 = torch.full((num_blocks, BLOCK, D_IDX // 32), 127, dtype=torch.uint8, device=device)
+    else:
+        key_fp8 = torch.empty((num_blocks, BLOCK, D_IDX), dtype=torch.uint8, device=device)
+        key_scale = torch.ones((num_blocks, BLOCK), dtype=torch.float32, device=device)
+        key_fp4 = key_e8m0 = None
     lat_fp8 = torch.empty((num_blocks, BLOCK, D_LAT), dtype=torch.uint8, device=device)
     lat_scale = torch.ones((num_blocks, BLOCK), dtype=torch.float32, device=device)
     if extra_blocks:
-        key_fp8.zero_()
+        if not f4:
+            key_fp8.zero_()
         lat_fp8.zero_()
 
     planted = torch.zeros((B, max_blocks * BLOCK), dtype=torch.bool) if plant_frac > 0 else None
@@ -185,15 +203,21 @@ def make_case(
             mask_d = mask.to(device)
         for t0 in range(0, ntok, CH):
             t1 = min(ntok, t0 + CH)
-            k = torch.randn((t1 - t0, D_IDX), generator=gen, device=device)
-            if plant_frac > 0:
-                k += plant_sigma * mask_d[t0:t1, None].float() * u[None, :]
-            kc, ks = quantize_e4m3_rows(k)
+            bsel = blocks[t0 // BLOCK : t1 // BLOCK]
+            if f4:
+                kb = torch.randint(0, 256, (t1 - t0, D_IDX // 2), generator=gen, device=device, dtype=torch.int32)
+                ke = torch.randint(125, 129, (t1 - t0, D_IDX // 32), generator=gen, device=device, dtype=torch.int32)
+                key_fp4[bsel] = kb.to(torch.uint8).reshape(-1, BLOCK, D_IDX // 2)
+                key_e8m0[bsel] = ke.to(torch.uint8).reshape(-1, BLOCK, D_IDX // 32)
+            else:
+                k = torch.randn((t1 - t0, D_IDX), generator=gen, device=device)
+                if plant_frac > 0:
+                    k += plant_sigma * mask_d[t0:t1, None].float() * u[None, :]
+                kc, ks = quantize_e4m3_rows(k)
+                key_fp8[bsel] = kc.reshape(-1, BLOCK, D_IDX)
+                key_scale[bsel] = ks.reshape(-1, BLOCK)
             c = torch.randn((t1 - t0, D_LAT), generator=gen, device=device)
             cc, cs = quantize_e4m3_rows(c)
-            bsel = blocks[t0 // BLOCK : t1 // BLOCK]
-            key_fp8[bsel] = kc.reshape(-1, BLOCK, D_IDX)
-            key_scale[bsel] = ks.reshape(-1, BLOCK)
             lat_fp8[bsel] = cc.reshape(-1, BLOCK, D_LAT)
             lat_scale[bsel] = cs.reshape(-1, BLOCK)
 
@@ -214,6 +238,9 @@ def make_case(
         sm_scale=1.0 / math.sqrt(D_LAT),
         topk=topk,
         planted=planted,
+        key_format=key_format,
+        key_fp4=key_fp4,
+        key_e8m0=key_e8m0,
     )
 
 
@@ -225,6 +252,7 @@ WORKLOADS = {
     "decode_16x4_ragged_128k_256k": dict(B=16, R=4, lengths=None, seed=20260003, permute_blocks=True),
     "decode_16x8_32k": dict(B=16, R=8, lengths=[32768] * 16, seed=20260006),
     "decode_4x4_1m_planted": dict(B=4, R=4, lengths=[1 << 20] * 4, seed=20260004, plant_frac=0.01),
+    "decode_4x4_1m_mxfp4": dict(B=4, R=4, lengths=[1 << 20] * 4, seed=20260007, key_format="mxfp4"),
     "prefill_4096_on_128k": dict(B=1, R=4096, lengths=[131072 + 4096], seed=20260005, fp8_query=True),
 }
 
