@@ -96,7 +96,7 @@ def cpu_baseline(workload_name, budget_s):
 
     cfg = case_config(workload_name)
     R, lens = cfg["R"], cfg["lengths"]
-    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query")}
+    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query", "key_format")}
     if R > 64:  # prefill chunk: one request, sample its query rows
         case = make_case(1, R, lens[:1], seed=cfg["seed"] + 1000, **kw)
         rows, spent = 0, 0.0
@@ -168,12 +168,13 @@ def run_decode(args, torch, dsa, traffic, cfg):
     B, R, lens = cfg["B"], cfg["R"], cfg["lengths"]
     k = 2048
     rows = B * R
-    step_bytes = traffic.decode_step_bytes(lens, R, k)
-    set_bytes = sum(lens) * (traffic.KEY_BYTES + traffic.LAT_ROW_BYTES)
+    kfmt = cfg.get("key_format", "fp8")
+    step_bytes = traffic.decode_step_bytes(lens, R, k, kfmt)
+    set_bytes = sum(lens) * (traffic.key_bytes(kfmt) + traffic.LAT_ROW_BYTES)
     nsets = args.sets or max(2, math.ceil(3 * MALL_BYTES / min(step_bytes, set_bytes)))
     nsets = min(nsets, max(2, int(40e9 // set_bytes)))
 
-    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query")}
+    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query", "key_format")}
     cases = [make_case(B, R, lens, seed=cfg["seed"] + 100 * i, device="cuda", name=args.workload, **kw)
              for i in range(nsets)]
     batches = [dsa.Batch.of(c) for c in cases]
@@ -246,7 +247,7 @@ def run_decode(args, torch, dsa, traffic, cfg):
 
     # ---- dominant kernel: the indexer scorer (its share of the step grows with context)
     score_us = kernel_time(torch, score, nsets)
-    dom_bytes = traffic.scorer_bytes(lens, R)
+    dom_bytes = traffic.scorer_bytes(lens, R, kfmt)
     achieved = dom_bytes / (score_us * 1e-6) / 1e9
 
     tokens = sum(lens)
@@ -270,7 +271,8 @@ def run_decode(args, torch, dsa, traffic, cfg):
             "rows_per_request": R,
             "context": lens[0] if len(set(lens)) == 1 else [min(lens), max(lens)],
             "topk": k,
-            "indexer": "32h x 128d, E4M3 keys + fp32 scale",
+            "indexer": ("32h x 128d, MXFP4 keys (E2M1 + E8M0 per 32 dims, 68 B)" if kfmt == "mxfp4"
+                        else "32h x 128d, E4M3 keys + fp32 scale"),
             "mla": "16h x 576 latent (E4M3 + fp32 scale) -> 512",
             "input_sets_rotated": nsets,
             "launch": "eager" if graph is None else "hip graph",
@@ -300,7 +302,7 @@ def run_prefill(args, torch, dsa, traffic, cfg):
 
     R, L = cfg["R"], cfg["lengths"][0]
     k = 2048
-    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query")}
+    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query", "key_format")}
     case = make_case(1, R, [L], seed=cfg["seed"], device="cuda", name=args.workload, **kw)
     batch, cache = dsa.Batch.of(case), dsa.Cache.of(case)
     ld = (L + 63) // 64 * 64

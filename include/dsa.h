@@ -46,6 +46,9 @@ typedef enum {
 
 enum { DSA_Q_BF16 = 0, DSA_Q_FP8 = 1 };
 
+/* Index-key formats of a cache (dsa_cache.key_format). */
+enum { DSA_KEY_FP8 = 0, DSA_KEY_MXFP4 = 1 };
+
 /* Workspace kinds for dsa_workspace_size(). */
 enum { DSA_WS_TOPK = 1, DSA_WS_MLA_DECODE = 2, DSA_WS_MLA_PREFILL = 3, DSA_WS_DECODE = 4 };
 
@@ -68,6 +71,17 @@ enum { DSA_WS_TOPK = 1, DSA_WS_MLA_DECODE = 2, DSA_WS_MLA_PREFILL = 3, DSA_WS_DE
  *   lat_scale [num_blocks][64]      fp32 per-token latent scale
  * A key or latent dequantises as code value * scale. Planes must be 16-byte
  * aligned.
+ *
+ * With key_format DSA_KEY_MXFP4 the index keys are MXFP4 instead, 68 B per
+ * token ("vLLM Day-0 Support for Kimi K3.1 Pro", section "Native MXFP4
+ * indexer": 68 bytes including scales in place of 132; "Inside vLLM's
+ * hybrid KV cache" lists both widths), and key_fp8 / key_scale are unused:
+ *   key_fp4   [num_blocks][64][64] E2M1 codes, two per byte: dim 2i in the
+ *             low nibble of byte i, dim 2i + 1 in the high nibble
+ *   key_e8m0  [num_blocks][64][4]  E8M0 scale of dims 32j .. 32j + 31
+ * A key dim dequantises as E2M1(code) * 2^(scale - 127) (OCP MX: blocks of
+ * 32 values sharing one power-of-two scale). Scale byte 255 (NaN) is not
+ * supported.
  */
 typedef struct {
   const uint8_t* key_fp8;
@@ -76,6 +90,9 @@ typedef struct {
   const float* lat_scale;
   int32_t num_blocks;
   int32_t block_size; /* must be 64 */
+  int32_t key_format; /* DSA_KEY_FP8 (0, the default) or DSA_KEY_MXFP4 */
+  const uint8_t* key_fp4;
+  const uint8_t* key_e8m0;
 } dsa_cache;
 
 /*
@@ -123,7 +140,8 @@ int32_t dsa_index_key_write(const dsa_batch* batch, const void* k, const float* 
 /*
  * Score: the lightning indexer. For every row and every token s the row sees,
  *   scores[row * ld + s] = sum_h w[row][h] * ReLU(q[row][h] . khat_s)
- * with khat_s = key_fp8[s] * key_scale[s] and q[row][h] the row's query for
+ * with khat_s the dequantised key of token s (FP8: key_fp8[s] * key_scale[s];
+ * MXFP4: each dim's E2M1 value times its block's power of two) and q[row][h] the row's query for
  * head h (DeepSeek-V3.2 form, to which "vLLM Day-0 Support for Kimi K3.1
  * Pro", section "What Kimi K3.1 Pro changes", points; 32 heads x 128 dims,
  * 132-byte FP8 keys). Each key is read once for all rows of its request
@@ -136,8 +154,8 @@ int32_t dsa_index_key_write(const dsa_batch* batch, const void* k, const float* 
  *   w        bf16 [rows][32] head weights (any sign).
  *   scores   fp32 [rows][ld], ld >= max_ctx. Entries s > position(row) are not
  *            written.
- * Accumulation is fp32; products of bf16 or E4M3 query values with E4M3 key
- * values are exact.
+ * Accumulation is fp32; products of bf16 or E4M3 query values with E4M3 or
+ * E2M1 key values are exact.
  */
 int32_t dsa_index_score(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t q_dtype,
                         const float* q_scale, const void* w, float* scores, int64_t ld, void* stream);

@@ -84,31 +84,53 @@ def _check(status: int, what: str):
         raise DsaError(status, what, detail)
 
 
+DSA_KEY_FP8 = 0
+DSA_KEY_MXFP4 = 1
+
+
 class Cache:
     """Paged cache planes (device tensors): key_fp8 u8 [nb,64,128], key_scale f32 [nb,64],
-    lat_fp8 u8 [nb,64,576], lat_scale f32 [nb,64]."""
+    lat_fp8 u8 [nb,64,576], lat_scale f32 [nb,64]; or, for MXFP4 index keys,
+    key_fp4 u8 [nb,64,64] (E2M1 pairs, even dim in the low nibble) and
+    key_e8m0 u8 [nb,64,4] in place of key_fp8 / key_scale."""
 
-    def __init__(self, key_fp8, key_scale, lat_fp8, lat_scale):
+    def __init__(self, key_fp8, key_scale, lat_fp8, lat_scale, key_fp4=None, key_e8m0=None):
+        if key_fp8 is not None and key_fp4 is not None:
+            raise ValueError("give FP8 or MXFP4 key planes, not both")
+        nb = None
         if key_fp8 is not None:
             _need(key_fp8, "key_fp8", _CODES)
             nb = key_fp8.shape[0]
             if tuple(key_fp8.shape[1:]) != (64, 128):
                 raise ValueError("key_fp8 must be [num_blocks, 64, 128]")
             _need(key_scale, "key_scale", _F32, nb * 64)
+        if key_fp4 is not None:
+            _need(key_fp4, "key_fp4", _CODES)
+            nb = key_fp4.shape[0]
+            if tuple(key_fp4.shape[1:]) != (64, 64):
+                raise ValueError("key_fp4 must be [num_blocks, 64, 64]")
+            _need(key_e8m0, "key_e8m0", _CODES, nb * 64 * 4)
         if lat_fp8 is not None:
             _need(lat_fp8, "lat_fp8", _CODES)
             if tuple(lat_fp8.shape[1:]) != (64, 576):
                 raise ValueError("lat_fp8 must be [num_blocks, 64, 576]")
             _need(lat_scale, "lat_scale", _F32, lat_fp8.shape[0] * 64)
+            if nb is not None and lat_fp8.shape[0] != nb:
+                raise ValueError("key and latent planes must have the same number of blocks")
         self.key_fp8, self.key_scale, self.lat_fp8, self.lat_scale = key_fp8, key_scale, lat_fp8, lat_scale
-        nb = key_fp8.shape[0] if key_fp8 is not None else lat_fp8.shape[0]
+        self.key_fp4, self.key_e8m0 = key_fp4, key_e8m0
+        if nb is None:
+            nb = lat_fp8.shape[0]
+        fmt = DSA_KEY_MXFP4 if key_fp4 is not None else DSA_KEY_FP8
         self.c = _lib.DsaCacheC(
-            _ptr(key_fp8), _ptr(key_scale), _ptr(lat_fp8), _ptr(lat_scale), int(nb), 64
+            _ptr(key_fp8), _ptr(key_scale), _ptr(lat_fp8), _ptr(lat_scale), int(nb), 64, fmt, _ptr(key_fp4),
+            _ptr(key_e8m0)
         )
 
     @classmethod
     def of(cls, case) -> "Cache":
-        return cls(case.key_fp8, case.key_scale, case.lat_fp8, case.lat_scale)
+        return cls(case.key_fp8, case.key_scale, case.lat_fp8, case.lat_scale,
+                   getattr(case, "key_fp4", None), getattr(case, "key_e8m0", None))
 
 
 class Batch:

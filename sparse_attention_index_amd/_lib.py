@@ -42,6 +42,9 @@ class DsaCacheC(ctypes.Structure):
         ("lat_scale", ctypes.c_void_p),
         ("num_blocks", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
+        ("key_format", ctypes.c_int32),
+        ("key_fp4", ctypes.c_void_p),
+        ("key_e8m0", ctypes.c_void_p),
     ]
 
 

@@ -45,13 +45,31 @@ int32_t check_batch(const dsa_batch* b) {
   return DSA_OK;
 }
 
+// The scorer's key planes for the cache's key format.
+void set_keys(ScoreArgs& a, const dsa_cache* c) {
+  const bool f4 = c->key_format == DSA_KEY_MXFP4;
+  a.key_fp8 = f4 ? nullptr : c->key_fp8;
+  a.key_scale = f4 ? nullptr : c->key_scale;
+  a.key_fp4 = f4 ? c->key_fp4 : nullptr;
+  a.key_e8m0 = f4 ? c->key_e8m0 : nullptr;
+}
+
 int32_t check_cache(const dsa_cache* c, bool keys, bool lat) {
   if (!c) return fail(DSA_ERR_INVALID_ARG, "cache is null");
   if (c->block_size != DSA_BLOCK) return fail(DSA_ERR_UNSUPPORTED, "block_size must be 64");
   if (c->num_blocks < 1) return fail(DSA_ERR_INVALID_ARG, "num_blocks must be >= 1");
-  if (keys && (!c->key_fp8 || !c->key_scale)) return fail(DSA_ERR_INVALID_ARG, "key planes are null");
+  if (keys && c->key_format != DSA_KEY_FP8 && c->key_format != DSA_KEY_MXFP4)
+    return fail(DSA_ERR_UNSUPPORTED, "key_format must be DSA_KEY_FP8 or DSA_KEY_MXFP4");
+  if (keys && c->key_format == DSA_KEY_MXFP4) {
+    if (!c->key_fp4 || !c->key_e8m0) return fail(DSA_ERR_INVALID_ARG, "MXFP4 key planes are null");
+    if (!aligned(c->key_fp4, 16) || !aligned(c->key_e8m0, 4))
+      return fail(DSA_ERR_INVALID_ARG, "key_fp4 must be 16-byte and key_e8m0 4-byte aligned");
+  }
+  if (keys && c->key_format == DSA_KEY_FP8 && (!c->key_fp8 || !c->key_scale))
+    return fail(DSA_ERR_INVALID_ARG, "key planes are null");
   if (lat && (!c->lat_fp8 || !c->lat_scale)) return fail(DSA_ERR_INVALID_ARG, "latent planes are null");
-  if (keys && !aligned(c->key_fp8, 16)) return fail(DSA_ERR_INVALID_ARG, "key_fp8 must be 16-byte aligned");
+  if (keys && c->key_format == DSA_KEY_FP8 && !aligned(c->key_fp8, 16))
+    return fail(DSA_ERR_INVALID_ARG, "key_fp8 must be 16-byte aligned");
   if (lat && !aligned(c->lat_fp8, 16)) return fail(DSA_ERR_INVALID_ARG, "lat_fp8 must be 16-byte aligned");
   return DSA_OK;
 }
@@ -153,8 +171,7 @@ int32_t dsa_index_score(const dsa_batch* batch, const dsa_cache* cache, const vo
   a.q = q;
   a.q_scale = q_scale;
   a.w = static_cast<const uint16_t*>(w);
-  a.key_fp8 = cache->key_fp8;
-  a.key_scale = cache->key_scale;
+  set_keys(a, cache);
   a.ctx_len = batch->ctx_len;
   a.block_table = batch->block_table;
   a.max_blocks = batch->max_blocks;
@@ -256,8 +273,7 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
   a.q = q_idx;
   a.q_scale = nullptr;
   a.w = static_cast<const uint16_t*>(w);
-  a.key_fp8 = cache->key_fp8;
-  a.key_scale = cache->key_scale;
+  set_keys(a, cache);
   a.ctx_len = batch->ctx_len;
   a.block_table = batch->block_table;
   a.max_blocks = batch->max_blocks;

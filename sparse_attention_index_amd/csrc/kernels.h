@@ -11,8 +11,10 @@ struct ScoreArgs {
   const void* q;            // bf16 [rows][32][128] or E4M3 [rows][32][128]
   const float* q_scale;     // fp32 [rows] (E4M3 queries) or null
   const uint16_t* w;        // bf16 [rows][32]
-  const uint8_t* key_fp8;   // [num_blocks][64][128]
+  const uint8_t* key_fp8;   // [num_blocks][64][128] E4M3, or null with MXFP4 keys
   const float* key_scale;   // [num_blocks][64]
+  const uint8_t* key_fp4 = nullptr;   // MXFP4 keys: [num_blocks][64][64] E2M1 pairs (even dim low nibble)
+  const uint8_t* key_e8m0 = nullptr;  // MXFP4 keys: [num_blocks][64][4] E8M0 scale of dims 32j .. 32j+31
   const int32_t* ctx_len;   // [B]
   const int32_t* block_table;  // [B][max_blocks]
   int32_t max_blocks;

@@ -60,6 +60,8 @@
 namespace dsa {
 
 static constexpr int kKeyBytes = kBlock * kIdxDim;  // one page of keys, 8 KB
+static constexpr int kF4KeyBytes = kBlock * kIdxDim / 2;  // one page of MXFP4 keys, 4 KB
+static constexpr int kF4Copies = kF4KeyBytes / 1024 + 1;  // 4 key copies + 1 scale copy
 static constexpr int kRing = 4;                     // LDS page slots per workgroup
 static constexpr int kMaxWgPages = 2048;            // pages one workgroup walks at most
 static constexpr int kThreads = 256;                // 4 waves
@@ -102,22 +104,43 @@ DSA_DEV uint32_t e4m3x2_from_f32(float a, float b) {
 // The E4M3 A operands of one query row: q * 2^e = hi + lo (bf16 queries) or
 // the query codes as they are; returns the factor 2^-e (or the row scale)
 // that multiplies the head's dot products.
-template <bool QFP8>
+//
+// K order. With FP8 keys, byte i of lane half g's operand for step s is dim
+// 64g + 32s + i. With MXFP4 keys the FP4 B operand of lane half g holds K
+// indices 16g + [0, 16) in its first 16 nibbles and 32 + 16g + [0, 16) in
+// the next 16 (measured on gfx950), and its one E8M0 scale covers all 32;
+// so that those 32 values are one MX block (dims 64g + 32s + [0, 32), read
+// as 16 contiguous bytes), the query's byte i of lane half g, step s, must
+// be dim 32s + 16g + i (i < 16) or 64 + 32s + 16g + i - 16 (i >= 16).
+template <bool QFP8, bool KF4>
 DSA_DEV float load_query(const ScoreArgs& a, size_t row, int n, int g, i32x8 (&A)[QFP8 ? 1 : 2][2]) {
   if constexpr (QFP8) {
-    const i32x8* qp = reinterpret_cast<const i32x8*>(reinterpret_cast<const uint8_t*>(a.q) +
-                                                     (row * kIdxHeads + n) * kIdxDim + 64 * g);
-    A[0][0] = qp[0];
-    A[0][1] = qp[1];
+    const uint8_t* q8 = reinterpret_cast<const uint8_t*>(a.q) + (row * kIdxHeads + n) * kIdxDim;
+    if constexpr (KF4) {
+      const u32x4 p0 = *reinterpret_cast<const u32x4*>(q8 + 16 * g);       // dims 16g + [0, 16)
+      const u32x4 p1 = *reinterpret_cast<const u32x4*>(q8 + 32 + 16 * g);  // 32 + 16g
+      const u32x4 p2 = *reinterpret_cast<const u32x4*>(q8 + 64 + 16 * g);  // 64 + 16g
+      const u32x4 p3 = *reinterpret_cast<const u32x4*>(q8 + 96 + 16 * g);  // 96 + 16g
+      A[0][0] = i32x8{(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3], (int)p2[0], (int)p2[1], (int)p2[2], (int)p2[3]};
+      A[0][1] = i32x8{(int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3], (int)p3[0], (int)p3[1], (int)p3[2], (int)p3[3]};
+    } else {
+      const i32x8* qp = reinterpret_cast<const i32x8*>(q8 + 64 * g);
+      A[0][0] = qp[0];
+      A[0][1] = qp[1];
+    }
     return a.q_scale[row];
   } else {
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) +
-                                                       (row * kIdxHeads + n) * kIdxDim + 64 * g);
+                                                       (row * kIdxHeads + n) * kIdxDim);
+    // x[32s + i]: the value at byte i of step s
     float x[64];
     float amax = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const bf16x8 v = qp[c];
+      // piece c of 8 values: FP8 keys: dims 64g + 8c; MXFP4 keys: dims
+      // 16g + 32u + 8(c & 1) for u = 0, 2, 1, 3 (c >> 1 = 0..3)
+      const int u = (c >> 1) == 1 ? 2 : ((c >> 1) == 2 ? 1 : (c >> 1));
+      const bf16x8 v = KF4 ? qp[(16 * g + 32 * u) / 8 + (c & 1)] : qp[8 * g + c];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[8 * c + e] = (float)v[e];
@@ -157,13 +180,14 @@ DSA_DEV float load_query(const ScoreArgs& a, size_t row, int n, int g, i32x8 (&A
 // LDS; waves 0-2 also move the pages into LDS, wave 3 stores the scores.
 enum WaveRole { kCopier, kFlusher };
 
-template <int RPW, bool QFP8>
+template <int RPW, bool QFP8, bool KF4>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void score_kernel(ScoreArgs a) {
   constexpr int ROWS = 4 * RPW;
   constexpr int NT = QFP8 ? 1 : 2;  // E4M3 terms per query value
   constexpr int LAG = 2;             // a page's scores are complete two barriers later
-  __shared__ __attribute__((aligned(16))) uint8_t key_s[kRing][kKeyBytes];
-  __shared__ __attribute__((aligned(16))) float ks_s[kRing][kBlock];
+  constexpr int PAGE = KF4 ? kF4KeyBytes : kKeyBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t key_s[kRing][PAGE];
+  __shared__ __attribute__((aligned(16))) float ks_s[kRing][kBlock];  // fp32 scales, or 4 E8M0 per key
   __shared__ int32_t tbl_s[kMaxWgPages];
   __shared__ __attribute__((aligned(16))) float w_s[ROWS][kIdxHeads];
   __shared__ float sc_s[LAG + 1][ROWS][kBlock];  // scores of the group's rows, by page
@@ -197,7 +221,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int rr = 0; rr < RPW; ++rr) {
     const int gr = min(wr0 + rr, nr - 1);  // clamp: rows past the group reuse a valid row, never written
     const size_t row = row0 + gr;
-    const float head_scale = load_query<QFP8>(a, row, n, g, A[rr]);
+    const float head_scale = load_query<QFP8, KF4>(a, row, n, g, A[rr]);
     // head weights with the head's scale folded in: w_s[row][head]
     if (g == 0) {
       const float wv = __uint_as_float((uint32_t)a.w[row * kIdxHeads + n] << 16);
@@ -225,9 +249,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // layout: lane l fetches the global chunk that belongs at LDS chunk 64j + l.
   // The last copy moves the page's 64 scales. Wave w issues copies
   // w*kCopiesPerWave .. w*kCopiesPerWave + kCopiesPerWave - 1.
+  // MXFP4 pages: 4 copies of 1 KB (16-byte chunks of 64-byte key rows,
+  // chunk c of key r at position c ^ ((r >> 2) & 3)) and one of the 64 keys'
+  // E8M0 words; waves 0 and 1 issue two key copies each, wave 2 the scales.
   auto issue = [&](int i) {
     const int slot = i % kRing;
     const size_t page = (size_t)tbl_s[i];
+    if constexpr (KF4) {
+      const uint8_t* pg = a.key_fp4 + page * kF4KeyBytes;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * wave + jj;  // wave-uniform
+        if (j < kF4Copies - 1) {
+          const int c = 64 * j + lane;
+          const int key = c >> 2;
+          copy16_to_lds(pg + key * (kIdxDim / 2) + (((c & 3) ^ ((key >> 2) & 3)) << 4), key_s[slot] + 1024 * j);
+        } else if (j == kF4Copies - 1) {
+          copy4_to_lds(a.key_e8m0 + (page * kBlock + lane) * 4, ks_s[slot]);
+        }
+      }
+      return;
+    }
     const uint8_t* pg = a.key_fp8 + page * kKeyBytes;
 #pragma unroll
     for (int jj = 0; jj < kCopiesPerWave; ++jj) {
@@ -282,7 +324,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_s[i % (LAG + 1)][gr][lane]), row_rsrc(gr), off, 0,
                                               0);
     };
-    auto mfma_unit = [&](f32x16(&acc)[G], const i32x8(&Bh)[2], int gi) {
+    auto mfma_unit = [&](f32x16(&acc)[G], const i32x8(&Bh)[2], const int (&sb)[2], int gi) {
 #pragma unroll
       for (int r = 0; r < G; ++r) {
         acc[r] = f32x16{};
@@ -290,18 +332,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int s = 0; s < 2; ++s)
-            acc[r] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[gi * G + r][t][s], Bh[s], acc[r], 0, 0, 0,
-                                                                     127, 0, 127);
+            acc[r] = KF4 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[gi * G + r][t][s], Bh[s], acc[r], 0, 4,
+                                                                          0, 127, 0, sb[s])
+                         : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[gi * G + r][t][s], Bh[s], acc[r], 0, 0,
+                                                                          0, 127, 0, 127);
       }
     };
-    auto load_b = [&](const uint8_t* kbuf, int h, i32x8(&Bh)[2]) {
+    // B operands of keys 32h .. 32h+31 of a staged page. MXFP4: lane half
+    // g, step s reads the 16-byte chunk 2g + s of its key (one MX block) and
+    // that block's E8M0 scale (sb).
+    auto load_b = [&](const uint8_t* kbuf, const float* ksb, int h, i32x8(&Bh)[2], int (&sb)[2]) {
       const int key = 32 * h + n;
+      if constexpr (KF4) {
+        const uint32_t sw = __float_as_uint(ksb[key]);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s));
-        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s + 1));
-        Bh[s] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                      (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+        for (int s = 0; s < 2; ++s) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(kbuf + key * (kIdxDim / 2) +
+                                                          (((2 * g + s) ^ ((key >> 2) & 3)) << 4));
+          Bh[s] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+          sb[s] = (int)((sw >> (8 * (2 * g + s))) & 0xffu);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s));
+          const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kbuf + key_chunk_off(key, 4 * g + 2 * s + 1));
+          Bh[s] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                        (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+          sb[s] = 127;
+        }
       }
     };
     // kRing - 1 pages are in flight. A copier's only vector-memory
@@ -309,8 +368,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // its copies of the pages after page i.
     auto wait_page = [&](int i) {
       if constexpr (role == kCopier) {
-        if (i + kRing - 2 < n_my) wait_vmcnt<kCopiesPerWave * (kRing - 2)>();
-        else wait_vmcnt<0>();
+        if (i + kRing - 2 < n_my) {
+          if constexpr (KF4) {
+            if (wave < 2) wait_vmcnt<2 * (kRing - 2)>();
+            else wait_vmcnt<kRing - 2>();
+          } else {
+            wait_vmcnt<kCopiesPerWave * (kRing - 2)>();
+          }
+        } else {
+          wait_vmcnt<0>();
+        }
       }
     };
     if constexpr (role == kCopier) {
@@ -340,16 +407,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       // keys of both halves up front for one group per half; with two
       // groups the second half's keys are read when its first unit starts
       i32x8 B[NG == 1 ? 2 : 1][2];
-      load_b(kbuf, 0, B[0]);
-      if constexpr (NG == 1) load_b(kbuf, 1, B[NG == 1 ? 1 : 0]);
-      const float ks[2] = {ksb[n], ksb[32 + n]};
+      int SB[NG == 1 ? 2 : 1][2];
+      load_b(kbuf, ksb, 0, B[0], SB[0]);
+      if constexpr (NG == 1) load_b(kbuf, ksb, 1, B[NG == 1 ? 1 : 0], SB[NG == 1 ? 1 : 0]);
+      // MXFP4 keys carry their scales inside the dot products (E8M0 per block)
+      const float ks[2] = {KF4 ? 1.f : ksb[n], KF4 ? 1.f : ksb[32 + n]};
 #pragma unroll
       for (int u = 0; u < 2 * NG; ++u) {  // unit u: half u / NG, group u % NG
         const int h = u / NG, gi = u % NG;
         if constexpr (NG > 1) {
-          if (u == NG) load_b(kbuf, 1, B[0]);
+          if (u == NG) load_b(kbuf, ksb, 1, B[0], SB[0]);
         }
-        mfma_unit(acc[u & 1], B[NG == 1 ? h : 0], gi);
+        mfma_unit(acc[u & 1], B[NG == 1 ? h : 0], SB[NG == 1 ? h : 0], gi);
         if (u == 0) epilogue(acc[1], ks_prev, i - 1, 1, NG - 1);  // last unit of the previous page
         else epilogue(acc[(u - 1) & 1], ks[(u - 1) / NG], i, (u - 1) / NG, (u - 1) % NG);
       }
@@ -367,11 +436,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
 // Workgroups of a variant that fit one CU at once (registers, LDS), from
 // the runtime's occupancy calculator; computed once per variant.
-template <int RPW, bool QFP8>
+template <int RPW, bool QFP8, bool KF4>
 static int resident_per_cu() {
   static const int n = [] {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, score_kernel<RPW, QFP8>, kThreads, 0) != hipSuccess || v < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, score_kernel<RPW, QFP8, KF4>, kThreads, 0) != hipSuccess ||
+        v < 1)
       v = 1;
     return v;
   }();
@@ -390,34 +460,40 @@ static int cu_count() {
   return n;
 }
 
-template <int RPW, bool QFP8>
+template <int RPW, bool QFP8, bool KF4>
 static void launch_variant(const ScoreArgs& a, int B, int max_ctx, hipStream_t st) {
   const int groups = (a.R + 4 * RPW - 1) / (4 * RPW);
   const int max_blk = (max_ctx + kBlock - 1) / kBlock;
   // One round of resident workgroups over the whole grid, at least 2 pages
   // each, and no workgroup past kMaxWgPages.
-  const long long slots = (long long)resident_per_cu<RPW, QFP8>() * cu_count();
+  const long long slots = (long long)resident_per_cu<RPW, QFP8, KF4>() * cu_count();
   long long per_req = (slots + (long long)B * groups - 1) / ((long long)B * groups);
   const long long cap = (max_blk + 1) / 2;
   if (per_req > cap) per_req = cap;
   if (per_req < 1) per_req = 1;
   const long long need = (max_blk + kMaxWgPages - 1) / kMaxWgPages;
   if (per_req < need) per_req = need;
-  hipLaunchKernelGGL((score_kernel<RPW, QFP8>), dim3((unsigned)per_req, B, groups), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((score_kernel<RPW, QFP8, KF4>), dim3((unsigned)per_req, B, groups), dim3(kThreads), 0, st, a);
 }
 
-hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st) {
+template <bool KF4>
+static void launch_format(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st) {
   // Rows per wave: one for decode-sized requests; more when a request brings
   // many FP8 query rows (prefill chunks), so that more rows share each page.
   if (q_fp8) {
-    if (a.R > 16) launch_variant<4, true>(a, B, max_ctx, st);
-    else if (a.R > 4) launch_variant<2, true>(a, B, max_ctx, st);
-    else launch_variant<1, true>(a, B, max_ctx, st);
+    if (a.R > 16) launch_variant<4, true, KF4>(a, B, max_ctx, st);
+    else if (a.R > 4) launch_variant<2, true, KF4>(a, B, max_ctx, st);
+    else launch_variant<1, true, KF4>(a, B, max_ctx, st);
   } else {
     // up to 8 verification rows read each page once
-    if (a.R > 4) launch_variant<2, false>(a, B, max_ctx, st);
-    else launch_variant<1, false>(a, B, max_ctx, st);
+    if (a.R > 4) launch_variant<2, false, KF4>(a, B, max_ctx, st);
+    else launch_variant<1, false, KF4>(a, B, max_ctx, st);
   }
+}
+
+hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st) {
+  if (a.key_fp4) launch_format<true>(a, B, max_ctx, q_fp8, st);
+  else launch_format<false>(a, B, max_ctx, q_fp8, st);
   return hipGetLastError();
 }
 

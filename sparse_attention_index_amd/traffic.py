@@ -1,7 +1,8 @@
 """Algorithmic HBM bytes of the DSA decode step and of each kernel (for rooflines).
 
 Per request, every context token's 132-byte index key (128 E4M3 values + fp32
-scale) is read once for all of its rows. Per query row: the 2,048 selected
+scale; 68 bytes as MXFP4: 64 bytes of E2M1 pairs + 4 E8M0 block scales) is
+read once for all of its rows. Per query row: the 2,048 selected
 latent rows (576 E4M3 values + fp32 scale = 580 bytes) and the fp32 score of
 every visible token, written by the scorer and read by the selection (the
 pages count this round trip too: "TokenSpeed Kimi K3.1", section "Sparse
@@ -13,6 +14,7 @@ where a kernel moves them.
 from __future__ import annotations
 
 KEY_BYTES = 132
+KEY_BYTES_MXFP4 = 68
 LAT_ROW_BYTES = 580
 SCORE_BYTES = 4
 Q_IDX_BYTES = 32 * 128 * 2 + 32 * 2  # bf16 indexer query + bf16 head weights per row
@@ -25,9 +27,13 @@ def visible(ctx_lens, R):
     return [L - R + r + 1 for L in ctx_lens for r in range(R)]
 
 
-def scorer_bytes(ctx_lens, R):
+def key_bytes(key_format="fp8"):
+    return KEY_BYTES_MXFP4 if key_format == "mxfp4" else KEY_BYTES
+
+
+def scorer_bytes(ctx_lens, R, key_format="fp8"):
     vis = visible(ctx_lens, R)
-    return sum(ctx_lens) * KEY_BYTES + SCORE_BYTES * sum(vis) + len(vis) * Q_IDX_BYTES
+    return sum(ctx_lens) * key_bytes(key_format) + SCORE_BYTES * sum(vis) + len(vis) * Q_IDX_BYTES
 
 
 def topk_bytes(ctx_lens, R, k):
@@ -40,10 +46,10 @@ def mla_bytes(ctx_lens, R, k):
     return sum(min(k, v) * (LAT_ROW_BYTES + 4) for v in vis) + len(vis) * (Q_MLA_BYTES + OUT_BYTES)
 
 
-def decode_step_bytes(ctx_lens, R, k):
+def decode_step_bytes(ctx_lens, R, k, key_format="fp8"):
     """Keys once per request + per row: selected latents and the score round trip."""
     vis = visible(ctx_lens, R)
-    return sum(ctx_lens) * KEY_BYTES + sum(min(k, v) * LAT_ROW_BYTES + 2 * SCORE_BYTES * v for v in vis)
+    return sum(ctx_lens) * key_bytes(key_format) + sum(min(k, v) * LAT_ROW_BYTES + 2 * SCORE_BYTES * v for v in vis)
 
 
 def scorer_flops(ctx_lens, R, heads=32, dim=128):

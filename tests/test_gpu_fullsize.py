@@ -27,12 +27,12 @@ from workloads import case_config, make_case
 pytestmark = pytest.mark.gpu
 
 DECODE = ["decode_1x1_8k", "decode_16x4_32k", "decode_16x8_32k", "decode_16x4_ragged_128k_256k",
-          "decode_4x4_1m_planted"]
+          "decode_4x4_1m_planted", "decode_4x4_1m_mxfp4"]
 
 
 def _make(name):
     cfg = case_config(name)
-    kw = {k: v for k, v in cfg.items() if k in ("permute_blocks", "plant_frac", "fp8_query")}
+    kw = {k: v for k, v in cfg.items() if k in ("permute_blocks", "plant_frac", "fp8_query", "key_format")}
     print(f"\n[fullsize] {name} B={cfg['B']} R={cfg['R']} lengths[0:4]={cfg['lengths'][:4]}", flush=True)
     return make_case(cfg["B"], cfg["R"], cfg["lengths"], seed=cfg["seed"], device="cuda", name=name, **kw)
 
