@@ -38,6 +38,7 @@ from .dsa import (  # noqa: F401
 )
 from .traffic import dsa_bytes, dense_mla_bytes, counted_bytes  # noqa: F401
 from .mxfp4 import e2m1_table, mxfp4_decode, mxfp4_encode  # noqa: F401
+from .dcp import dcp_select, local_topk, lse_combine, shard_attend  # noqa: F401
 from .key_write import (  # noqa: F401
     e4m3_encode,
     index_key_write,
