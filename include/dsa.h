@@ -51,6 +51,8 @@ enum { DSA_KEY_FP8 = 0, DSA_KEY_MXFP4 = 1 };
 
 /* Workspace kinds for dsa_workspace_size(). */
 enum { DSA_WS_TOPK = 1, DSA_WS_MLA_DECODE = 2, DSA_WS_MLA_PREFILL = 3, DSA_WS_DECODE = 4 };
+/* Workspace kinds for dsa_dcp_workspace_size(). */
+enum { DSA_WS_DCP_TOPK = 5, DSA_WS_DCP_MLA = 6 };
 
 #define DSA_BLOCK 64        /* tokens per cache page */
 #define DSA_IDX_HEADS 32    /* indexer heads */
@@ -219,6 +221,53 @@ int32_t dsa_sparse_mla_prefill(const dsa_batch* batch, const dsa_cache* cache, c
 int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
                    const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale, void* out,
                    float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Decode context parallelism, simulated on one device. Under DCP, token p of
+ * a request lives on shard p mod W of W devices; each shard scores and ranks
+ * only its own tokens, the shards merge their candidates exactly, attend to
+ * the winners they own, and combine the partial outputs by log-sum-exp
+ * ("SGLang Day-0 Support for Kimi K3.1 Pro", section "Decode: DSA with decode
+ * context parallelism"; "vLLM Day-0 Support for Kimi K3.1 Pro", section "An
+ * exact top-k merge with about 10x less traffic"; "TokenSpeed Kimi K3.1",
+ * section "Sharding long contexts with decode context parallelism"). Here the
+ * W shards are regions of one device's memory: these calls reproduce the
+ * protocol's results, not its communication.
+ *
+ * dsa_dcp_topk: per row, each shard's top-k and best C candidates; the
+ * cutoff is the k-th best of all W * C candidates; a shard whose C
+ * candidates all rank above the cutoff adds its whole top-k; the k best of
+ * that pool are written to idx. Ranking is dsa_topk's (score, then lower
+ * position), so idx holds exactly dsa_topk's set.
+ *   scores, ld, row_len, rows, k, idx  as for dsa_topk.
+ *   W        shards, 2 <= W <= 64, rows * W <= 65535; C candidates per
+ *            shard, 1 <= C <= k (the
+ *            pages use C = 1.5 k / W: 384 for k = 2048, W = 8).
+ *   resend   uint8 [rows][W]: 1 where shard w added its whole top-k. With
+ *            fewer than k candidates in all (short rows) there is no cutoff
+ *            and every shard that sent C candidates resends; a shard with
+ *            fewer than C tokens sent all of them and never resends.
+ *   ws       dsa_dcp_workspace_size(DSA_WS_DCP_TOPK, rows, ld, k, W, C) bytes.
+ */
+int32_t dsa_dcp_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows, int32_t k, int32_t W,
+                     int32_t C, int32_t* idx, uint8_t* resend, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_dcp_mla_decode: shard w runs dsa_sparse_mla_decode over the entries of
+ * idx it owns (p mod W == w, the others skipped), giving a bf16 partial
+ * output and its lse; the W partials are combined as
+ *   L = log sum_w exp(lse_w),  out = sum_w exp(lse_w - L) out_w,
+ * into out (bf16 [rows][16][512]) and lse (fp32 [rows][16], may be NULL).
+ * Arguments as for dsa_sparse_mla_decode, plus W (2..64); at most 65535 rows.
+ *   ws  dsa_dcp_workspace_size(DSA_WS_DCP_MLA, rows, 0, k, W, 0) bytes.
+ */
+int32_t dsa_dcp_mla_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t num_heads,
+                           const int32_t* idx, int32_t k, int32_t W, float softmax_scale, void* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of the DCP entry points (ld is unused for DSA_WS_DCP_MLA, C
+ * for DSA_WS_DCP_MLA). */
+size_t dsa_dcp_workspace_size(int32_t kind, int32_t rows, int64_t ld, int32_t k, int32_t W, int32_t C);
 
 /* Workspace bytes an entry point needs (0 if it needs none). For DSA_WS_TOPK,
  * `max_ctx` is the longest row_len. Returns 0 and no error for an unknown kind. */

@@ -22,6 +22,8 @@ from ._lib import (  # noqa: F401
     DSA_OK,
     DSA_Q_BF16,
     DSA_Q_FP8,
+    DSA_WS_DCP_MLA,
+    DSA_WS_DCP_TOPK,
     DSA_WS_DECODE,
     DSA_WS_MLA_DECODE,
     DSA_WS_MLA_PREFILL,
@@ -163,6 +165,10 @@ def dsa_workspace_size(kind: int, rows: int, max_ctx: int, k: int, num_heads: in
     return int(load().dsa_workspace_size(kind, rows, max_ctx, k, num_heads))
 
 
+def dsa_dcp_workspace_size(kind: int, rows: int, ld: int, k: int, W: int, C: int = 0) -> int:
+    return int(load().dsa_dcp_workspace_size(kind, rows, ld, k, W, C))
+
+
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
@@ -219,6 +225,33 @@ def dsa_topk(scores, row_len, k: int, idx, ws, stream=None):
         _ptr(ws), int(ws.numel()) if ws is not None else 0, _stream(stream),
     )
     _check(st, "dsa_topk")
+
+
+def dsa_dcp_topk(scores, row_len, k: int, W: int, C: int, idx, resend, ws, stream=None):
+    """The exact top-k merged across W virtual shards (token p on shard p mod W);
+    idx as dsa_topk, resend uint8 [rows, W]."""
+    rows = int(scores.shape[0])
+    _check_scores(scores, rows, 1)
+    _need(row_len, "row_len", _I32, rows)
+    _need(idx, "idx", _I32, rows * int(k))
+    _need(resend, "resend", (torch.uint8,), rows * int(W))
+    if ws is not None:
+        _need(ws, "ws", (torch.uint8,))
+    st = load().dsa_dcp_topk(
+        _ptr(scores), int(scores.stride(0)), _ptr(row_len), rows, int(k), int(W), int(C), _ptr(idx), _ptr(resend),
+        _ptr(ws), int(ws.numel()) if ws is not None else 0, _stream(stream),
+    )
+    _check(st, "dsa_dcp_topk")
+
+
+def dsa_dcp_mla_decode(batch, cache, q, idx, W: int, softmax_scale, out, lse=None, ws=None, stream=None):
+    """Each of W virtual shards attends over the entries of idx it owns; partials combined by LSE."""
+    fn = load().dsa_dcp_mla_decode
+
+    def call(b, c, qp, nh, ip, k, sm, op, lp, wp, wn, s):
+        return fn(b, c, qp, nh, ip, k, int(W), sm, op, lp, wp, wn, s)
+
+    _mla(call, "dsa_dcp_mla_decode", batch, cache, q, idx, softmax_scale, out, lse, ws, stream)
 
 
 def _mla(fn, name, batch, cache, q, idx, softmax_scale, out, lse, ws, stream):

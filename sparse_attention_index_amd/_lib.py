@@ -19,6 +19,8 @@ DSA_WS_TOPK = 1
 DSA_WS_MLA_DECODE = 2
 DSA_WS_MLA_PREFILL = 3
 DSA_WS_DECODE = 4
+DSA_WS_DCP_TOPK = 5
+DSA_WS_DCP_MLA = 6
 
 EXPORTS = (
     "dsa_index_key_write",
@@ -28,6 +30,9 @@ EXPORTS = (
     "dsa_sparse_mla_prefill",
     "dsa_decode",
     "dsa_workspace_size",
+    "dsa_dcp_topk",
+    "dsa_dcp_mla_decode",
+    "dsa_dcp_workspace_size",
     "dsa_status_string",
     "dsa_last_error",
     "dsa_version",
@@ -88,6 +93,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsa_sparse_mla_prefill": (I32, [BP, CP, P, I32, P, I32, F, P, P, P, SZ, P]),
         "dsa_decode": (I32, [BP, CP, P, P, P, I32, I32, F, P, P, P, P, SZ, P]),
         "dsa_workspace_size": (SZ, [I32, I32, I64, I32, I32]),
+        "dsa_dcp_topk": (I32, [P, I64, P, I32, I32, I32, I32, P, P, P, SZ, P]),
+        "dsa_dcp_mla_decode": (I32, [BP, CP, P, I32, P, I32, I32, F, P, P, P, SZ, P]),
+        "dsa_dcp_workspace_size": (SZ, [I32, I32, I64, I32, I32, I32]),
         "dsa_status_string": (ctypes.c_char_p, [I32]),
         "dsa_last_error": (ctypes.c_char_p, []),
         "dsa_version": (I32, []),

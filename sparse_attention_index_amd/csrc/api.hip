@@ -313,6 +313,64 @@ size_t dsa_workspace_size(int32_t kind, int32_t rows, int64_t max_ctx, int32_t k
   }
 }
 
+int32_t dsa_dcp_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows, int32_t k, int32_t W,
+                     int32_t C, int32_t* idx, uint8_t* resend, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (rows < 0 || ld < 1) return fail(DSA_ERR_INVALID_ARG, "rows must be >= 0 and ld >= 1");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in [1, 2048]");
+  if (W < 2 || W > 64) return fail(DSA_ERR_UNSUPPORTED, "W must be in [2, 64]");
+  if (C < 1 || C > k) return fail(DSA_ERR_INVALID_ARG, "C must be in [1, k]");
+  if (rows == 0) return DSA_OK;
+  if (!scores || !row_len || !idx || !resend) return fail(DSA_ERR_INVALID_ARG, "scores, row_len, idx or resend is null");
+  if (ld > INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "rows longer than 2^31 scores");
+  if ((int64_t)rows * W > 65535) return fail(DSA_ERR_UNSUPPORTED, "rows * W must be <= 65535");
+  const size_t need = dsa_dcp_workspace_size(DSA_WS_DCP_TOPK, rows, ld, k, W, C);
+  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "dcp topk needs %zu workspace bytes", need);
+  return hip_status(launch_dcp_topk(scores, ld, row_len, rows, k, W, C, idx, resend, ws,
+                                    static_cast<hipStream_t>(stream)),
+                    "dcp topk");
+}
+
+int32_t dsa_dcp_mla_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t num_heads,
+                           const int32_t* idx, int32_t k, int32_t W, float softmax_scale, void* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int32_t r = check_batch(batch);
+  if (r) return r;
+  if ((r = check_cache(cache, false, true))) return r;
+  if ((r = check_mla(num_heads, k, q, idx, out, true))) return r;
+  if (W < 2 || W > 64) return fail(DSA_ERR_UNSUPPORTED, "W must be in [2, 64]");
+  const int32_t rows = batch->num_requests * batch->rows_per_request;
+  if (rows > 65535) return fail(DSA_ERR_UNSUPPORTED, "at most 65535 rows");
+  const size_t need = dsa_dcp_workspace_size(DSA_WS_DCP_MLA, rows, 0, k, W, 0);
+  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "dcp mla needs %zu workspace bytes", need);
+  MlaArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.idx = idx;
+  a.lat_fp8 = cache->lat_fp8;
+  a.lat_scale = cache->lat_scale;
+  a.block_table = batch->block_table;
+  a.max_blocks = batch->max_blocks;
+  a.R = batch->rows_per_request;
+  a.k = k;
+  a.sm_scale = softmax_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  return hip_status(launch_dcp_mla(a, rows, W, ws, static_cast<hipStream_t>(stream)), "dcp mla");
+}
+
+size_t dsa_dcp_workspace_size(int32_t kind, int32_t rows, int64_t ld, int32_t k, int32_t W, int32_t C) {
+  if (rows <= 0 || k < 1 || W < 1) return 0;
+  switch (kind) {
+    case DSA_WS_DCP_TOPK:
+      return C < 1 ? 0 : dcp_topk_ws_bytes(rows, ld < 1 ? 1 : ld, k, W, C);
+    case DSA_WS_DCP_MLA:
+      return dcp_mla_ws_bytes(rows, k, W);
+    default:
+      return 0;
+  }
+}
+
 const char* dsa_status_string(int32_t status) {
   switch (status) {
     case DSA_OK: return "ok";

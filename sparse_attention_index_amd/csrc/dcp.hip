@@ -1,0 +1,292 @@
+// Decode context parallelism simulated on one device: the exact top-k merge
+// across W virtual shards and the log-sum-exp combine of their partial
+// attention outputs.
+//
+// "SGLang Day-0 Support for Kimi K3.1 Pro", section "Decode: DSA with decode
+// context parallelism", and "vLLM Day-0 Support for Kimi K3.1 Pro", section
+// "An exact top-k merge with about 10x less traffic": token p lives on shard
+// p mod W; each shard takes its local top-k and sends its best C candidates;
+// the k-th best of the W x C candidates is the cutoff; a shard whose C
+// candidates all beat the cutoff may hold more winners and adds its whole
+// local top-k; the k best of that pool are exactly the single-device top-k.
+// Each shard then attends to the winners it owns, and the partial outputs are
+// combined by their log-sum-exp ("TokenSpeed Kimi K3.1", section "Sharding
+// long contexts with decode context parallelism").
+//
+// Here the shards are rows of one device's memory and the exchanges are
+// plain reads. Ranking everywhere is the selection's total order: score
+// descending, then position ascending, as one 64-bit composite (ordered
+// score key, ~position). Candidate pools are position-indexed score rows
+// with -inf outside the pool, so the selection kernels (which break ties by
+// the lower index) rank a pool exactly as the single device ranks the row.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+
+static constexpr int kDcpThreads = 256;
+
+static size_t a256(size_t x) { return (x + 255) / 256 * 256; }
+
+static int64_t shard_ld(int64_t ld, int W) { return ((ld + W - 1) / W + 63) / 64 * 64; }
+
+struct DcpTopkWs {
+  float* shard_scores;  // [rows W][lds]
+  int32_t* shard_len;   // [rows W]
+  int32_t* local_idx;   // [rows W][k]  shard indices of each shard's top-k
+  int32_t* cand_idx;    // [rows W][C]  shard indices of each shard's top-C
+  float* pool;          // [rows][ld]   position-indexed pool row (-inf outside)
+  int32_t* sel;         // [rows][k]    the cutoff selection
+  void* topk;           // selection workspace
+};
+
+static size_t dcp_topk_parts(int rows, int64_t ld, int k, int W, int C, DcpTopkWs* p, void* base) {
+  const int64_t lds = shard_ld(ld, W);
+  const size_t rw = (size_t)rows * W;
+  const size_t sizes[7] = {a256(rw * lds * 4), a256(rw * 4), a256(rw * k * 4), a256(rw * C * 4),
+                           a256((size_t)rows * ld * 4), a256((size_t)rows * k * 4),
+                           a256(topk_ws_bytes((int)rw, lds) > topk_ws_bytes(rows, ld) ? topk_ws_bytes((int)rw, lds)
+                                                                                       : topk_ws_bytes(rows, ld))};
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  if (p) {
+    p->shard_scores = reinterpret_cast<float*>(b + off);
+    off += sizes[0];
+    p->shard_len = reinterpret_cast<int32_t*>(b + off);
+    off += sizes[1];
+    p->local_idx = reinterpret_cast<int32_t*>(b + off);
+    off += sizes[2];
+    p->cand_idx = reinterpret_cast<int32_t*>(b + off);
+    off += sizes[3];
+    p->pool = reinterpret_cast<float*>(b + off);
+    off += sizes[4];
+    p->sel = reinterpret_cast<int32_t*>(b + off);
+    off += sizes[5];
+    p->topk = b + off;
+    off += sizes[6];
+    return off;
+  }
+  for (size_t s : sizes) off += s;
+  return off;
+}
+
+size_t dcp_topk_ws_bytes(int rows, int64_t ld, int k, int W, int C) {
+  return dcp_topk_parts(rows, ld, k, W, C, nullptr, nullptr);
+}
+
+// Shard w of row r: positions w, w + W, ... below row_len[r], packed.
+__global__ __launch_bounds__(kDcpThreads) void dcp_gather_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                 const int32_t* __restrict__ row_len, int W,
+                                                                 float* __restrict__ shard, int64_t lds,
+                                                                 int32_t* __restrict__ shard_len) {
+  const int rw = blockIdx.y;
+  const int r = rw / W, w = rw % W;
+  const int n = row_len[r];
+  const int len = n > w ? (n - w + W - 1) / W : 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) shard_len[rw] = len;
+  const int64_t i = (int64_t)blockIdx.x * kDcpThreads + threadIdx.x;
+  if (i < len) shard[(size_t)rw * lds + i] = scores[(size_t)r * ld + w + (int64_t)W * i];
+}
+
+// pool[r][p] = -inf for every visible position p.
+__global__ __launch_bounds__(kDcpThreads) void dcp_clear_kernel(float* __restrict__ pool, int64_t ld,
+                                                                const int32_t* __restrict__ row_len) {
+  const int r = blockIdx.y;
+  const int64_t p = (int64_t)blockIdx.x * kDcpThreads + threadIdx.x;
+  if (p < row_len[r]) pool[(size_t)r * ld + p] = -INFINITY;
+}
+
+// Put shard entries into the pool: shard w of row r contributes its top-k
+// (if use_local and its resend flag is set) or its top-C.
+__global__ __launch_bounds__(kDcpThreads) void dcp_scatter_kernel(const float* __restrict__ scores, int64_t ld, int W,
+                                                                  int k, int C, const int32_t* __restrict__ local_idx,
+                                                                  const int32_t* __restrict__ cand_idx,
+                                                                  const uint8_t* __restrict__ resend,
+                                                                  float* __restrict__ pool) {
+  const int rw = blockIdx.x;
+  const int r = rw / W, w = rw % W;
+  const bool full = resend && resend[rw];
+  const int32_t* src = full ? local_idx + (size_t)rw * k : cand_idx + (size_t)rw * C;
+  const int n = full ? k : C;
+  for (int j = threadIdx.x; j < n; j += kDcpThreads) {
+    const int i = src[j];
+    if (i >= 0) {
+      const int64_t p = w + (int64_t)W * i;
+      pool[(size_t)r * ld + p] = scores[(size_t)r * ld + p];
+    }
+  }
+}
+
+DSA_DEV uint64_t rank_of(const float* srow, int64_t p) {
+  return ((uint64_t)ordered_key(srow[p]) << 32) | (uint64_t)(~(uint32_t)p);
+}
+
+// Minimum of a 64-bit value over the workgroup (every thread gets it).
+DSA_DEV uint64_t block_min64(uint64_t v, uint64_t* red) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t u = __shfl_xor(v, o);
+    v = u < v ? u : v;
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t m = red[0];
+  for (int i = 1; i < kDcpThreads / 64; ++i) m = red[i] < m ? red[i] : m;
+  return m;
+}
+
+// Per row: the cutoff (the worst of the k best candidates) and each shard's
+// resend flag (its C candidates all rank above the cutoff; with fewer than
+// k candidates there is no cutoff and every shard that sent C resends).
+__global__ __launch_bounds__(kDcpThreads) void dcp_cutoff_kernel(const float* __restrict__ scores, int64_t ld, int W,
+                                                                 int k, int C, const int32_t* __restrict__ shard_len,
+                                                                 const int32_t* __restrict__ cand_idx,
+                                                                 const int32_t* __restrict__ sel,
+                                                                 uint8_t* __restrict__ resend) {
+  __shared__ uint64_t red[kDcpThreads / 64];
+  const int r = blockIdx.x;
+  const float* srow = scores + (size_t)r * ld;
+  int ncand = 0;
+  for (int w = 0; w < W; ++w) ncand += min(C, shard_len[r * W + w]);
+  const bool have_cut = ncand >= k;
+  uint64_t cut = 0;
+  if (have_cut) {  // uniform
+    uint64_t m = ~0ull;
+    for (int j = threadIdx.x; j < k; j += kDcpThreads) {
+      const int p = sel[(size_t)r * k + j];
+      if (p >= 0) {
+        const uint64_t v = rank_of(srow, p);
+        m = v < m ? v : m;
+      }
+    }
+    cut = block_min64(m, red);
+  }
+  for (int w = 0; w < W; ++w) {
+    const int rw = r * W + w;
+    if (shard_len[rw] < C) {  // sent everything it holds
+      if (threadIdx.x == 0) resend[rw] = 0;
+      continue;
+    }
+    uint64_t m = ~0ull;
+    for (int j = threadIdx.x; j < C; j += kDcpThreads) {
+      const int i = cand_idx[(size_t)rw * C + j];
+      const uint64_t v = rank_of(srow, w + (int64_t)W * i);
+      m = v < m ? v : m;
+    }
+    const uint64_t last = block_min64(m, red);
+    if (threadIdx.x == 0) resend[rw] = (!have_cut || last > cut) ? 1 : 0;
+  }
+}
+
+hipError_t launch_dcp_topk(const float* scores, int64_t ld, const int32_t* row_len, int rows, int k, int W, int C,
+                           int32_t* idx, uint8_t* resend, void* ws, hipStream_t st) {
+  DcpTopkWs p;
+  dcp_topk_parts(rows, ld, k, W, C, &p, ws);
+  const int64_t lds = shard_ld(ld, W);
+  const int rw = rows * W;
+  hipError_t e;
+  // 1-2. shards and their local top-k and top-C
+  hipLaunchKernelGGL(dcp_gather_kernel, dim3((unsigned)((lds + kDcpThreads - 1) / kDcpThreads), rw),
+                     dim3(kDcpThreads), 0, st, scores, ld, row_len, W, p.shard_scores, lds, p.shard_len);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const TopkWs sw = topk_ws_carve(p.topk, rw, lds);
+  if ((e = launch_topk(p.shard_scores, lds, p.shard_len, rw, lds, k, p.local_idx, sw, st)) != hipSuccess) return e;
+  if ((e = launch_topk(p.shard_scores, lds, p.shard_len, rw, lds, C, p.cand_idx, sw, st)) != hipSuccess) return e;
+  // 3-4. the W x C candidates, their k best, the cutoff and the resend flags
+  const TopkWs tw = topk_ws_carve(p.topk, rows, ld);
+  const dim3 rows_grid((unsigned)((ld + kDcpThreads - 1) / kDcpThreads), rows);
+  hipLaunchKernelGGL(dcp_clear_kernel, rows_grid, dim3(kDcpThreads), 0, st, p.pool, ld, row_len);
+  hipLaunchKernelGGL(dcp_scatter_kernel, dim3(rw), dim3(kDcpThreads), 0, st, scores, ld, W, k, C, p.local_idx,
+                     p.cand_idx, (const uint8_t*)nullptr, p.pool);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_topk(p.pool, ld, const_cast<int32_t*>(row_len), rows, ld, k, p.sel, tw, st)) != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(dcp_cutoff_kernel, dim3(rows), dim3(kDcpThreads), 0, st, scores, ld, W, k, C, p.shard_len,
+                     p.cand_idx, p.sel, resend);
+  // 5-6. the pool with resent top-k lists, and its k best
+  hipLaunchKernelGGL(dcp_clear_kernel, rows_grid, dim3(kDcpThreads), 0, st, p.pool, ld, row_len);
+  hipLaunchKernelGGL(dcp_scatter_kernel, dim3(rw), dim3(kDcpThreads), 0, st, scores, ld, W, k, C, p.local_idx,
+                     p.cand_idx, (const uint8_t*)resend, p.pool);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_topk(p.pool, ld, const_cast<int32_t*>(row_len), rows, ld, k, idx, tw, st);
+}
+
+// ---------------------------------------------------------------- attention
+
+size_t dcp_mla_ws_bytes(int rows, int k, int W) {
+  return a256((size_t)W * rows * k * 4) + a256((size_t)W * rows * kMlaHeads * kV * 2) +
+         a256((size_t)W * rows * kMlaHeads * 4) + a256(mla_ws_bytes(rows, k, true));
+}
+
+// idx_w[w][r][j] = idx[r][j] where shard w owns it, else -1.
+__global__ __launch_bounds__(kDcpThreads) void dcp_owner_kernel(const int32_t* __restrict__ idx, int rows, int k,
+                                                                int W, int32_t* __restrict__ idx_w) {
+  const size_t n = (size_t)rows * k;
+  const size_t i = (size_t)blockIdx.x * kDcpThreads + threadIdx.x;
+  if (i >= n) return;
+  const int p = idx[i];
+  for (int w = 0; w < W; ++w) idx_w[(size_t)w * n + i] = (p >= 0 && p % W == w) ? p : -1;
+}
+
+// out = sum_w exp(lse_w - L) out_w, L = log sum_w exp(lse_w); one thread per
+// (row, head, 4 dims).
+__global__ __launch_bounds__(kDcpThreads) void dcp_combine_kernel(const uint16_t* __restrict__ out_w,
+                                                                  const float* __restrict__ lse_w, int rows, int W,
+                                                                  uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int r = blockIdx.y;
+  const int h = threadIdx.x >> 4;
+  const int d = 64 * blockIdx.x + 4 * (threadIdx.x & 15);
+  const size_t rh = (size_t)r * kMlaHeads + h;
+  const size_t stride_l = (size_t)rows * kMlaHeads;
+  float M = -INFINITY;
+  for (int w = 0; w < W; ++w) M = fmaxf(M, lse_w[w * stride_l + rh]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (M != -INFINITY) {
+    for (int w = 0; w < W; ++w) {
+      const float lw = lse_w[w * stride_l + rh];
+      if (lw == -INFINITY) continue;
+      const float f = __expf(lw - M);
+      tot += f;
+      const __bf16* ow = reinterpret_cast<const __bf16*>(out_w) + (w * stride_l + rh) * kV + d;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += f * (float)ow[e];
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  __bf16* o = reinterpret_cast<__bf16*>(out) + rh * kV + d;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[e] * inv);
+  if (lse && blockIdx.x == 0 && (threadIdx.x & 15) == 0) lse[rh] = tot > 0.f ? M + __logf(tot) : -INFINITY;
+}
+
+hipError_t launch_dcp_mla(const MlaArgs& a, int rows, int W, void* ws, hipStream_t st) {
+  char* b = static_cast<char*>(ws);
+  int32_t* idx_w = reinterpret_cast<int32_t*>(b);
+  b += a256((size_t)W * rows * a.k * 4);
+  uint16_t* out_w = reinterpret_cast<uint16_t*>(b);
+  b += a256((size_t)W * rows * kMlaHeads * kV * 2);
+  float* lse_w = reinterpret_cast<float*>(b);
+  b += a256((size_t)W * rows * kMlaHeads * 4);
+  void* mla_ws = b;
+  const size_t n = (size_t)rows * a.k;
+  hipLaunchKernelGGL(dcp_owner_kernel, dim3((unsigned)((n + kDcpThreads - 1) / kDcpThreads)), dim3(kDcpThreads), 0,
+                     st, a.idx, rows, a.k, W, idx_w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int w = 0; w < W; ++w) {  // each shard's partial attention over the winners it owns
+    MlaArgs s = a;
+    s.idx = idx_w + (size_t)w * n;
+    s.slots = nullptr;
+    s.out = out_w + (size_t)w * rows * kMlaHeads * kV;
+    s.lse = lse_w + (size_t)w * rows * kMlaHeads;
+    if ((e = launch_sparse_mla(s, rows, true, mla_ws, st)) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(dcp_combine_kernel, dim3(kV / 64, rows), dim3(kDcpThreads), 0, st, out_w, lse_w, rows, W,
+                     a.out, a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

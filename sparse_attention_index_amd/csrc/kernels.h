@@ -69,6 +69,13 @@ struct MlaArgs {
 };
 
 size_t mla_ws_bytes(int rows, int k, bool split);
+
+// Decode context parallelism over W virtual shards of one device.
+size_t dcp_topk_ws_bytes(int rows, int64_t ld, int k, int W, int C);
+hipError_t launch_dcp_topk(const float* scores, int64_t ld, const int32_t* row_len, int rows, int k, int W, int C,
+                           int32_t* idx, uint8_t* resend, void* ws, hipStream_t st);
+size_t dcp_mla_ws_bytes(int rows, int k, int W);
+hipError_t launch_dcp_mla(const struct MlaArgs& a, int rows, int W, void* ws, hipStream_t st);
 // split == true spreads each row's k positions over several workgroups and
 // merges the partial results by log-sum-exp; false gives each row one workgroup.
 hipError_t launch_sparse_mla(const MlaArgs& a, int rows, bool split, void* ws, hipStream_t st);
