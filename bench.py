@@ -448,6 +448,134 @@ def run_key_write(args, torch, dsa):
     }
 
 
+DCP = {
+    # name: (decode workload, virtual shards W)
+    "dcp8_decode_16x4_32k": ("decode_16x4_32k", 8),
+    "dcp8_decode_16x4_ragged_128k_256k": ("decode_16x4_ragged_128k_256k", 8),
+}
+
+
+def run_dcp(args, torch, dsa, traffic):
+    """One decode step under decode context parallelism, simulated on this
+    GPU: score -> exact top-k merge over W virtual shards -> per-shard sparse
+    MLA + LSE combine. The shards are regions of one device's memory, so this
+    measures the merge's and the combine's device work, not the exchanges."""
+    from workloads import case_config, make_case
+
+    base, W = DCP[args.workload]
+    cfg = case_config(base)
+    B, R, lens = cfg["B"], cfg["R"], cfg["lengths"]
+    k, C = 2048, int(1.5 * 2048 / W)
+    rows = B * R
+    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query", "key_format")}
+    nsets = 2
+    cases = [make_case(B, R, lens, seed=cfg["seed"] + 100 * i, device="cuda", name=base, **kw) for i in range(nsets)]
+    batches = [dsa.Batch.of(c) for c in cases]
+    caches = [dsa.Cache.of(c) for c in cases]
+    row_len = [(c.positions() + 1).to(torch.int32).cuda() for c in cases]
+    ld = (max(lens) + 63) // 64 * 64
+    scores = torch.empty((rows, ld), dtype=torch.float32, device="cuda")
+    idx = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    resend = torch.empty((rows, W), dtype=torch.uint8, device="cuda")
+    out = torch.empty((rows, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((rows, 16), dtype=torch.float32, device="cuda")
+    tws = dsa.workspace(dsa.dsa_dcp_workspace_size(dsa.DSA_WS_DCP_TOPK, rows, ld, k, W, C))
+    mws = dsa.workspace(dsa.dsa_dcp_workspace_size(dsa.DSA_WS_DCP_MLA, rows, 0, k, W))
+
+    def score(i):
+        j = i % nsets
+        dsa.dsa_index_score(batches[j], caches[j], cases[j].q_idx, cases[j].w, scores)
+
+    def merge(i):
+        dsa.dsa_dcp_topk(scores, row_len[i % nsets], k, W, C, idx, resend, tws)
+
+    def attend(i):
+        j = i % nsets
+        dsa.dsa_dcp_mla_decode(batches[j], caches[j], cases[j].q_mla, idx, W, cases[j].sm_scale, out, lse, mws)
+
+    def step(i):
+        score(i)
+        merge(i)
+        attend(i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(1e8))
+    ev0.record()
+    for i in range(n):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / n
+    stage_us = stage_times(torch, [("score", score), ("dcp_topk", merge), ("dcp_attend", attend)], min(n, 50))
+    # the merge stage against HBM: its algorithmic input is every visible score, read once
+    merge_us = kernel_time(torch, merge, nsets)
+    vis = sum(traffic.visible(lens, R))
+    merge_bytes = vis * traffic.SCORE_BYTES + rows * k * 4
+    achieved = merge_bytes / (merge_us * 1e-6) / 1e9
+    sec = ms_step * 1e-3
+    return {
+        "metric": METRIC,
+        "value": sum(lens) / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "decode_workload": base, "virtual_shards": W, "candidates": C,
+                   "requests": B, "rows_per_request": R, "topk": k,
+                   "note": "DCP simulated on one GPU: merge and LSE combine on device, no exchange",
+                   "launch": "eager, back to back"},
+        "rows_per_s": rows / sec,
+        "stages_us": stage_us,
+        "resend_rows": int(resend.any(dim=1).sum().item()),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "dcp_topk (stage)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes": merge_bytes,
+            "avg_launch_us": merge_us,
+        },
+    }
+
+
+def dcp_cpu_baseline(workload_name, budget_s):
+    """The oracle's DCP merge on random score rows of the workload's length."""
+    import numpy as np
+
+    import oracle
+    from workloads import case_config
+
+    base, W = DCP[workload_name]
+    cfg = case_config(base)
+    L = cfg["lengths"][0]
+    rng = np.random.default_rng(2)
+    rows, spent = 0, 0.0
+    while spent < budget_s or rows == 0:
+        s = rng.standard_normal(L)
+        t0 = time.perf_counter()
+        oracle.dcp_select(s, W, 2048)
+        spent += time.perf_counter() - t0
+        rows += 1
+        if rows >= 200:
+            break
+    return {"value": rows * L / spent, "unit": "tokens/s", "rows_per_s": rows / spent, "cores": _threads(),
+            "kind": "oracle",
+            "sample": f"{rows} score rows of {L} tokens, merge only (W = {W}), numpy on the host, {spent:.1f} s"}
+
+
 def key_write_cpu_baseline(workload_name, budget_s):
     """The oracle's key write on the same number of rows (host numpy)."""
     import numpy as np
@@ -485,6 +613,12 @@ def main():
 
     dsa.load()
     torch.cuda.set_device(0)
+    if args.workload in DCP:
+        result = run_dcp(args, torch, dsa, traffic)
+        if args.cpu_seconds > 0:
+            result["cpu_baseline"] = dcp_cpu_baseline(args.workload, min(args.cpu_seconds, 15.0))
+        print(json.dumps(result), flush=True)
+        return
     if args.workload in KEY_WRITE:
         result = run_key_write(args, torch, dsa)
         if args.cpu_seconds > 0:

@@ -248,6 +248,7 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
  *            and every shard that sent C candidates resends; a shard with
  *            fewer than C tokens sent all of them and never resends.
  *   ws       dsa_dcp_workspace_size(DSA_WS_DCP_TOPK, rows, ld, k, W, C) bytes.
+ * Scores must be finite (-inf marks positions outside a candidate pool).
  */
 int32_t dsa_dcp_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows, int32_t k, int32_t W,
                      int32_t C, int32_t* idx, uint8_t* resend, void* ws, size_t ws_bytes, void* stream);

@@ -16,9 +16,10 @@
 // Here the shards are rows of one device's memory and the exchanges are
 // plain reads. Ranking everywhere is the selection's total order: score
 // descending, then position ascending, as one 64-bit composite (ordered
-// score key, ~position). Candidate pools are position-indexed score rows
-// with -inf outside the pool, so the selection kernels (which break ties by
-// the lower index) rank a pool exactly as the single device ranks the row.
+// score key, ~position). A candidate pool is first scattered into a
+// position-indexed row (-inf outside the pool), then compacted in position
+// order, so the selection kernels (which break ties by the lower index) rank
+// the pool exactly as the single device ranks the row.
 #include <math.h>
 
 #include "common.h"
@@ -32,43 +33,57 @@ static size_t a256(size_t x) { return (x + 255) / 256 * 256; }
 
 static int64_t shard_ld(int64_t ld, int W) { return ((ld + W - 1) / W + 63) / 64 * 64; }
 
+// Longest compacted pool of a row: every shard's whole top-k, or the row.
+static int64_t comp_ld(int64_t ld, int k, int W) {
+  const int64_t m = (int64_t)W * k < ld ? (int64_t)W * k : ld;
+  return (m + 63) / 64 * 64;
+}
+
 struct DcpTopkWs {
   float* shard_scores;  // [rows W][lds]
   int32_t* shard_len;   // [rows W]
   int32_t* local_idx;   // [rows W][k]  shard indices of each shard's top-k
   int32_t* cand_idx;    // [rows W][C]  shard indices of each shard's top-C
   float* pool;          // [rows][ld]   position-indexed pool row (-inf outside)
-  int32_t* sel;         // [rows][k]    the cutoff selection
+  int32_t* sel;         // [rows][k]    the cutoff selection (positions)
+  float* comp_score;    // [rows][cld]  the pool compacted in position order
+  int32_t* comp_pos;    // [rows][cld]  their positions
+  int32_t* comp_len;    // [rows]
+  int32_t* comp_sel;    // [rows][k]    a selection over the compacted pool
   void* topk;           // selection workspace
 };
 
 static size_t dcp_topk_parts(int rows, int64_t ld, int k, int W, int C, DcpTopkWs* p, void* base) {
   const int64_t lds = shard_ld(ld, W);
+  const int64_t cld = comp_ld(ld, k, W);
   const size_t rw = (size_t)rows * W;
-  const size_t sizes[7] = {a256(rw * lds * 4), a256(rw * 4), a256(rw * k * 4), a256(rw * C * 4),
-                           a256((size_t)rows * ld * 4), a256((size_t)rows * k * 4),
-                           a256(topk_ws_bytes((int)rw, lds) > topk_ws_bytes(rows, ld) ? topk_ws_bytes((int)rw, lds)
-                                                                                       : topk_ws_bytes(rows, ld))};
-  size_t off = 0;
+  const size_t tk1 = topk_ws_bytes((int)rw, lds), tk2 = topk_ws_bytes(rows, cld);
+  const size_t sizes[11] = {a256(rw * lds * 4),       a256(rw * 4),
+                            a256(rw * k * 4),         a256(rw * C * 4),
+                            a256((size_t)rows * ld * 4), a256((size_t)rows * k * 4),
+                            a256((size_t)rows * cld * 4), a256((size_t)rows * cld * 4),
+                            a256((size_t)rows * 4),    a256((size_t)rows * k * 4),
+                            a256(tk1 > tk2 ? tk1 : tk2)};
   char* b = static_cast<char*>(base);
+  void** slots[11] = {nullptr};
   if (p) {
-    p->shard_scores = reinterpret_cast<float*>(b + off);
-    off += sizes[0];
-    p->shard_len = reinterpret_cast<int32_t*>(b + off);
-    off += sizes[1];
-    p->local_idx = reinterpret_cast<int32_t*>(b + off);
-    off += sizes[2];
-    p->cand_idx = reinterpret_cast<int32_t*>(b + off);
-    off += sizes[3];
-    p->pool = reinterpret_cast<float*>(b + off);
-    off += sizes[4];
-    p->sel = reinterpret_cast<int32_t*>(b + off);
-    off += sizes[5];
-    p->topk = b + off;
-    off += sizes[6];
-    return off;
+    slots[0] = reinterpret_cast<void**>(&p->shard_scores);
+    slots[1] = reinterpret_cast<void**>(&p->shard_len);
+    slots[2] = reinterpret_cast<void**>(&p->local_idx);
+    slots[3] = reinterpret_cast<void**>(&p->cand_idx);
+    slots[4] = reinterpret_cast<void**>(&p->pool);
+    slots[5] = reinterpret_cast<void**>(&p->sel);
+    slots[6] = reinterpret_cast<void**>(&p->comp_score);
+    slots[7] = reinterpret_cast<void**>(&p->comp_pos);
+    slots[8] = reinterpret_cast<void**>(&p->comp_len);
+    slots[9] = reinterpret_cast<void**>(&p->comp_sel);
+    slots[10] = reinterpret_cast<void**>(&p->topk);
   }
-  for (size_t s : sizes) off += s;
+  size_t off = 0;
+  for (int i = 0; i < 11; ++i) {
+    if (p) *slots[i] = b + off;
+    off += sizes[i];
+  }
   return off;
 }
 
@@ -117,6 +132,77 @@ __global__ __launch_bounds__(kDcpThreads) void dcp_scatter_kernel(const float* _
       pool[(size_t)r * ld + p] = scores[(size_t)r * ld + p];
     }
   }
+}
+
+static constexpr int kCompThreads = 1024;
+
+// Inclusive sum over the wave (DPP row shifts, then row broadcasts).
+DSA_DEV uint32_t incl_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr 1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr 2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr 4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr 8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast 15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast 31
+  return x;
+}
+
+// The pool members of row r (entries above -inf) in position order:
+// comp_score / comp_pos[0 .. comp_len), one workgroup per row.
+__global__ __launch_bounds__(kCompThreads) void dcp_compact_kernel(const float* __restrict__ pool, int64_t ld,
+                                                                   const int32_t* __restrict__ row_len,
+                                                                   float* __restrict__ comp_score,
+                                                                   int32_t* __restrict__ comp_pos, int64_t cld,
+                                                                   int32_t* __restrict__ comp_len) {
+  __shared__ uint32_t wsum[kCompThreads / 64];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n = row_len[r];
+  const float* row = pool + (size_t)r * ld;
+  int64_t base = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += 4 * kCompThreads) {
+    const int64_t p0 = c0 + 4 * tid;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = p0 + e < n ? row[p0 + e] : -INFINITY;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cnt += v[e] > -INFINITY ? 1u : 0u;
+    const uint32_t incl = incl_sum(cnt);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+    for (int w = 0; w < kCompThreads / 64; ++w) {
+      const uint32_t s = wsum[w];
+      before += w < wave ? s : 0u;
+      total += s;
+    }
+    int64_t off = base + before + incl - cnt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (v[e] > -INFINITY) {
+        if (off < cld) {
+          comp_score[(size_t)r * cld + off] = v[e];
+          comp_pos[(size_t)r * cld + off] = (int32_t)(p0 + e);
+        }
+        ++off;
+      }
+    }
+    base += total;
+    __syncthreads();  // wsum is rewritten by the next chunk
+  }
+  if (tid == 0) comp_len[r] = (int32_t)(base < cld ? base : cld);
+}
+
+// Positions of a selection over the compacted pool.
+__global__ __launch_bounds__(kDcpThreads) void dcp_map_kernel(const int32_t* __restrict__ comp_sel,
+                                                              const int32_t* __restrict__ comp_pos, int64_t cld,
+                                                              int rows, int k, int32_t* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * kDcpThreads + threadIdx.x;
+  if (i >= (size_t)rows * k) return;
+  const size_t r = i / k;
+  const int j = comp_sel[i];
+  out[i] = j >= 0 ? comp_pos[r * cld + j] : -1;
 }
 
 DSA_DEV uint64_t rank_of(const float* srow, int64_t p) {
@@ -195,14 +281,26 @@ hipError_t launch_dcp_topk(const float* scores, int64_t ld, const int32_t* row_l
   if ((e = launch_topk(p.shard_scores, lds, p.shard_len, rw, lds, k, p.local_idx, sw, st)) != hipSuccess) return e;
   if ((e = launch_topk(p.shard_scores, lds, p.shard_len, rw, lds, C, p.cand_idx, sw, st)) != hipSuccess) return e;
   // 3-4. the W x C candidates, their k best, the cutoff and the resend flags
-  const TopkWs tw = topk_ws_carve(p.topk, rows, ld);
+  const int64_t cld = comp_ld(ld, k, W);
+  const TopkWs tw = topk_ws_carve(p.topk, rows, cld);
   const dim3 rows_grid((unsigned)((ld + kDcpThreads - 1) / kDcpThreads), rows);
+  const unsigned map_grid = (unsigned)(((size_t)rows * k + kDcpThreads - 1) / kDcpThreads);
+  // the k best of a scattered pool, as positions
+  auto select_pool = [&](int32_t* dst) -> hipError_t {
+    hipLaunchKernelGGL(dcp_compact_kernel, dim3(rows), dim3(kCompThreads), 0, st, p.pool, ld, row_len, p.comp_score,
+                       p.comp_pos, cld, p.comp_len);
+    hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    if ((e2 = launch_topk(p.comp_score, cld, p.comp_len, rows, cld, k, p.comp_sel, tw, st)) != hipSuccess) return e2;
+    hipLaunchKernelGGL(dcp_map_kernel, dim3(map_grid), dim3(kDcpThreads), 0, st, p.comp_sel, p.comp_pos, cld, rows, k,
+                       dst);
+    return hipGetLastError();
+  };
   hipLaunchKernelGGL(dcp_clear_kernel, rows_grid, dim3(kDcpThreads), 0, st, p.pool, ld, row_len);
   hipLaunchKernelGGL(dcp_scatter_kernel, dim3(rw), dim3(kDcpThreads), 0, st, scores, ld, W, k, C, p.local_idx,
                      p.cand_idx, (const uint8_t*)nullptr, p.pool);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = launch_topk(p.pool, ld, const_cast<int32_t*>(row_len), rows, ld, k, p.sel, tw, st)) != hipSuccess)
-    return e;
+  if ((e = select_pool(p.sel)) != hipSuccess) return e;
   hipLaunchKernelGGL(dcp_cutoff_kernel, dim3(rows), dim3(kDcpThreads), 0, st, scores, ld, W, k, C, p.shard_len,
                      p.cand_idx, p.sel, resend);
   // 5-6. the pool with resent top-k lists, and its k best
@@ -210,7 +308,7 @@ hipError_t launch_dcp_topk(const float* scores, int64_t ld, const int32_t* row_l
   hipLaunchKernelGGL(dcp_scatter_kernel, dim3(rw), dim3(kDcpThreads), 0, st, scores, ld, W, k, C, p.local_idx,
                      p.cand_idx, (const uint8_t*)resend, p.pool);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return launch_topk(p.pool, ld, const_cast<int32_t*>(row_len), rows, ld, k, idx, tw, st);
+  return select_pool(idx);
 }
 
 // ---------------------------------------------------------------- attention
