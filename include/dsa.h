@@ -227,7 +227,7 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
  * a request lives on shard p mod W of W devices; each shard scores and ranks
  * only its own tokens, the shards merge their candidates exactly, attend to
  * the winners they own, and combine the partial outputs by log-sum-exp
- * ("SGLang Day-0 Support for Kimi K3.1 Pro", section "Decode: DSA with decode
+ * ("Kimi K3.1 Pro: Day-0 Inference and RL Support with SGLang and Miles", section "Decode: DSA with decode
  * context parallelism"; "vLLM Day-0 Support for Kimi K3.1 Pro", section "An
  * exact top-k merge with about 10x less traffic"; "TokenSpeed Kimi K3.1",
  * section "Sharding long contexts with decode context parallelism"). Here the

@@ -1,7 +1,7 @@
 """Exact top-k merge and LSE combine under decode context parallelism,
 simulated on one device -- TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-The steps follow "SGLang Day-0 Support for Kimi K3.1 Pro", section "Decode:
+The steps follow "Kimi K3.1 Pro: Day-0 Inference and RL Support with SGLang and Miles", section "Decode:
 DSA with decode context parallelism", and "vLLM Day-0 Support for Kimi K3.1
 Pro", section "An exact top-k merge with about 10x less traffic":
 1. token p lives on shard p mod W; each shard scores only its tokens;

@@ -2,7 +2,7 @@
 // across W virtual shards and the log-sum-exp combine of their partial
 // attention outputs.
 //
-// "SGLang Day-0 Support for Kimi K3.1 Pro", section "Decode: DSA with decode
+// "Kimi K3.1 Pro: Day-0 Inference and RL Support with SGLang and Miles", section "Decode: DSA with decode
 // context parallelism", and "vLLM Day-0 Support for Kimi K3.1 Pro", section
 // "An exact top-k merge with about 10x less traffic": token p lives on shard
 // p mod W; each shard takes its local top-k and sends its best C candidates;
