@@ -29,8 +29,8 @@
 // the hardware drops stores past it, which applies the causal mask without
 // branches.
 //
-// The dot products run on v_mfma_scale_f32_32x32x64_f8f6f4 with the raw E4M3
-// key bytes as the B operand (no conversion). Queries enter as E4M3:
+// The dot products run on v_mfma_f32_32x32x64_f8f6f4 (the scaled form for
+// MXFP4 keys) with the raw key bytes as the B operand (no conversion). Queries enter as E4M3:
 //  * E4M3 queries (prefill chunks) are used as they are, their row scale
 //    applied after the head reduction;
 //  * bf16 queries are split exactly into two E4M3 terms, q * 2^e = hi + lo,
@@ -102,8 +102,9 @@ DSA_DEV uint32_t e4m3x2_from_f32(float a, float b) {
 
 
 // The E4M3 A operands of one query row: q * 2^e = hi + lo (bf16 queries) or
-// the query codes as they are; returns the factor 2^-e (or the row scale)
-// that multiplies the head's dot products.
+// the query codes as they are, with the factor 2^-e (or the row scale) that
+// multiplies the head's dot products. fetch_query loads the lane's raw bytes;
+// finish_query converts them, later, while the first key pages are in flight.
 //
 // K order. With FP8 keys, byte i of lane half g's operand for step s is dim
 // 64g + 32s + i. With MXFP4 keys the FP4 B operand of lane half g holds K
@@ -113,34 +114,66 @@ DSA_DEV uint32_t e4m3x2_from_f32(float a, float b) {
 // as 16 contiguous bytes), the query's byte i of lane half g, step s, must
 // be dim 32s + 16g + i (i < 16) or 64 + 32s + 16g + i - 16 (i >= 16).
 template <bool QFP8, bool KF4>
-DSA_DEV float load_query(const ScoreArgs& a, size_t row, int n, int g, i32x8 (&A)[QFP8 ? 1 : 2][2]) {
+struct QueryRaw {
+  u32x4 v[8];  // bf16 queries: 64 values per lane
+};
+template <bool KF4>
+struct QueryRaw<true, KF4> {
+  u32x4 p[4];  // E4M3 codes: 64 per lane
+  float scale;
+};
+
+template <bool QFP8, bool KF4>
+DSA_DEV void fetch_query(const ScoreArgs& a, size_t row, int n, int g, QueryRaw<QFP8, KF4>& r) {
   if constexpr (QFP8) {
     const uint8_t* q8 = reinterpret_cast<const uint8_t*>(a.q) + (row * kIdxHeads + n) * kIdxDim;
-    if constexpr (KF4) {
-      const u32x4 p0 = *reinterpret_cast<const u32x4*>(q8 + 16 * g);       // dims 16g + [0, 16)
-      const u32x4 p1 = *reinterpret_cast<const u32x4*>(q8 + 32 + 16 * g);  // 32 + 16g
-      const u32x4 p2 = *reinterpret_cast<const u32x4*>(q8 + 64 + 16 * g);  // 64 + 16g
-      const u32x4 p3 = *reinterpret_cast<const u32x4*>(q8 + 96 + 16 * g);  // 96 + 16g
-      A[0][0] = i32x8{(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3], (int)p2[0], (int)p2[1], (int)p2[2], (int)p2[3]};
-      A[0][1] = i32x8{(int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3], (int)p3[0], (int)p3[1], (int)p3[2], (int)p3[3]};
-    } else {
-      const i32x8* qp = reinterpret_cast<const i32x8*>(q8 + 64 * g);
-      A[0][0] = qp[0];
-      A[0][1] = qp[1];
-    }
-    return a.q_scale[row];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)  // MXFP4 keys: dims 32c + 16g + [0, 16); FP8 keys: dims 64g + 16c + [0, 16)
+      r.p[c] = *reinterpret_cast<const u32x4*>(q8 + (KF4 ? 32 * c + 16 * g : 64 * g + 16 * c));
+    r.scale = a.q_scale[row];
   } else {
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) +
-                                                       (row * kIdxHeads + n) * kIdxDim);
-    // x[32s + i]: the value at byte i of step s
-    float x[64];
-    float amax = 0.f;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.q) +
+                                                     (row * kIdxHeads + n) * kIdxDim);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       // piece c of 8 values: FP8 keys: dims 64g + 8c; MXFP4 keys: dims
       // 16g + 32u + 8(c & 1) for u = 0, 2, 1, 3 (c >> 1 = 0..3)
       const int u = (c >> 1) == 1 ? 2 : ((c >> 1) == 2 ? 1 : (c >> 1));
-      const bf16x8 v = KF4 ? qp[(16 * g + 32 * u) / 8 + (c & 1)] : qp[8 * g + c];
+      r.v[c] = KF4 ? qp[(16 * g + 32 * u) / 8 + (c & 1)] : qp[8 * g + c];
+    }
+  }
+}
+
+// Keeps the code that reads r after this point of the program (the raw
+// registers pass through an empty asm statement).
+template <bool QFP8, bool KF4>
+DSA_DEV void hold_query(QueryRaw<QFP8, KF4>& r) {
+  if constexpr (QFP8) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(r.p[c]));
+    asm volatile("" : "+v"(r.scale));
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(r.v[c]));
+  }
+}
+
+template <bool QFP8, bool KF4>
+DSA_DEV float finish_query(const QueryRaw<QFP8, KF4>& r, i32x8 (&A)[QFP8 ? 1 : 2][2]) {
+  if constexpr (QFP8) {
+    auto cat = [](const u32x4& x, const u32x4& y) {
+      return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+    };
+    A[0][0] = KF4 ? cat(r.p[0], r.p[2]) : cat(r.p[0], r.p[1]);
+    A[0][1] = KF4 ? cat(r.p[1], r.p[3]) : cat(r.p[2], r.p[3]);
+    return r.scale;
+  } else {
+    // x[32s + i]: the value at byte i of step s
+    float x[64];
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, r.v[c]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[8 * c + e] = (float)v[e];
@@ -209,31 +242,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // this workgroup's pages: blockIdx.x, +gridDim.x, ... below blk_lim
   const int stride = gridDim.x;
   const int n_my = blk_lim > (int)blockIdx.x ? (blk_lim - (int)blockIdx.x + stride - 1) / stride : 0;
-  {
-    const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
-    for (int i = tid; i < n_my; i += kThreads) tbl_s[i] = table[blockIdx.x + i * stride];
-  }
-
-  // ---- queries of this wave's rows (E4M3 terms) and head weights
   const int wr0 = wave * RPW;
-  i32x8 A[RPW][NT][2];
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    const int gr = min(wr0 + rr, nr - 1);  // clamp: rows past the group reuse a valid row, never written
-    const size_t row = row0 + gr;
-    const float head_scale = load_query<QFP8, KF4>(a, row, n, g, A[rr]);
-    // head weights with the head's scale folded in: w_s[row][head]
-    if (g == 0) {
-      const float wv = __uint_as_float((uint32_t)a.w[row * kIdxHeads + n] << 16);
-      w_s[wr0 + rr][n] = wv * head_scale;
-    }
-  }
-  __syncthreads();  // tbl_s and w_s ready
-  // the 16 heads this lane reduces (rows 8*(i/4) + 4g + i%4 of the 32x32 tile);
-  // kept in VGPRs for one row per wave, read from LDS otherwise
-  float wv[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) wv[i] = w_s[wr0][8 * (i >> 2) + 4 * g + (i & 3)];
 
   // Score stores go through one buffer descriptor per row whose size is the
   // row's visible prefix (positions 0 .. pos): the hardware drops any store
@@ -284,6 +293,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   };
 
+  // ---- prologue. The query rows and head weights are loaded first and the
+  // page table second, so that both loads are in flight together; one wait
+  // takes all of them. The copiers then put the first pages in flight before
+  // the queries are converted, so the conversion overlaps their latency.
+  // From here on a copier's only vector-memory operations are its copies.
+  QueryRaw<QFP8, KF4> qraw[RPW];
+  uint32_t wbits[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const size_t row = row0 + min(wr0 + rr, nr - 1);  // clamp: rows past the group reuse a valid row, never written
+    fetch_query<QFP8, KF4>(a, row, n, g, qraw[rr]);
+    wbits[rr] = a.w[row * kIdxHeads + n];
+  }
+  {
+    const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
+    for (int i = tid; i < n_my; i += kThreads) tbl_s[i] = table[blockIdx.x + i * stride];
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // tbl_s ready
+  if (wave < kCopiers) {
+    for (int i = 0; i < kRing - 1 && i < n_my; ++i) issue(i);
+  }
+  i32x8 A[RPW][NT][2];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    hold_query(qraw[rr]);
+    const float head_scale = finish_query(qraw[rr], A[rr]);
+    // head weights with the head's scale folded in: w_s[row][head]
+    if (g == 0) w_s[wr0 + rr][n] = __uint_as_float(wbits[rr] << 16) * head_scale;
+  }
+  __syncthreads();  // w_s ready
+  // the 16 heads this lane reduces (rows 8*(i/4) + 4g + i%4 of the 32x32 tile);
+  // kept in VGPRs for one row per wave, read from LDS otherwise
+  float wv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) wv[i] = w_s[wr0][8 * (i >> 2) + 4 * g + (i & 3)];
+
   auto run = [&](auto role_tag) {
     constexpr WaveRole role = decltype(role_tag)::value;
     // The rows of a wave are taken in groups of G (one or two): a unit of
@@ -324,6 +370,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_s[i % (LAG + 1)][gr][lane]), row_rsrc(gr), off, 0,
                                               0);
     };
+    // FP8 keys pass both scale operands as 0: the compiler then emits the
+    // plain v_mfma_f32_32x32x64_f8f6f4 (no scaling), which overlaps better
+    // with VALU work than the scaled opcode (4% faster prefill scoring, same
+    // results). MXFP4 keys need the scaled opcode for their block scales.
     auto mfma_unit = [&](f32x16(&acc)[G], const i32x8(&Bh)[2], const int (&sb)[2], int gi) {
 #pragma unroll
       for (int r = 0; r < G; ++r) {
@@ -335,7 +385,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             acc[r] = KF4 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[gi * G + r][t][s], Bh[s], acc[r], 0, 4,
                                                                           0, 127, 0, sb[s])
                          : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[gi * G + r][t][s], Bh[s], acc[r], 0, 0,
-                                                                          0, 127, 0, 127);
+                                                                          0, 0, 0, 0);
       }
     };
     // B operands of keys 32h .. 32h+31 of a staged page. MXFP4: lane half
@@ -380,10 +430,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
       }
     };
-    if constexpr (role == kCopier) {
-      wait_vmcnt<0>();  // nothing but the copies is outstanding from here on
-      for (int i = 0; i < kRing - 1 && i < n_my; ++i) issue(i);
-    }
 
     // Software pipeline over units: the MFMAs of one unit run while the
     // VALU epilogue of the unit before it (of this page or, for the first
