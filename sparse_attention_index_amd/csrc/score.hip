@@ -30,7 +30,8 @@
 // branches.
 //
 // The dot products run on v_mfma_f32_32x32x64_f8f6f4 (the scaled form for
-// MXFP4 keys) with the raw key bytes as the B operand (no conversion). Queries enter as E4M3:
+// MXFP4 keys) with the raw key bytes as the B operand (no conversion).
+// Queries enter as E4M3:
 //  * E4M3 queries (prefill chunks) are used as they are, their row scale
 //    applied after the head reduction;
 //  * bf16 queries are split exactly into two E4M3 terms, q * 2^e = hi + lo,
