@@ -80,6 +80,25 @@ def counters_for(kernel_file, workload):
     return None
 
 
+def measured_step_bytes(workload):
+    """HBM bytes of one whole step as rocprofv3 counted them: the sum over every
+    kernel that profiles/hbm_counters.txt lists for the workload, or None if
+    there are none or any kernel's source has changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    total, seen = 0.0, False
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 6 and not line.startswith("#") and parts[1] == workload:
+                if parts[3] != kernel_source_hash([parts[0], "common.h"]):
+                    return None
+                total += float(parts[4]) + float(parts[5])
+                seen = True
+    return total if seen else None
+
+
 def _threads():
     try:
         from threadpoolctl import threadpool_info
@@ -160,6 +179,23 @@ def stage_times(torch, stages, n):
             evs[s].append((e0, e1))
     torch.cuda.synchronize()
     return {s: 1e3 * sum(a.elapsed_time(b) for a, b in v) / n for s, v in evs.items()}
+
+
+def step_hbm_fields(traffic, lens, R, k, kfmt, step_bytes, sec, workload):
+    """The step's algorithmic bytes over its time; the same without the fp32
+    score round trip (written by the scorer, read by the selection); and the
+    rocprofv3-counted bytes of the step's kernels over the same time."""
+    vis = traffic.visible(lens, R)
+    no_rt = step_bytes - 2 * traffic.SCORE_BYTES * sum(vis)
+    meas = measured_step_bytes(workload)
+    return {
+        "bytes": step_bytes,
+        "achieved_GBs": step_bytes / sec / 1e9,
+        "frac": step_bytes / sec / 1e9 / HBM_PEAK_GBS,
+        "frac_without_score_round_trip": no_rt / sec / 1e9 / HBM_PEAK_GBS,
+        "measured_bytes": meas,
+        "measured_frac": None if meas is None else meas / sec / 1e9 / HBM_PEAK_GBS,
+    }
 
 
 def run_decode(args, torch, dsa, traffic, cfg):
@@ -278,8 +314,7 @@ def run_decode(args, torch, dsa, traffic, cfg):
             "launch": "eager" if graph is None else "hip graph",
         },
         "rows_per_s": rows / sec,
-        "step_hbm": {"bytes": step_bytes, "achieved_GBs": step_bytes / sec / 1e9,
-                     "frac": step_bytes / sec / 1e9 / HBM_PEAK_GBS},
+        "step_hbm": step_hbm_fields(traffic, lens, R, k, kfmt, step_bytes, sec, args.workload),
         "stages_us": stage_us,
         "wall_s": wall,
         "roofline": {
