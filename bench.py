@@ -3,17 +3,18 @@
 
 A step is one pass of the whole hot path -- Score (lightning indexer over
 every cached FP8 key), Select (exact top-2048 per query row) and Attend
-(sparse MLA over the selected latent rows) -- for one batch of 16 requests x
-4 verification rows at 32,768 tokens of context each, through the fused
-dsa_decode entry point. Inputs are seeded synthetic tensors resident in HBM;
-several independent input sets are rotated so that successive steps do not
-hit in the 256 MB Infinity Cache.
+(sparse MLA over the selected latent rows) -- through the fused dsa_decode
+entry point. The default batch is the largest decode configuration: 4
+requests x 4 verification rows at 1,048,576 tokens of context each, with
+about 1% of the keys planted along the query direction (+3 sigma). Inputs
+are seeded synthetic tensors resident in HBM; independent input sets are
+rotated so that successive steps do not hit in the 256 MB Infinity Cache.
 
 Prints one JSON line. `value` is context tokens scanned per second (the sum
 of the requests' context lengths per step over the step time); rows/s, the
 whole-step HBM fraction, per-stage times, the roofline of the dominant kernel
-(the indexer scorer: 20 launches replayed from a HIP graph between two events
-on the replay stream) and a float64 CPU oracle baseline are added beside it.
+(the indexer scorer: launches back to back on the current stream between two
+events) and a float64 CPU oracle baseline are added beside it.
 
 `--workload prefill_4096_on_128k` measures a prefill chunk instead (FP8-query
 indexer over the causal history, per-row top-k, sparse MLA prefill) and reports
@@ -44,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200, help="timed steps")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_16x4_32k")
+    ap.add_argument("--workload", default="decode_4x4_1m_planted")
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough to exceed 3x the MALL)")
     ap.add_argument("--eager", action="store_true", help="launch every step from the host instead of a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle baseline (0: skip)")
@@ -99,7 +100,8 @@ def measured_step_bytes(workload):
     return total if seen else None
 
 
-def _threads():
+def _blas_threads():
+    """Threads of numpy's BLAS pool (the oracle's matrix products run there)."""
     try:
         from threadpoolctl import threadpool_info
 
@@ -108,14 +110,28 @@ def _threads():
         return 1
 
 
+def _host_cores():
+    """Cores this process may run on (its CPU affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def _cores_fields():
+    # the oracle is numpy: its matrix products use the BLAS pool, the rest one thread
+    return {"cores": min(_host_cores(), _blas_threads()), "host_cores": _host_cores(),
+            "blas_threads": _blas_threads()}
+
+
 def cpu_baseline(workload_name, budget_s):
     """The float64 oracle (as it stands) on a bounded sample of the same workload."""
     import oracle
-    from workloads import case_config, make_case
+    from workloads import case_config, make_case, structure_kwargs
 
     cfg = case_config(workload_name)
     R, lens = cfg["R"], cfg["lengths"]
-    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query", "key_format")}
+    kw = structure_kwargs(cfg)
     if R > 64:  # prefill chunk: one request, sample its query rows
         case = make_case(1, R, lens[:1], seed=cfg["seed"] + 1000, **kw)
         rows, spent = 0, 0.0
@@ -125,9 +141,9 @@ def cpu_baseline(workload_name, budget_s):
             oracle.dsa_rows(case, rows=[(rows * step) % R])
             spent += time.perf_counter() - t0
             rows += 1
-        return {"value": rows / spent, "unit": "rows/s", "cores": _threads(), "kind": "oracle",
-                "sample": f"{rows} of {R} query rows (spread over the chunk), all stages, numpy float64 "
-                          f"on the host, {spent:.1f} s"}
+        return {"value": rows / spent, "unit": "rows/s", **_cores_fields(), "kind": "oracle",
+                "sample": f"{rows} of {R} query rows (spread over the chunk) of a re-seeded chunk of the same "
+                          f"shape and structure, all stages, numpy float64 on the host, {spent:.1f} s"}
     done, tokens, rows, spent = 0, 0, 0, 0.0
     while done < len(lens) and (spent < budget_s or done == 0):
         case = make_case(1, R, [lens[done]], seed=cfg["seed"] + 1000 + done, **kw)
@@ -141,10 +157,10 @@ def cpu_baseline(workload_name, budget_s):
         "value": tokens / spent,
         "unit": "tokens/s",
         "rows_per_s": rows / spent,
-        "cores": _threads(),
+        **_cores_fields(),
         "kind": "oracle",
-        "sample": f"{done} of {len(lens)} requests ({rows} rows, context {lens[0]}), all stages, "
-                  f"numpy float64 on the host, {spent:.1f} s",
+        "sample": f"{done} of {len(lens)} requests ({rows} rows, context {lens[:done]}), each re-seeded with "
+                  f"the workload's shape and structure, all stages, numpy float64 on the host, {spent:.1f} s",
     }
 
 
@@ -199,7 +215,7 @@ def step_hbm_fields(traffic, lens, R, k, kfmt, step_bytes, sec, workload):
 
 
 def run_decode(args, torch, dsa, traffic, cfg):
-    from workloads import make_case
+    from workloads import make_case, structure_kwargs
 
     B, R, lens = cfg["B"], cfg["R"], cfg["lengths"]
     k = 2048
@@ -210,7 +226,7 @@ def run_decode(args, torch, dsa, traffic, cfg):
     nsets = args.sets or max(2, math.ceil(3 * MALL_BYTES / min(step_bytes, set_bytes)))
     nsets = min(nsets, max(2, int(40e9 // set_bytes)))
 
-    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query", "key_format")}
+    kw = structure_kwargs(cfg)
     cases = [make_case(B, R, lens, seed=cfg["seed"] + 100 * i, device="cuda", name=args.workload, **kw)
              for i in range(nsets)]
     batches = [dsa.Batch.of(c) for c in cases]
@@ -333,11 +349,11 @@ def run_decode(args, torch, dsa, traffic, cfg):
 
 def run_prefill(args, torch, dsa, traffic, cfg):
     """Prefill chunk: FP8-query indexer over the whole causal history, per-row top-k, sparse MLA."""
-    from workloads import make_case
+    from workloads import make_case, structure_kwargs
 
     R, L = cfg["R"], cfg["lengths"][0]
     k = 2048
-    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query", "key_format")}
+    kw = structure_kwargs(cfg)
     case = make_case(1, R, [L], seed=cfg["seed"], device="cuda", name=args.workload, **kw)
     batch, cache = dsa.Batch.of(case), dsa.Cache.of(case)
     ld = (L + 63) // 64 * 64
@@ -495,14 +511,14 @@ def run_dcp(args, torch, dsa, traffic):
     GPU: score -> exact top-k merge over W virtual shards -> per-shard sparse
     MLA + LSE combine. The shards are regions of one device's memory, so this
     measures the merge's and the combine's device work, not the exchanges."""
-    from workloads import case_config, make_case
+    from workloads import case_config, make_case, structure_kwargs
 
     base, W = DCP[args.workload]
     cfg = case_config(base)
     B, R, lens = cfg["B"], cfg["R"], cfg["lengths"]
     k, C = 2048, int(1.5 * 2048 / W)
     rows = B * R
-    kw = {k_: v for k_, v in cfg.items() if k_ in ("permute_blocks", "plant_frac", "fp8_query", "key_format")}
+    kw = structure_kwargs(cfg)
     nsets = 2
     cases = [make_case(B, R, lens, seed=cfg["seed"] + 100 * i, device="cuda", name=base, **kw) for i in range(nsets)]
     batches = [dsa.Batch.of(c) for c in cases]
@@ -606,7 +622,7 @@ def dcp_cpu_baseline(workload_name, budget_s):
         rows += 1
         if rows >= 200:
             break
-    return {"value": rows * L / spent, "unit": "tokens/s", "rows_per_s": rows / spent, "cores": _threads(),
+    return {"value": rows * L / spent, "unit": "tokens/s", "rows_per_s": rows / spent, **_cores_fields(),
             "kind": "oracle",
             "sample": f"{rows} score rows of {L} tokens, merge only (W = {W}), numpy on the host, {spent:.1f} s"}
 
@@ -629,7 +645,7 @@ def key_write_cpu_baseline(workload_name, budget_s):
         reps += 1
         if reps >= 50:
             break
-    return {"value": reps * B * R / spent, "unit": "rows/s", "cores": _threads(), "kind": "oracle",
+    return {"value": reps * B * R / spent, "unit": "rows/s", **_cores_fields(), "kind": "oracle",
             "sample": f"{reps} x {B * R} rows, LayerNorm + quantisation, numpy on the host, {spent:.1f} s"}
 
 

@@ -156,8 +156,16 @@ int32_t dsa_index_key_write(const dsa_batch* batch, const void* k, const float* 
  *   w        bf16 [rows][32] head weights (any sign).
  *   scores   fp32 [rows][ld], ld >= max_ctx. Entries s > position(row) are not
  *            written.
- * Accumulation is fp32; products of bf16 or E4M3 query values with E4M3 or
- * E2M1 key values are exact.
+ * key_scale and q_scale must be positive and finite: they live in device
+ * memory, so the host cannot check them, and the kernels apply them after
+ * the ReLU (ReLU(c x) = c ReLU(x) holds for c > 0 only).
+ * Accumulation is fp32. E4M3 query values times E4M3 or E2M1 key values are
+ * exact products. A bf16 query head enters as two E4M3 terms under one
+ * power-of-two scale that puts the head's largest magnitude m in
+ * (224, 448]; their sum reproduces every element whose magnitude is at
+ * least about m * 2^-10 exactly, and smaller elements to within
+ * m * 2^-10 / 224 (about 4.4e-6 m), so a head's dot product is off by at
+ * most 4.4e-6 * m * sum_d |khat_s[d]|.
  */
 int32_t dsa_index_score(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t q_dtype,
                         const float* q_scale, const void* w, float* scores, int64_t ld, void* stream);
@@ -166,8 +174,8 @@ int32_t dsa_index_score(const dsa_batch* batch, const dsa_cache* cache, const vo
  * Select: per row, the k highest scores among scores[row * ld + 0 .. row_len[row]-1]
  * ("TokenSpeed Kimi K3.1", step 3: a radix top-k keeps the 2,048
  * highest-scoring positions for each query). The selection is exact: ranking
- * is by score (fp32 total order, -0 < +0), ties go to the lower position, so
- * the selected set is unique and identical across runs.
+ * is by fp32 score, -0 ranks equal to +0, and equal scores go to the lower
+ * position, so the selected set is unique and identical across runs.
  *   row_len  device int32 [rows], 0 <= row_len[row] <= ld.
  *   idx      int32 [rows][k]: the selected positions in unspecified order;
  *            if row_len < k the first row_len entries hold every position and
@@ -197,6 +205,11 @@ int32_t dsa_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_
  * num_heads == 16, 1 <= k <= 2048. The decode variant splits each row's k
  * positions over several workgroups and merges them by log-sum-exp; the
  * prefill variant gives each row one workgroup.
+ * The logits use the bf16 query as two E4M3 terms under one power-of-two
+ * scale per head, as the indexer does (see dsa_index_score): elements more
+ * than about 2^10 below the head's largest magnitude m carry an error of at
+ * most about 4.4e-6 m. Probabilities and values multiply in bf16 with fp32
+ * accumulation.
  */
 int32_t dsa_sparse_mla_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t num_heads,
                               const int32_t* idx, int32_t k, float softmax_scale, void* out, float* lse,
@@ -217,10 +230,39 @@ int32_t dsa_sparse_mla_prefill(const dsa_batch* batch, const dsa_cache* cache, c
  *   idx_out  int32 [rows][k] or NULL: receives the selection.
  *   ws       workspace of dsa_workspace_size(DSA_WS_DECODE, rows, max_ctx, k, num_heads)
  *            (holds the fp32 scores, the selection and the attention partials).
+ * Results are the same as dsa_index_score -> dsa_topk -> dsa_sparse_mla_decode
+ * (the same selected set): the scorer stores every score, the top-k kernels
+ * select, and attention reads the selection's cache rows directly.
  */
 int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
                    const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale, void* out,
                    float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_decode with scores filtered inside the scorer against a per-row
+ * threshold the caller gives: the scorer keeps (score, position) of every
+ * score at or above the row's threshold instead of storing every score, and
+ * the k largest of those candidates are selected. The fused indexer of
+ * "vLLM Day-0 Support for Kimi K3.1 Pro", section "Fused low-latency decode
+ * for DSA layers", likewise hands an exact top-k select only what its
+ * scorer keeps. A row whose candidates cannot decide the result (fewer than
+ * k reach the threshold, or more than the buffers hold) is scored again in
+ * full and selected over its whole row, so the selection is always exact.
+ * A good threshold is any value a little below the row's k-th score (for
+ * instance the same request's k-th score at the previous decode step).
+ *   threshold  fp32 [rows], device: the scorer keeps every score >= it. Any
+ *              value works, NaN and +-inf included: too high a threshold
+ *              (fewer than k scores reach it) or too low (more candidates
+ *              than the buffers hold) sends the row to the exact fallback,
+ *              so idx, out and lse are those of dsa_decode whatever it is.
+ * Other arguments and the workspace are dsa_decode's. Returns
+ * DSA_ERR_UNSUPPORTED if a request would need more than 1,024 scoring
+ * workgroups (contexts beyond about 128M tokens).
+ */
+int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                               const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale,
+                               const float* threshold, void* out, float* lse, int32_t* idx_out, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /*
  * Decode context parallelism, simulated on one device. Under DCP, token p of

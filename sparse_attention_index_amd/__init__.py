@@ -286,7 +286,10 @@ def dsa_sparse_mla_prefill(batch, cache, q, idx, softmax_scale, out, lse=None, w
 
 
 def dsa_decode(batch, cache, q_idx, w, q_mla, k, softmax_scale, out, lse=None, idx_out=None, ws=None,
-               stream=None):
+               stream=None, threshold=None):
+    """The whole decode step (score -> select -> attend). With `threshold`
+    (fp32 [rows] on the device) the rows' candidate thresholds are the
+    caller's (dsa_decode_thresholded) instead of sampled; results are the same."""
     rows = batch.rows
     _need(q_idx, "q_idx", _BF16, rows * 32 * 128)
     _need(w, "w", _BF16, rows * 32)
@@ -300,9 +303,12 @@ def dsa_decode(batch, cache, q_idx, w, q_mla, k, softmax_scale, out, lse=None, i
         _need(idx_out, "idx_out", _I32, rows * int(k))
     if ws is not None:
         _need(ws, "ws", (torch.uint8,))
-    st = load().dsa_decode(
-        ctypes.byref(batch.c), ctypes.byref(cache.c), _ptr(q_idx), _ptr(w), _ptr(q_mla), int(q_mla.shape[1]),
-        int(k), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws),
-        int(ws.numel()) if ws is not None else 0, _stream(stream),
-    )
-    _check(st, "dsa_decode")
+    lib = load()
+    head = (ctypes.byref(batch.c), ctypes.byref(cache.c), _ptr(q_idx), _ptr(w), _ptr(q_mla), int(q_mla.shape[1]),
+            int(k), float(softmax_scale))
+    tail = (_ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), int(ws.numel()) if ws is not None else 0, _stream(stream))
+    if threshold is None:
+        _check(lib.dsa_decode(*head, *tail), "dsa_decode")
+    else:
+        _need(threshold, "threshold", _F32, rows)
+        _check(lib.dsa_decode_thresholded(*head, _ptr(threshold), *tail), "dsa_decode_thresholded")

@@ -84,41 +84,58 @@ int32_t check_mla(int32_t num_heads, int32_t k, const void* q, const int32_t* id
 
 int64_t decode_ld(int32_t max_ctx) { return ((int64_t)max_ctx + 63) / 64 * 64; }
 
+// Candidate slots per row of the filtered decode: the sampled threshold
+// leaves about 1.25k to 3.4k of a row's scores plus a margin (at most
+// 12,288 can be selected from), split into one region per scoring workgroup
+// of the row's request; rows of few requests have the most workgroups.
+int32_t filter_cap(int32_t rows) { return rows <= 128 ? 65536 : 16384; }
+
 struct DecodeWs {
-  float* scores;
+  float* scores;   // full scores: the stored path, and the filtered path's fallback
   int32_t* row_len;
   int32_t* idx;
   int32_t* slots;  // physical cache rows of the selection
   void* topk;
   void* mla;
+  float* thr;      // filtered path: per-row score threshold
+  uint32_t* fail;  // filtered path: rows the candidates could not decide
+  uint32_t* fcnt;  // filtered path: [rows][kMaxFilterWg] candidates per scoring workgroup
+  uint2* fcand;    // filtered path: [rows][filter_cap] candidates
 };
 
 size_t decode_ws_parts(int32_t rows, int64_t max_ctx, int32_t k, DecodeWs* out, void* base) {
   const int64_t ld = decode_ld((int32_t)max_ctx);
-  size_t off = 0;
-  const size_t s_scores = align256((size_t)rows * ld * sizeof(float));
-  const size_t s_len = align256((size_t)rows * sizeof(int32_t));
-  const size_t s_idx = align256((size_t)rows * k * sizeof(int32_t));
-  const size_t s_slots = s_idx;
-  const size_t s_topk = align256(topk_ws_bytes(rows, ld));
-  const size_t s_mla = align256(mla_ws_bytes(rows, k, true));
-  if (out) {
-    char* p = static_cast<char*>(base);
-    out->scores = reinterpret_cast<float*>(p + off);
-    off += s_scores;
-    out->row_len = reinterpret_cast<int32_t*>(p + off);
-    off += s_len;
-    out->idx = reinterpret_cast<int32_t*>(p + off);
-    off += s_idx;
-    out->slots = reinterpret_cast<int32_t*>(p + off);
-    off += s_slots;
-    out->topk = p + off;
-    off += s_topk;
-    out->mla = s_mla ? p + off : nullptr;
-    off += s_mla;
-    return off;
+  const size_t sizes[] = {
+      align256((size_t)rows * ld * sizeof(float)),                    // scores
+      align256((size_t)rows * sizeof(int32_t)),                       // row_len
+      align256((size_t)rows * k * sizeof(int32_t)),                   // idx
+      align256((size_t)rows * k * sizeof(int32_t)),                   // slots
+      align256(topk_ws_bytes(rows, ld)),                              // topk
+      align256(mla_ws_bytes(rows, k, true)),                          // mla
+      align256((size_t)rows * sizeof(float)),                         // thr
+      align256((size_t)rows * sizeof(uint32_t)),                      // fail
+      align256((size_t)rows * kMaxFilterWg * sizeof(uint32_t)),       // fcnt
+      align256((size_t)rows * filter_cap(rows) * sizeof(uint2)),      // fcand
+  };
+  size_t total = 0;
+  char* part[10];
+  for (int i = 0; i < 10; ++i) {
+    part[i] = static_cast<char*>(base) + total;
+    total += sizes[i];
   }
-  return s_scores + s_len + s_idx + s_slots + s_topk + s_mla;
+  if (out) {
+    out->scores = reinterpret_cast<float*>(part[0]);
+    out->row_len = reinterpret_cast<int32_t*>(part[1]);
+    out->idx = reinterpret_cast<int32_t*>(part[2]);
+    out->slots = reinterpret_cast<int32_t*>(part[3]);
+    out->topk = part[4];
+    out->mla = sizes[5] ? part[5] : nullptr;
+    out->thr = reinterpret_cast<float*>(part[6]);
+    out->fail = reinterpret_cast<uint32_t*>(part[7]);
+    out->fcnt = reinterpret_cast<uint32_t*>(part[8]);
+    out->fcand = reinterpret_cast<uint2*>(part[9]);
+  }
+  return total;
 }
 
 int32_t run_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows, int32_t k, int32_t* idx,
@@ -249,9 +266,19 @@ int32_t dsa_sparse_mla_prefill(const dsa_batch* batch, const dsa_cache* cache, c
   return mla_entry(false, batch, cache, q, num_heads, idx, k, softmax_scale, out, lse, ws, ws_bytes, stream);
 }
 
-int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                   const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale, void* out, float* lse,
-                   int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+// dsa_decode takes the filtered path (scores filtered into candidates
+// inside the scorer) for batches with max_ctx above this; 0 keeps every
+// batch on the stored-score path. The stored path is the faster one on
+// MI355X at every measured length, because the sampling pass costs more
+// than the score round trip it saves; dsa_decode_thresholded always filters.
+static constexpr int kFilterMinCtx = 0;
+
+// The decode step. thr_in (device, [rows]) set: the filtered path with the
+// caller's thresholds, whatever max_ctx is.
+static int32_t decode_impl(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                           const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale,
+                           const float* thr_in, void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                           void* stream) {
   g_err[0] = 0;
   int32_t r = check_batch(batch);
   if (r) return r;
@@ -267,8 +294,7 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
   decode_ws_parts(rows, batch->max_ctx, k, &p, ws);
   const int64_t ld = decode_ld(batch->max_ctx);
   int32_t* idx = idx_out ? idx_out : p.idx;
-  const TopkWs tw = topk_ws_carve(p.topk, rows, ld);
-  // 1. score
+  const int B = batch->num_requests;
   ScoreArgs a;
   a.q = q_idx;
   a.q_scale = nullptr;
@@ -280,20 +306,76 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
   a.R = batch->rows_per_request;
   a.scores = p.scores;
   a.ld = ld;
-  if ((r = hip_status(launch_index_score(a, batch->num_requests, batch->max_ctx, false, st), "decode score")))
-    return r;
-  // 2. select (the visible lengths are derived on the way), also writing the
-  //    cache rows of the selection so that attention reads no block table
   SlotOut so;
   so.slots = p.slots;
   so.block_table = batch->block_table;
   so.max_blocks = batch->max_blocks;
-  if ((r = hip_status(launch_topk(p.scores, ld, p.row_len, rows, ld, k, idx, tw, st, batch->ctx_len,
-                                  batch->rows_per_request, so),
-                      "decode topk")))
-    return r;
-  // 3. attend
+  const int grid =
+      index_score_grid_x(B, batch->rows_per_request, batch->max_ctx, cache->key_format == DSA_KEY_MXFP4);
+  const bool filtered = (thr_in || (kFilterMinCtx > 0 && batch->max_ctx > kFilterMinCtx)) &&
+                        grid - B + 1 <= kMaxFilterWg;
+  if (thr_in && !filtered) return fail(DSA_ERR_UNSUPPORTED, "too many scoring workgroups per request");
+  if (filtered) {
+    // 1. each row's visible length and threshold (sampled, or the caller's)
+    if ((r = hip_status(launch_sample_threshold(a, rows, k, thr_in, p.thr, p.row_len, st), "decode threshold")))
+      return r;
+    // 2. score, keeping only the candidates at or above the threshold
+    ScoreArgs f = a;
+    f.scores = nullptr;
+    f.thr = p.thr;
+    f.cand = p.fcand;
+    f.cnt = p.fcnt;
+    f.cap = filter_cap(rows);
+    f.cnt_stride = kMaxFilterWg;
+    int gx = 0;
+    if ((r = hip_status(launch_index_score(f, B, batch->max_ctx, false, st, &gx), "decode filtered score")))
+      return r;
+    // 3. exact selection from the candidates; rows they cannot decide are flagged
+    if ((r = hip_status(launch_candidate_select(p.fcand, p.fcnt, f.cap, kMaxFilterWg, gx, batch->ctx_len, B, p.thr,
+                                                p.row_len, rows, batch->rows_per_request, k, idx, p.fail, so, st),
+                        "decode candidate select")))
+      return r;
+    // 4. exact fallback for flagged rows: their full scores, then a whole-row
+    //    selection (both return at once for unflagged rows)
+    ScoreArgs fb = a;
+    fb.row_fail = p.fail;
+    if ((r = hip_status(launch_index_score(fb, B, batch->max_ctx, false, st), "decode fallback score"))) return r;
+    if ((r = hip_status(launch_topk_failed_rows(p.scores, ld, p.row_len, rows, batch->rows_per_request, k, idx,
+                                                p.fail, so, st),
+                        "decode fallback select")))
+      return r;
+  } else {
+    const TopkWs tw = topk_ws_carve(p.topk, rows, ld);
+    // 1. score
+    if ((r = hip_status(launch_index_score(a, B, batch->max_ctx, false, st), "decode score"))) return r;
+    // 2. select (the visible lengths are derived on the way), also writing the
+    //    cache rows of the selection so that attention reads no block table
+    if ((r = hip_status(launch_topk(p.scores, ld, p.row_len, rows, ld, k, idx, tw, st, batch->ctx_len,
+                                    batch->rows_per_request, so),
+                        "decode topk")))
+      return r;
+  }
+  // attend
   return run_mla(batch, cache, q_mla, idx, k, softmax_scale, out, lse, p.mla, true, st, p.slots);
+}
+
+int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                   const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale, void* out, float* lse,
+                   int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(batch, cache, q_idx, w, q_mla, num_heads, k, softmax_scale, nullptr, out, lse, idx_out, ws,
+                     ws_bytes, stream);
+}
+
+int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                               const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale,
+                               const float* threshold, void* out, float* lse, int32_t* idx_out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!threshold) {
+    g_err[0] = 0;
+    return fail(DSA_ERR_INVALID_ARG, "threshold is null");
+  }
+  return decode_impl(batch, cache, q_idx, w, q_mla, num_heads, k, softmax_scale, threshold, out, lse, idx_out, ws,
+                     ws_bytes, stream);
 }
 
 size_t dsa_workspace_size(int32_t kind, int32_t rows, int64_t max_ctx, int32_t k, int32_t num_heads) {

@@ -17,7 +17,8 @@
 //     which spreads both read patterns below over distinct LDS banks;
 //  2. QK: wave w computes the logits of 16 heads x 16 tokens [16w, 16w+16)
 //     with FP8 MFMAs on the raw E4M3 latent (no conversion): the bf16 query
-//     is split exactly into two E4M3 terms with a power-of-two block scale
+//     is split into two E4M3 terms (exact down to ~2^-10 of the head's
+//     largest element) with a power-of-two block scale
 //     per head, once per workgroup, and stays in VGPRs for the whole call;
 //  3. online softmax against a per-head reference shared by all waves: p =
 //     exp(logit - reference). The reference only moves when a logit of the

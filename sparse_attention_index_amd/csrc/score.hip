@@ -34,7 +34,7 @@
 // Queries enter as E4M3:
 //  * E4M3 queries (prefill chunks) are used as they are, their row scale
 //    applied after the head reduction;
-//  * bf16 queries are split exactly into two E4M3 terms, q * 2^e = hi + lo,
+//  * bf16 queries are split into two E4M3 terms, q * 2^e = hi + lo,
 //    with a power-of-two scale 2^e per (row, head) that puts the head's
 //    largest magnitude in (224, 448]. A bf16 value has 8 significant bits
 //    and each E4M3 term carries 4, so hi + lo reproduces it exactly except
@@ -57,6 +57,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace dsa {
 
@@ -214,8 +215,9 @@ DSA_DEV float finish_query(const QueryRaw<QFP8, KF4>& r, i32x8 (&A)[QFP8 ? 1 : 2
 // LDS; waves 0-2 also move the pages into LDS, wave 3 stores the scores.
 enum WaveRole { kCopier, kFlusher };
 
-template <int RPW, bool QFP8, bool KF4>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void score_kernel(ScoreArgs a) {
+template <int RPW, bool QFP8, bool KF4, bool FILT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void score_kernel(ScoreArgs a,
+                                                                                                 int B) {
   constexpr int ROWS = 4 * RPW;
   constexpr int NT = QFP8 ? 1 : 2;  // E4M3 terms per query value
   constexpr int LAG = 2;             // a page's scores are complete two barriers later
@@ -231,7 +233,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 5;   // lane half
   const int n = lane & 31;   // A row (head) / B and D column (key)
-  const int b = blockIdx.y;
+  // this workgroup's request and its place among that request's workgroups
+  // (workgroups are handed out in proportion to the requests' pages)
+  const WgRange wgr = wg_range(a.ctx_len, B, gridDim.x, blockIdx.x, -1);
+  const int b = wgr.b;
   const int R = a.R;
   const int r0 = blockIdx.z * ROWS;           // first row of the group within the request
   const int nr = min(ROWS, R - r0);           // rows of the group that exist
@@ -239,10 +244,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int pos0 = L - R + r0;                // position of the group's first row
   const int blk_lim = ((pos0 + nr - 1) >> 6) + 1;  // pages any row of the group sees
   const size_t row0 = (size_t)b * R + r0;
+  if (a.row_fail) {  // fallback scoring: only groups holding a row the selection could not finish
+    bool any = false;
+    for (int gr = 0; gr < nr; ++gr) any |= a.row_fail[row0 + gr] != 0u;
+    if (!any) return;  // every thread read the same flags
+  }
 
-  // this workgroup's pages: blockIdx.x, +gridDim.x, ... below blk_lim
-  const int stride = gridDim.x;
-  const int n_my = blk_lim > (int)blockIdx.x ? (blk_lim - (int)blockIdx.x + stride - 1) / stride : 0;
+  // this workgroup's pages: jx, jx + stride, ... below blk_lim
+  const int jx = blockIdx.x - wgr.first;
+  const int stride = wgr.count;
+  const int n_my = blk_lim > jx ? (blk_lim - jx + stride - 1) / stride : 0;
   const int wr0 = wave * RPW;
 
   // Score stores go through one buffer descriptor per row whose size is the
@@ -307,9 +318,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     fetch_query<QFP8, KF4>(a, row, n, g, qraw[rr]);
     wbits[rr] = a.w[row * kIdxHeads + n];
   }
+  // filtered decode: each row's threshold, loaded with the queries
+  float thr_f[ROWS];
+#pragma unroll
+  for (int gr = 0; gr < ROWS; ++gr) thr_f[gr] = FILT && gr < nr ? a.thr[row0 + gr] : 0.f;
   {
     const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
-    for (int i = tid; i < n_my; i += kThreads) tbl_s[i] = table[blockIdx.x + i * stride];
+    for (int i = tid; i < n_my; i += kThreads) tbl_s[i] = table[jx + i * stride];
   }
   wait_vmcnt<0>();
   __syncthreads();  // tbl_s ready
@@ -330,6 +345,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   float wv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) wv[i] = w_s[wr0][8 * (i >> 2) + 4 * g + (i & 3)];
+
+  // filtered decode: the workgroup's candidate region per row and its
+  // running counts
+  uint2* fregion[ROWS];
+  uint32_t fcnt[ROWS];
+  const uint32_t fsub = FILT ? (uint32_t)(a.cap / stride) : 0u;
+#pragma unroll
+  for (int gr = 0; gr < ROWS; ++gr) {
+    fcnt[gr] = 0;
+    fregion[gr] = FILT ? a.cand + (row0 + min(gr, nr - 1)) * (size_t)a.cap + (size_t)jx * fsub : nullptr;
+  }
 
   auto run = [&](auto role_tag) {
     constexpr WaveRole role = decltype(role_tag)::value;
@@ -363,13 +389,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int rr = gi * G + (G == 2 ? g : 0);
       if (i >= 0) sc_s[i % (LAG + 1)][wr0 + rr][32 * h + n] = v;
     };
-    // wave 3: store the group's scores of page i (complete once barrier i + LAG passed)
+    // wave 3: store the group's scores of page i (complete once barrier i + LAG passed);
+    // in the filtered decode, keep the (key, position) of each score >= its
+    // row's threshold in this workgroup's region instead (rare: a few per
+    // page at long contexts)
     auto flush = [&](int i) {
-      const uint32_t off = 4u * (uint32_t)(((int)blockIdx.x + i * stride) * kBlock + lane);
+      if constexpr (FILT) {
+        const int p = (jx + i * stride) * kBlock + lane;
 #pragma unroll
-      for (int gr = 0; gr < ROWS; ++gr)  // descriptors rebuilt here: scalar work, no registers held
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_s[i % (LAG + 1)][gr][lane]), row_rsrc(gr), off, 0,
-                                              0);
+        for (int gr = 0; gr < ROWS; ++gr) {
+          if (gr < nr) {
+            const float v = sc_s[i % (LAG + 1)][gr][lane];
+            const bool keep = p <= pos0 + gr && v >= thr_f[gr];
+            const uint64_t m = __ballot(keep);
+            if (m) {
+              const uint32_t slot = fcnt[gr] + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+              if (keep && slot < fsub) fregion[gr][slot] = make_uint2(ordered_key(v), (uint32_t)p);
+              fcnt[gr] += (uint32_t)__popcll(m);
+            }
+          }
+        }
+      } else {
+        const uint32_t off = 4u * (uint32_t)((jx + i * stride) * kBlock + lane);
+#pragma unroll
+        for (int gr = 0; gr < ROWS; ++gr)  // descriptors rebuilt here: scalar work, no registers held
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_s[i % (LAG + 1)][gr][lane]), row_rsrc(gr), off, 0,
+                                                0);
+      }
     };
     // FP8 keys pass both scale operands as 0: the compiler then emits the
     // plain v_mfma_f32_32x32x64_f8f6f4 (no scaling), which overlaps better
@@ -475,19 +522,154 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __syncthreads();  // the last scores are in LDS
     if constexpr (role == kFlusher) {
       for (int i = max(0, n_my - LAG); i < n_my; ++i) flush(i);
+      if constexpr (FILT) {  // this workgroup's true count per row (also past its region)
+#pragma unroll
+        for (int gr = 0; gr < ROWS; ++gr)
+          if (gr < nr && lane == 0) a.cnt[(row0 + gr) * a.cnt_stride + jx] = fcnt[gr];
+      }
     }
   };
   if (wave < kCopiers) run(std::integral_constant<WaveRole, kCopier>{});
   else run(std::integral_constant<WaveRole, kFlusher>{});
 }
 
+// ------------------------------------------------------------------ sampling pass
+
+static constexpr int kSampleThreads = 512;  // 8 waves
+static constexpr int kSamplePpw = 4;        // pages each wave has in flight
+
+// Filtered decode, step 1, one workgroup per query row. The row's visible
+// length n goes to row_len. A row of more than kTakeAll tokens scores
+// ns = 2,048 (n <= 2^18) or 4,096 sampled keys -- ns / 64 whole pages evenly
+// spaced over the pages it sees in full -- with the scorer's arithmetic
+// (the same query split, MFMAs and head-weighted ReLU reduction; the keys go
+// from global memory straight into MFMA operands), and takes the top-k's
+// sampled threshold over those scores (sample_select), written to thr as
+// the float a kept score must reach. Shorter rows keep every score (-inf).
+template <bool KF4>
+__global__ __launch_bounds__(kSampleThreads) void sample_threshold_kernel(ScoreArgs a, int k, const float* thr_in,
+                                                                         float* thr, int32_t* row_len) {
+  constexpr int NT = kSampleThreads, NW = NT / 64, PPW = kSamplePpw;
+  static_assert((2048 / kBlock) % (NW * PPW) == 0, "sampled pages split evenly over the waves");
+  __shared__ float samp[kSample];
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ ScanLds<NT> scan;
+  __shared__ float wsc[NW][kIdxHeads];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, n = lane & 31;
+  const int row = blockIdx.x, R = a.R, b = row / R;
+  const int vis = a.ctx_len[b] - R + row % R + 1;
+  const int64_t nvis = vis > 0 ? vis : 0;
+  if (t == 0) row_len[row] = (int32_t)nvis;
+  if (thr_in) {  // the caller's threshold
+    if (t == 0) thr[row] = thr_in[row];
+    return;
+  }
+  if (nvis <= kTakeAll) {
+    if (t == 0) thr[row] = -INFINITY;
+    return;
+  }
+  const int ns = nvis > (1 << 18) ? 4096 : 2048;
+  const int S = ns / kBlock;              // sampled pages
+  const int full = (int)(nvis / kBlock);  // pages whose 64 keys the row all sees (> 128)
+  const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
+
+  QueryRaw<false, KF4> qraw;
+  fetch_query<false, KF4>(a, row, n, g, qraw);
+  const uint32_t wbits = a.w[(size_t)row * kIdxHeads + n];
+  i32x8 A[2][2];
+  const float head_scale = finish_query(qraw, A);
+  if (g == 0) wsc[wave][n] = __uint_as_float(wbits << 16) * head_scale;
+  __syncthreads();
+  float wv[16];  // the weights of the 16 heads this lane reduces (as in the scorer)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) wv[i] = wsc[wave][8 * (i >> 2) + 4 * g + (i & 3)];
+
+  for (int j0 = wave * PPW; j0 < S; j0 += NW * PPW) {
+    int32_t pid[PPW];
+#pragma unroll
+    for (int q = 0; q < PPW; ++q) pid[q] = table[(int64_t)(j0 + q) * full / S];
+    // B operands of keys 32h + n (lane half g, step s: dims 64g + 32s + [0, 32);
+    // MXFP4: the 16-byte MX block 2g + s and its E8M0 scale) and key scales
+    i32x8 Bk[PPW][2][2];
+    int SB[PPW][2][2];
+    float ks[PPW][2];
+#pragma unroll
+    for (int q = 0; q < PPW; ++q) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const size_t key = (size_t)pid[q] * kBlock + 32 * h + n;
+        if constexpr (KF4) {
+          const uint8_t* kp = a.key_fp4 + key * (kIdxDim / 2);
+          const uint32_t sw = *reinterpret_cast<const uint32_t*>(a.key_e8m0 + key * 4);
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(kp + 16 * (2 * g + st));
+            Bk[q][h][st] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+            SB[q][h][st] = (int)((sw >> (8 * (2 * g + st))) & 0xffu);
+          }
+          ks[q][h] = 1.f;
+        } else {
+          const uint8_t* kp = a.key_fp8 + key * kIdxDim + 64 * g;
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kp + 32 * st);
+            const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kp + 32 * st + 16);
+            Bk[q][h][st] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                                 (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+            SB[q][h][st] = 127;
+          }
+          ks[q][h] = a.key_scale[key];
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PPW; ++q) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            acc = KF4 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[tt][st], Bk[q][h][st], acc, 0, 4, 0, 127,
+                                                                       0, SB[q][h][st])
+                      : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[tt][st], Bk[q][h][st], acc, 0, 0, 0, 0,
+                                                                       0, 0);
+        float sum = 0.f;
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) sum = __builtin_fmaf(wv[i2], relu(acc[i2]), sum);
+        const float v = halves_sum_pair(sum, sum) * ks[q][h];
+        if (g == 0) samp[(j0 + q) * kBlock + 32 * h + n] = v;
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t raw[kSample / NT];
+#pragma unroll
+  for (int i = 0; i < kSample / NT; ++i) raw[i] = t + NT * i < ns ? __float_as_uint(samp[t + NT * i]) : 0u;
+  const uint32_t T = sample_select<NT>(raw, nvis, k, hist, scan);
+  if (t == 0) thr[row] = key_threshold_float(T);
+}
+
+hipError_t launch_sample_threshold(const ScoreArgs& a, int rows, int k, const float* thr_in, float* thr,
+                                   int32_t* row_len, hipStream_t st) {
+  if (a.key_fp4)
+    hipLaunchKernelGGL(sample_threshold_kernel<true>, dim3(rows), dim3(kSampleThreads), 0, st, a, k, thr_in, thr,
+                       row_len);
+  else
+    hipLaunchKernelGGL(sample_threshold_kernel<false>, dim3(rows), dim3(kSampleThreads), 0, st, a, k, thr_in, thr,
+                       row_len);
+  return hipGetLastError();
+}
+
 // Workgroups of a variant that fit one CU at once (registers, LDS), from
 // the runtime's occupancy calculator; computed once per variant.
-template <int RPW, bool QFP8, bool KF4>
+template <int RPW, bool QFP8, bool KF4, bool FILT>
 static int resident_per_cu() {
   static const int n = [] {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, score_kernel<RPW, QFP8, KF4>, kThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, score_kernel<RPW, QFP8, KF4, FILT>, kThreads, 0) !=
+            hipSuccess ||
         v < 1)
       v = 1;
     return v;
@@ -507,41 +689,62 @@ static int cu_count() {
   return n;
 }
 
-template <int RPW, bool QFP8, bool KF4>
-static void launch_variant(const ScoreArgs& a, int B, int max_ctx, hipStream_t st) {
+// Workgroups per row group: one round of resident workgroups over the whole
+// grid, at least one per request, none past kMaxWgPages pages (each gets at
+// most about B * max_blk / (G - B) pages) and about two pages each at least.
+template <int RPW, bool QFP8, bool KF4, bool FILT>
+static long long grid_x(int B, int R, int max_ctx) {
+  const int groups = (R + 4 * RPW - 1) / (4 * RPW);
+  const long long max_blk = (max_ctx + kBlock - 1) / kBlock;
+  const long long slots = (long long)resident_per_cu<RPW, QFP8, KF4, FILT>() * cu_count();
+  long long G = slots / groups;
+  const long long most = (long long)B * ((max_blk + 1) / 2);
+  if (G > most) G = most;
+  const long long least = (long long)B + ((long long)B * max_blk + kMaxWgPages - 1) / kMaxWgPages;
+  if (G < least) G = least;
+  return G;
+}
+
+template <int RPW, bool QFP8, bool KF4, bool FILT>
+static void launch_variant(const ScoreArgs& a, int B, int max_ctx, hipStream_t st, int* gx) {
   const int groups = (a.R + 4 * RPW - 1) / (4 * RPW);
-  const int max_blk = (max_ctx + kBlock - 1) / kBlock;
-  // One round of resident workgroups over the whole grid, at least 2 pages
-  // each, and no workgroup past kMaxWgPages.
-  const long long slots = (long long)resident_per_cu<RPW, QFP8, KF4>() * cu_count();
-  long long per_req = (slots + (long long)B * groups - 1) / ((long long)B * groups);
-  const long long cap = (max_blk + 1) / 2;
-  if (per_req > cap) per_req = cap;
-  if (per_req < 1) per_req = 1;
-  const long long need = (max_blk + kMaxWgPages - 1) / kMaxWgPages;
-  if (per_req < need) per_req = need;
-  hipLaunchKernelGGL((score_kernel<RPW, QFP8, KF4>), dim3((unsigned)per_req, B, groups), dim3(kThreads), 0, st, a);
+  const long long G = grid_x<RPW, QFP8, KF4, FILT>(B, a.R, max_ctx);
+  if (gx) *gx = (int)G;
+  hipLaunchKernelGGL((score_kernel<RPW, QFP8, KF4, FILT>), dim3((unsigned)G, 1, groups), dim3(kThreads), 0, st, a,
+                     B);
 }
 
 template <bool KF4>
-static void launch_format(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st) {
+static void launch_format(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st, int* gx) {
   // Rows per wave: one for decode-sized requests; more when a request brings
   // many FP8 query rows (prefill chunks), so that more rows share each page.
   if (q_fp8) {
-    if (a.R > 16) launch_variant<4, true, KF4>(a, B, max_ctx, st);
-    else if (a.R > 4) launch_variant<2, true, KF4>(a, B, max_ctx, st);
-    else launch_variant<1, true, KF4>(a, B, max_ctx, st);
+    if (a.R > 16) launch_variant<4, true, KF4, false>(a, B, max_ctx, st, gx);
+    else if (a.R > 4) launch_variant<2, true, KF4, false>(a, B, max_ctx, st, gx);
+    else launch_variant<1, true, KF4, false>(a, B, max_ctx, st, gx);
+  } else if (a.cand) {  // filtered decode
+    if (a.R > 4) launch_variant<2, false, KF4, true>(a, B, max_ctx, st, gx);
+    else launch_variant<1, false, KF4, true>(a, B, max_ctx, st, gx);
   } else {
     // up to 8 verification rows read each page once
-    if (a.R > 4) launch_variant<2, false, KF4>(a, B, max_ctx, st);
-    else launch_variant<1, false, KF4>(a, B, max_ctx, st);
+    if (a.R > 4) launch_variant<2, false, KF4, false>(a, B, max_ctx, st, gx);
+    else launch_variant<1, false, KF4, false>(a, B, max_ctx, st, gx);
   }
 }
 
-hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st) {
-  if (a.key_fp4) launch_format<true>(a, B, max_ctx, q_fp8, st);
-  else launch_format<false>(a, B, max_ctx, q_fp8, st);
+hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st, int* gx) {
+  if (a.key_fp4) launch_format<true>(a, B, max_ctx, q_fp8, st, gx);
+  else launch_format<false>(a, B, max_ctx, q_fp8, st, gx);
   return hipGetLastError();
+}
+
+template <bool KF4>
+static int filter_grid_x(int B, int R, int max_ctx) {
+  return (int)(R > 4 ? grid_x<2, false, KF4, true>(B, R, max_ctx) : grid_x<1, false, KF4, true>(B, R, max_ctx));
+}
+
+int index_score_grid_x(int B, int R, int max_ctx, bool mxfp4) {
+  return mxfp4 ? filter_grid_x<true>(B, R, max_ctx) : filter_grid_x<false>(B, R, max_ctx);
 }
 
 }  // namespace dsa

@@ -29,13 +29,11 @@
 //          The sample only decides the speed, never the result.
 #include "common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace dsa {
 
 static constexpr int kTF = 1024;         // threads per final workgroup
-static constexpr int kSample = 4096;     // most scores sampled per row
-static constexpr int kRunLen = 128;      // ... in evenly spaced runs of this length
-static constexpr int kTakeAll = 8192;    // rows up to this length keep every element
 static constexpr int kFinalLds = 12288;  // candidates the final kernel holds in LDS
 static constexpr int kMaxSlices = 64;    // filter workgroups per row at most
 
@@ -72,309 +70,6 @@ TopkWs topk_ws_carve(void* ws, int rows, int64_t max_len) {
   w.cand = reinterpret_cast<uint2*>(p);
   w.cap = cand_cap(rows);
   return w;
-}
-
-// ------------------------------------------------------------------ helpers
-
-// Cross-lane moves through DPP (a VALU operand modifier, a few cycles) rather
-// than ds_bpermute (an LDS round trip of ~300 cycles): lanes whose source is
-// outside the pattern, or whose row is masked off, read 0.
-template <int CTRL, int ROW_MASK = 0xf>
-DSA_DEV uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, true);
-}
-constexpr int kDppXor1 = 0xb1;         // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4e;         // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;  // lane 7 - i within each 8
-constexpr int kDppMirror = 0x140;      // lane 15 - i within each 16
-constexpr int kDppShr1 = 0x111;        // row_shr:n = 0x110 + n
-constexpr int kDppBcast15 = 0x142;     // lane 15 of each row -> the next row
-constexpr int kDppBcast31 = 0x143;     // lane 31 -> rows 2 and 3
-
-// Inclusive prefix sum over the 64 lanes (Hillis-Steele inside rows of 16,
-// then the row totals carried across with the row broadcasts).
-DSA_DEV uint32_t wave_incl_sum(uint32_t x) {
-  x += dpp<kDppShr1>(x);
-  x += dpp<kDppShr1 + 1>(x);
-  x += dpp<kDppShr1 + 3>(x);
-  x += dpp<kDppShr1 + 7>(x);
-  x += dpp<kDppBcast15, 0xa>(x);
-  x += dpp<kDppBcast31, 0xc>(x);
-  return x;
-}
-
-// 64-bit value of lane ^ 1, ^ 2 or the mirrored lane, one DPP move per half.
-template <int CTRL>
-DSA_DEV uint64_t dpp64(uint64_t v) {
-  return ((uint64_t)dpp<CTRL>((uint32_t)(v >> 32)) << 32) | dpp<CTRL>((uint32_t)v);
-}
-
-// Max over the wave, returned in every lane (uniform).
-DSA_DEV uint32_t wave_max32(uint32_t v) {
-  v = max(v, dpp<kDppXor1>(v));
-  v = max(v, dpp<kDppXor2>(v));
-  v = max(v, dpp<kDppHalfMirror>(v));
-  v = max(v, dpp<kDppMirror>(v));
-  return max(max((uint32_t)__builtin_amdgcn_readlane(v, 0), (uint32_t)__builtin_amdgcn_readlane(v, 16)),
-             max((uint32_t)__builtin_amdgcn_readlane(v, 32), (uint32_t)__builtin_amdgcn_readlane(v, 48)));
-}
-
-// Min and max over the wave, returned in every lane (uniform).
-DSA_DEV void wave_minmax64(uint64_t& lo, uint64_t& hi) {
-#define DSA_MINMAX_STEP(CTRL)                       \
-  {                                                 \
-    const uint64_t a = dpp64<CTRL>(lo), b = dpp64<CTRL>(hi); \
-    lo = a < lo ? a : lo;                           \
-    hi = b > hi ? b : hi;                           \
-  }
-  DSA_MINMAX_STEP(kDppXor1)
-  DSA_MINMAX_STEP(kDppXor2)
-  DSA_MINMAX_STEP(kDppHalfMirror)
-  DSA_MINMAX_STEP(kDppMirror)
-#undef DSA_MINMAX_STEP
-  // every lane of a row now holds the row's result; combine the four rows
-  uint64_t l = ~0ull, h = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint64_t a = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(lo >> 32), 16 * r) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((uint32_t)lo, 16 * r);
-    const uint64_t b = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(hi >> 32), 16 * r) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((uint32_t)hi, 16 * r);
-    l = a < l ? a : l;
-    h = b > h ? b : h;
-  }
-  lo = l;
-  hi = h;
-}
-
-// Append the predicated lanes of a wave to a counter (LDS or global); returns
-// each predicated lane's slot. One atomic per wave.
-DSA_DEV uint32_t wave_append(uint32_t* counter, bool pred) {
-  const uint64_t mask = __ballot(pred);
-  if (mask == 0) return 0;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((unsigned long long)mask) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-  base = __builtin_amdgcn_readlane(base, leader);
-  const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-  return base + below;
-}
-
-// Exclusive prefix of small per-lane counts (below 2^BITS) over the wave,
-// from BITS bit-sliced ballots (no LDS traffic); total is the wave sum.
-template <int BITS = 5>
-DSA_DEV uint32_t wave_prefix_small(uint32_t cnt, uint32_t& total) {
-  uint32_t pre = 0, tot = 0;
-#pragma unroll
-  for (int bit = 0; bit < BITS; ++bit) {
-    const uint64_t m = __ballot((cnt >> bit) & 1u);
-    pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << bit;
-    tot += (uint32_t)__popcll(m) << bit;
-  }
-  total = tot;
-  return pre;
-}
-
-// One atomic per wave reserves `total` consecutive slots; all lanes get the base.
-DSA_DEV uint32_t wave_reserve(uint32_t* counter, uint32_t total) {
-  uint32_t base = 0;
-  if (total != 0) {
-    if ((threadIdx.x & 63) == 0) base = atomicAdd(counter, total);
-    base = __builtin_amdgcn_readfirstlane(base);
-  }
-  return base;
-}
-
-struct Thresh {
-  int digit;       // the bin holding the need-th largest element
-  uint32_t above;  // elements in bins strictly above it
-  uint32_t at;     // elements in that bin
-};
-
-template <int NT>
-struct ScanLds {
-  uint32_t wsum[NT / 64];
-  uint32_t res[3];
-};
-
-// Thread t of NT owns bins [B t, B t + B) (B = 2048 / NT) with counts c[];
-// need >= 1 and at most the total. Finds d with count(bins > d) < need <=
-// count(bins >= d). Two barriers.
-template <int NT>
-DSA_DEV Thresh block_threshold(const uint32_t (&c)[kHistBins / NT], uint32_t need, ScanLds<NT>& s) {
-  constexpr int B = kHistBins / NT;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < B; ++i) mine += c[i];
-  const uint32_t pre = wave_incl_sum(mine);
-  const uint32_t wtot = __builtin_amdgcn_readlane(pre, 63);
-  if (lane == 0) s.wsum[wave] = wtot;
-  if (t == 0) s.res[0] = s.res[1] = s.res[2] = 0;
-  __syncthreads();
-  // bins of the later lanes of this wave, plus the later waves' totals (lane
-  // w < NT / 64 reads wave w's total: one LDS read per lane)
-  const uint32_t later = (lane < NT / 64 && lane > wave) ? s.wsum[lane] : 0u;
-  uint32_t above = wtot - pre + __builtin_amdgcn_readlane(wave_incl_sum(later), 63);
-  if (above < need && need <= above + mine) {
-#pragma unroll
-    for (int i = B - 1; i >= 0; --i) {
-      if (above < need && need <= above + c[i]) {
-        s.res[0] = B * t + i;
-        s.res[1] = above;
-        s.res[2] = c[i];
-      }
-      above += c[i];
-    }
-  }
-  __syncthreads();
-  // No barrier after this read: every caller passes at least two more
-  // barriers before the next call clears res.
-  return Thresh{(int)s.res[0], s.res[1], s.res[2]};
-}
-
-// Bins of an 11-bit digit: thread t reads its counters.
-template <int NT>
-DSA_DEV void load_bins(const uint32_t* hist, uint32_t (&c)[kHistBins / NT]) {
-  constexpr int B = kHistBins / NT;
-#pragma unroll
-  for (int i = 0; i < B; ++i) c[i] = hist[B * threadIdx.x + i];
-}
-
-DSA_DEV uint64_t composite(uint32_t key, uint32_t pos) { return ((uint64_t)key << 32) | (uint64_t)(~pos); }
-
-template <int NT>
-struct MinMaxLds {
-  uint64_t lo[NT / 64];
-  uint64_t hi[NT / 64];
-};
-
-// Workgroup-wide (min, max) of one value per thread; one barrier pair.
-template <int NT>
-DSA_DEV void block_minmax(uint64_t& lo, uint64_t& hi, MinMaxLds<NT>& s) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  wave_minmax64(lo, hi);
-  if (lane == 0) {
-    s.lo[wave] = lo;
-    s.hi[wave] = hi;
-  }
-  __syncthreads();
-  // lane w < NT / 64 takes wave w's result; one more wave reduction
-  lo = lane < NT / 64 ? s.lo[lane] : ~0ull;
-  hi = lane < NT / 64 ? s.hi[lane] : 0ull;
-  wave_minmax64(lo, hi);
-  __syncthreads();
-}
-
-// ------------------------------------------------------------------ filter
-
-// Visible length of a row: from row_len, or derived in the fused decode.
-// Clamped to [0, ld], so that a length beyond the row's storage never turns
-// into an out-of-bounds read.
-DSA_DEV int64_t visible_len(const int32_t* row_len, const int32_t* ctx_len, int R, int row, int64_t ld) {
-  const int64_t n = ctx_len ? (int64_t)ctx_len[row / R] - R + row % R + 1 : (int64_t)row_len[row];
-  return n < 0 ? 0 : (n > ld ? ld : n);
-}
-
-// Sampled threshold of a row (the same in every workgroup of it), in two
-// parts so that a caller can issue other loads in between.
-// sample_load: ns samples (2048, or 4096 past 256K elements); sample j
-// (thread t of NT takes j = t + NT i) is element (j % 128) of run j / 128, the
-// runs evenly spaced over the row.
-template <int NT>
-DSA_DEV void sample_load(const float* __restrict__ s, int64_t n, uint32_t (&raw)[kSample / NT]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < kSample / NT; ++i) raw[i] = 0u;
-  if (n <= kTakeAll) return;  // no samples needed (uniform)
-  const int ns = n > (1 << 18) ? 4096 : 2048;
-  const int per = ns / NT;
-  // Run r starts at floor(r span / d), span = n - 128, d = runs - 1 (31 or
-  // 15) = r q + floor(r rem / d) with q, rem = span divided by d, computed
-  // once; r rem < d^2 takes a constant-divisor 32-bit division (a 64-bit
-  // division by a variable would be a long software routine per sample).
-  // Every load is issued before any is used: the raw bits are converted to
-  // keys where they are first needed.
-  const uint32_t span = (uint32_t)(n - kRunLen);  // rows are shorter than 2^31
-  const bool wide = ns == 4096;
-  const uint32_t q = wide ? span / 31u : span / 15u;
-  const uint32_t rem = span - q * (wide ? 31u : 15u);
-#pragma unroll
-  for (int i = 0; i < kSample / NT; ++i) {
-    const uint32_t j = (uint32_t)(t + NT * i);
-    const uint32_t r = j / kRunLen;
-    const uint32_t start = r * q + (wide ? (r * rem) / 31u : (r * rem) / 15u);
-    const size_t pos = i < per ? (size_t)start + j % kRunLen : 0;  // extra slots re-read position 0
-    raw[i] = __float_as_uint(s[pos]);
-  }
-}
-
-// sample_select: the ordered-key threshold T from the samples; every element
-// is kept (T = 0) for rows of at most kTakeAll elements.
-template <int NT>
-DSA_DEV uint32_t sample_select(const uint32_t (&raw)[kSample / NT], int64_t n, int k, uint32_t* hist,
-                               ScanLds<NT>& scan) {
-  const int t = threadIdx.x;
-  if (n <= kTakeAll) return 0u;
-  const int ns = n > (1 << 18) ? 4096 : 2048;
-  const int per = ns / NT;
-  uint32_t key[kSample / NT];
-#pragma unroll
-  for (int i = 0; i < kSample / NT; ++i) key[i] = ordered_key(__uint_as_float(raw[i]));
-  // Rank m of the threshold among the samples: the samples expected above
-  // the k-th score of the row (e = k ns / n) times 1.25, plus 3 standard
-  // deviations of that count (sqrt e) and 8, so that a threshold above the
-  // k-th score (too few candidates) stays below about one in a million.
-  const double e = (double)k * ns / (double)n;
-  uint32_t m = (uint32_t)(1.25 * e + 3.0 * __builtin_sqrt(e)) + 8u;
-  if (m > (uint32_t)ns) m = ns;
-  // 11-bit radix steps that start just below the prefix every sample shares
-  // (from their min and max, so that the first step spreads over its bins):
-  // T is the lower edge of the bin that holds the m-th largest sample, once
-  // the bin is at most 2^10 keys wide.
-  const int lane = t & 63, wave = t >> 6;
-  uint32_t lo = ~0u, hi = 0u;
-#pragma unroll
-  for (int i = 0; i < kSample / NT; ++i)
-    if (i < per) {
-      lo = min(lo, key[i]);
-      hi = max(hi, key[i]);
-    }
-  lo = ~wave_max32(~lo);
-  hi = wave_max32(hi);
-  if (lane == 0) {
-    hist[wave] = lo;
-    hist[NT / 64 + wave] = hi;
-  }
-  __syncthreads();
-  lo = ~wave_max32(lane < NT / 64 ? ~hist[lane] : 0u);
-  hi = wave_max32(lane < NT / 64 ? hist[NT / 64 + lane] : 0u);
-  __syncthreads();  // the extremes are read before the histogram is cleared
-  if (lo == hi) return hi;  // every sample has the same key (uniform branch)
-  int shift = 32 - __clz((int)(lo ^ hi));  // bits below the shared prefix
-  uint32_t prefix = shift == 32 ? 0u : hi >> shift;
-  while (true) {  // uniform trip count
-    const int width = shift < 11 ? shift : 11;
-    const int lo_bit = shift - width;
-    for (int i = t; i < kHistBins; i += NT) hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kSample / NT; ++i)
-      if (i < per && (shift == 32 || (key[i] >> shift) == prefix))
-        atomicAdd(&hist[(key[i] >> lo_bit) & ((1u << width) - 1)], 1u);
-    __syncthreads();
-    uint32_t c[kHistBins / NT];
-    load_bins<NT>(hist, c);
-    const Thresh th = block_threshold<NT>(c, m, scan);
-    m -= th.above;
-    prefix = (shift == 32 ? 0u : prefix << width) | (uint32_t)th.digit;
-    shift = lo_bit;
-    if (shift <= 10) return prefix << shift;
-    // (every thread read its bins before block_threshold's first barrier, so
-    // the next clear is safe)
-  }
 }
 
 // ------------------------------------------------------------------ final
@@ -568,13 +263,6 @@ struct ShortLds {
   uint2 elems[kFinalLds + 1];       // survivors, plus one spare entry taking overflow writes
 };
 
-// key >= T as a float comparison (scores are not NaN): T is the lower edge of
-// a bin holding a sampled score, so its float is a number unless T lies below
-// every number's key, where every score passes.
-DSA_DEV float key_threshold_float(uint32_t T) {
-  return T <= ordered_key(-INFINITY) ? -INFINITY : __uint_as_float((T & 0x80000000u) ? (T & 0x7fffffffu) : ~T);
-}
-
 template <bool VEC>
 __global__ __launch_bounds__(kTF) void topk_short_kernel(const float* __restrict__ scores, int64_t ld,
                                                        int32_t* __restrict__ row_len, const int32_t* ctx_len, int R,
@@ -764,6 +452,21 @@ __global__ __launch_bounds__(kT) void topk_slice_kernel(const float* __restrict_
   for (int64_t base = s0; base < s1; base += 4096) {
     const bool whole = base + 4096 <= s1;  // uniform: no position test needed
     const int64_t wbase = base + 1024 * wave + 4 * lane;
+    if (VEC && !whole && (s1 & 3)) {
+      // The 16-byte load of the vector that crosses the slice's end (only
+      // the row's last slice ends off a multiple of 4) may return zeros for
+      // its in-range scores too: the one lane holding it reads them again
+      // one by one.
+      const int64_t vs = s1 & ~(int64_t)3;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (wbase + 256 * q == vs) {
+#pragma unroll
+          for (int e = 0; e < 3; ++e)
+            if (vs + e < s1) cur[4 * q + e] = s[vs + e];
+        }
+      }
+    }
     uint32_t cmask = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -797,6 +500,40 @@ __global__ __launch_bounds__(kT) void topk_slice_kernel(const float* __restrict_
   }
 }
 
+// Rows of at most k visible positions: all of them, then -1 padding (and
+// their physical slots when asked for).
+DSA_DEV void emit_all_positions(int row, int R, int64_t n, int k, int32_t* out, const SlotOut& so) {
+  const int t = threadIdx.x;
+  for (int64_t i = t; i < k; i += kTF) out[i] = i < n ? (int32_t)i : -1;
+  if (so.slots) {
+    const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
+    for (int i = t; i < k; i += kTF)
+      so.slots[(size_t)row * k + i] = i < n && (i >> 6) < so.max_blocks ? table[i >> 6] * kBlock + (i & 63) : -1;
+  }
+}
+
+// Physical slots of a row's written selection (rows this long have too many
+// pages to stage their table in LDS): every thread translates its entries
+// with all its loads in flight. The caller makes `out` workgroup-visible.
+DSA_DEV void emit_slots(int row, int R, int k, const int32_t* out, const SlotOut& so) {
+  const int t = threadIdx.x;
+  const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
+  constexpr int kPer = (kMaxTopk + kTF - 1) / kTF;
+  int32_t pos[kPer], page[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = t + j * kTF;
+    pos[j] = i < k ? out[i] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) page[j] = pos[j] >= 0 && (pos[j] >> 6) < so.max_blocks ? table[pos[j] >> 6] : -1;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = t + j * kTF;
+    if (i < k) so.slots[(size_t)row * k + i] = page[j] >= 0 ? page[j] * kBlock + (pos[j] & 63) : -1;
+  }
+}
+
 // One workgroup per row gathers the slices' survivors (a kernel boundary
 // orders the slice workgroups' writes before these reads; a device-scope fence
 // per workgroup would write back each XCD's L2). Every survivor lies in
@@ -811,12 +548,7 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
   const int64_t n = visible_len(row_len, nullptr, 1, row, ld);  // published by the slice pass
   int32_t* out = idx + (size_t)row * k;
   if (n <= k) {  // every visible position is selected; the rest is padding
-    for (int64_t i = t; i < k; i += kTF) out[i] = i < n ? (int32_t)i : -1;
-    if (so.slots) {
-      const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
-      for (int i = t; i < k; i += kTF)
-        so.slots[(size_t)row * k + i] = i < n && (i >> 6) < so.max_blocks ? table[i >> 6] * kBlock + (i & 63) : -1;
-    }
+    emit_all_positions(row, R, n, k, out, so);
     return;
   }
   const Emit emit{out, nullptr, nullptr};
@@ -870,27 +602,144 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
     const float* s = scores + (size_t)row * ld;
     select_top(L.s, n, k, emit, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
   }
-  // physical slots of the selection (rows of this length have too many pages
-  // to stage their table in LDS): every thread translates its entries with
-  // all its loads in flight
   if (so.slots) {
     __syncthreads();  // the selection is written (workgroup-visible)
-    const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
-    constexpr int kPer = (kMaxTopk + kTF - 1) / kTF;
-    int32_t pos[kPer], page[kPer];
+    emit_slots(row, R, k, out, so);
+  }
+}
+
+// ------------------------------------------------------------------ filtered decode
+
+// The decode scorer (filter mode) leaves, per row and scoring workgroup, the
+// (ordered key, position) of every score >= the row's sampled threshold T in
+// the workgroup's own region of the row's candidate buffer, with its true
+// count. One workgroup per row here gathers them into LDS and selects the k
+// largest composites. The selection is exact whenever no region overflowed
+// and at least k candidates arrived: the k-th largest score is then >= T, so
+// every element of the top k was kept. Otherwise the row is flagged for the
+// fallback (whole-row scoring and selection) and nothing else is written.
+struct CandLds {
+  SelectLds s;
+  uint32_t off[kMaxFilterWg];
+  uint32_t wsum[kTF / 64];
+  uint32_t wmax[kTF / 64];
+  uint2 elems[kFinalLds];
+};
+
+__global__ __launch_bounds__(kTF) void candidate_select_kernel(const uint2* __restrict__ cand,
+                                                               const uint32_t* __restrict__ cnt, int cap,
+                                                               int cnt_stride, const int32_t* __restrict__ ctx_len,
+                                                               int B, int G, const float* __restrict__ thr,
+                                                               const int32_t* __restrict__ row_len, int R, int k,
+                                                               int32_t* __restrict__ idx, uint32_t* row_fail,
+                                                               SlotOut so) {
+  __shared__ CandLds L;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int row = blockIdx.x;
+  const int64_t n = row_len[row];  // published by the sampling pass
+  int32_t* out = idx + (size_t)row * k;
+  if (n <= k) {  // every visible position is selected; the rest is padding
+    emit_all_positions(row, R, n, k, out, so);
+    if (t == 0) row_fail[row] = 0u;
+    return;
+  }
+  // the scoring workgroups of this row's request, as the scorer split them
+  const WgRange wr = wg_range(ctx_len, B, G, 0, row / R);
+  const int nw = wr.count;  // <= kMaxFilterWg (checked by the host)
+  const uint32_t sub = (uint32_t)(cap / nw);
+  const uint32_t c = t < nw ? cnt[(size_t)row * cnt_stride + t] : 0u;
+  const uint32_t incl = wave_incl_sum(c);
+  if (lane == 63) L.wsum[wave] = incl;
+  const int bad = __syncthreads_or(c > sub);
+  uint32_t before = 0, total = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = t + j * kTF;
-      pos[j] = i < k ? out[i] : -1;
+  for (int w = 0; w < kTF / 64; ++w) {
+    const uint32_t x = L.wsum[w];
+    before += w < wave ? x : 0u;
+    total += x;
+  }
+  if (t < nw) L.off[t] = before + incl - c;
+  // every candidate v has v >= thr, so its key is >= ordered_key(thr)
+  const uint32_t T = ordered_key(thr[row]);
+  __syncthreads();
+  const bool ok = !bad && total >= (uint32_t)k && total <= (uint32_t)kFinalLds;
+  if (t == 0) row_fail[row] = ok ? 0u : 1u;
+  if (!ok) return;  // uniform
+  // element i sits in the last workgroup region whose offset is <= i; eight
+  // loads in flight per lane
+  const uint2* base = cand + (size_t)row * cap;
+  uint32_t kmax = 0;
+  for (uint32_t b0 = 0; b0 < total; b0 += 8 * kTF) {
+    uint2 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t i = b0 + t + j * kTF;
+      v[j] = make_uint2(0u, 0u);
+      if (i < total) {
+        int sl = 0;
+#pragma unroll
+        for (int step = kMaxFilterWg / 2; step >= 1; step >>= 1)
+          if (sl + step < nw && L.off[sl + step] <= i) sl += step;
+        v[j] = base[(size_t)sl * sub + (i - L.off[sl])];
+      }
     }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) page[j] = pos[j] >= 0 && (pos[j] >> 6) < so.max_blocks ? table[pos[j] >> 6] : -1;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = t + j * kTF;
-      if (i < k) so.slots[(size_t)row * k + i] = page[j] >= 0 ? page[j] * kBlock + (pos[j] & 63) : -1;
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t i = b0 + t + j * kTF;
+      if (i < total) {
+        L.elems[i] = v[j];
+        kmax = max(kmax, v[j].x);
+      }
     }
   }
+  const uint32_t wm = wave_max32(kmax);
+  if (lane == 0) L.wmax[wave] = wm;
+  __syncthreads();
+  kmax = wave_max32(lane < kTF / 64 ? L.wmax[lane] : 0u);
+  const Emit emit{out, nullptr, nullptr};
+  select_top(
+      L.s, total, k, emit, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); }, true,
+      (uint64_t)T << 32, ((uint64_t)kmax << 32) | 0xffffffffull);
+  if (so.slots) {
+    __syncthreads();  // the selection is written (workgroup-visible)
+    emit_slots(row, R, k, out, so);
+  }
+}
+
+// Fallback of the filtered decode: a flagged row selects over its whole
+// score row (written by the fallback scoring); other rows return at once.
+__global__ __launch_bounds__(kTF) void topk_failed_rows_kernel(const float* __restrict__ scores, int64_t ld,
+                                                               const int32_t* __restrict__ row_len, int R, int k,
+                                                               int32_t* __restrict__ idx,
+                                                               const uint32_t* __restrict__ row_fail, SlotOut so) {
+  __shared__ SelectLds L;
+  const int row = blockIdx.x;
+  if (row_fail[row] == 0u) return;
+  const int64_t n = visible_len(row_len, nullptr, 1, row, ld);
+  int32_t* out = idx + (size_t)row * k;
+  const float* s = scores + (size_t)row * ld;
+  const Emit emit{out, nullptr, nullptr};
+  select_top(L, n, k, emit, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
+  if (so.slots) {
+    __syncthreads();
+    emit_slots(row, R, k, out, so);
+  }
+}
+
+hipError_t launch_candidate_select(const uint2* cand, const uint32_t* cnt, int cap, int cnt_stride, int nw_total,
+                                   const int32_t* ctx_len, int B, const float* thr, const int32_t* row_len,
+                                   int rows, int R, int k, int32_t* idx, uint32_t* row_fail, const SlotOut& so,
+                                   hipStream_t st) {
+  hipLaunchKernelGGL(candidate_select_kernel, dim3(rows), dim3(kTF), 0, st, cand, cnt, cap, cnt_stride, ctx_len, B,
+                     nw_total, thr, row_len, R, k, idx, row_fail, so);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_failed_rows(const float* scores, int64_t ld, const int32_t* row_len, int rows, int R, int k,
+                                   int32_t* idx, const uint32_t* row_fail, const SlotOut& so, hipStream_t st) {
+  hipLaunchKernelGGL(topk_failed_rows_kernel, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, R, k, idx, row_fail,
+                     so);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ launcher

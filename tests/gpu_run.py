@@ -50,13 +50,15 @@ def gpu_mla(case, idx, split=True, with_lse=True):
     return out, lse
 
 
-def gpu_decode(case, k=None):
+def gpu_decode(case, k=None, threshold=None):
+    """The fused decode; with `threshold` (fp32 [rows]) through dsa_decode_thresholded."""
     k = case.topk if k is None else k
     rows = case.rows
     ws = dsa.workspace(dsa.dsa_workspace_size(dsa.DSA_WS_DECODE, rows, case.max_ctx, k))
+    ws.fill_(0xA5)  # stale workspace contents must not matter
     out = torch.full((rows, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = torch.full((rows, 16), float("nan"), dtype=torch.float32, device="cuda")
     idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
     dsa.dsa_decode(dsa.Batch.of(case), dsa.Cache.of(case), case.q_idx, case.w, case.q_mla, k, case.sm_scale,
-                   out, lse, idx, ws)
+                   out, lse, idx, ws, threshold=threshold)
     return out, lse, idx

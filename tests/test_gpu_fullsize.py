@@ -22,17 +22,17 @@ import torch
 import oracle
 from tests.gpu_run import gpu_decode, gpu_mla, gpu_scores, gpu_topk, row_len_of
 from tests.parity import check_attention, check_scores, check_topk_band, check_topk_exact
-from workloads import case_config, make_case
+from workloads import case_config, make_case, structure_kwargs
 
 pytestmark = pytest.mark.gpu
 
 DECODE = ["decode_1x1_8k", "decode_16x4_32k", "decode_16x8_32k", "decode_16x4_ragged_128k_256k",
-          "decode_4x4_1m_planted", "decode_4x4_1m_mxfp4"]
+          "decode_4x4_1m_planted", "decode_4x4_1m_mxfp4", "decode_4x4_1m_recent", "decode_16x4_256k_1m"]
 
 
 def _make(name):
     cfg = case_config(name)
-    kw = {k: v for k, v in cfg.items() if k in ("permute_blocks", "plant_frac", "fp8_query", "key_format")}
+    kw = structure_kwargs(cfg)
     print(f"\n[fullsize] {name} B={cfg['B']} R={cfg['R']} lengths[0:4]={cfg['lengths'][:4]}", flush=True)
     return make_case(cfg["B"], cfg["R"], cfg["lengths"], seed=cfg["seed"], device="cuda", name=name, **kw)
 
@@ -71,8 +71,14 @@ def test_decode_workload_full_size(gpu, name):
     # same selection, same kernels: the staged outputs agree with the fused ones
     check_attention(s_out_h, s_lse_h, out_h, lse_h, f"{name} staged vs fused")
 
+    if name.endswith("_recent"):
+        # the workload's structure: most of every row's selection lies in its last 32K positions
+        L = case.ctx_len.cpu().numpy()
+        for row in range(case.rows):
+            frac = np.mean(idx_h[row] >= int(L[row // case.R]) - 32768)
+            assert frac >= 0.75, f"{name} row {row}: only {frac:.2f} of the selection in the recency window"
     host = case.to("cpu")
-    rows = _sample_rows(case.rows, seed=7)
+    rows = _sample_rows(case.rows, n_extra=1 if case.rows < 64 else 6, seed=7)
     res = oracle.dsa_rows(host, rows=rows, idx=idx_h)
     for row in rows:
         n = int(vis[row])

@@ -35,6 +35,10 @@ CASES = {
 # selection), with a row shorter than k, over permuted pages
 FUSED_ONLY = {
     "2x2_long_perm": dict(B=2, R=2, lengths=[50000, 1500], seed=109, permute_blocks=True),
+    # filtered decode (contexts past 40,960): ragged requests, one shorter than k,
+    # scoring workgroups split in proportion to the lengths
+    "5x3_filtered_ragged": dict(B=5, R=3, lengths=[41000, 60000, 1900, 45000, 90000], seed=113,
+                                permute_blocks=True),
 }
 
 
@@ -136,6 +140,42 @@ def test_topk_unaligned_rows(gpu, L):
             check_topk_exact(idx_h[i], s[i, :n], k, f"unaligned L {L} row {i} k {k}")
 
 
+def test_topk_vector_path_reads_a_partial_last_vector(gpu):
+    """16-byte-aligned rows with a row stride that is a multiple of 4 take the
+    vector-load slice path; rows of 3 * 40,960 + 1, + 2 and + 3 scores end
+    inside a 16-byte vector, and their largest scores sit in exactly those
+    last 1-3 positions (the most recent tokens of a decode row). Checked
+    through dsa_topk and through the DCP shard selection (shard rows end
+    off a multiple of 4 too)."""
+    rng = np.random.default_rng(41)
+    rows = []
+    for extra in (1, 2, 3):
+        r = rng.standard_normal(3 * SHORT_MAX + extra)
+        r[-extra:] = 100.0 + np.arange(extra)
+        rows.append(r)
+    rows.append(rng.standard_normal(3 * SHORT_MAX + 2))
+    rows[-1][-1] = 50.0
+    scores, row_len = _rows_tensor(rows)
+    assert scores.data_ptr() % 16 == 0 and scores.stride(0) % 4 == 0
+    print("\n[case] topk partial last vector", [len(r) for r in rows], flush=True)
+    s32 = scores.cpu().numpy()
+    for k in (2048, 3):
+        idx = gpu_topk(scores, row_len, k).cpu().numpy()
+        for i, r in enumerate(rows):
+            check_topk_exact(idx[i], s32[i, : len(r)], k, f"tail row {i} k {k}")
+            assert len(r) - 1 in set(idx[i].tolist()), f"tail row {i} k {k}: last position dropped"
+    W, k = 2, 2048
+    C = int(1.5 * k / W)
+    nrows = len(rows)
+    ws = dsa.workspace(dsa.dsa_dcp_workspace_size(dsa.DSA_WS_DCP_TOPK, nrows, scores.stride(0), k, W, C))
+    idx = torch.full((nrows, k), -7, dtype=torch.int32, device="cuda")
+    resend = torch.zeros((nrows, W), dtype=torch.uint8, device="cuda")
+    dsa.dsa_dcp_topk(scores, row_len, k, W, C, idx, resend, ws)
+    idx_h = idx.cpu().numpy()
+    for i, r in enumerate(rows):
+        check_topk_exact(idx_h[i], s32[i, : len(r)], k, f"dcp tail row {i}")
+
+
 @pytest.mark.parametrize("min_ld", [0, 2 * SHORT_MAX])
 def test_topk_all_ties_pick_lowest_positions(gpu, min_ld):
     scores, row_len = _rows_tensor([np.ones(9000), np.ones(2500)], min_ld=min_ld)
@@ -192,7 +232,8 @@ def test_sparse_mla_skips_invalid_entries(gpu):
         assert np.all(out[3] == 0) and np.all(np.isneginf(lse[3]))
 
 
-@pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "3x3_short_perm", "1x8", "2x2_long_perm"])
+@pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "3x3_short_perm", "1x8", "2x2_long_perm",
+                                  "5x3_filtered_ragged"])
 def test_fused_decode_matches_oracle_and_stages(gpu, name):
     case = _case(name)
     out, lse, idx = gpu_decode(case)
@@ -205,6 +246,88 @@ def test_fused_decode_matches_oracle_and_stages(gpu, name):
         assert set(idx_h[row].tolist()) == set(s_idx[row].tolist()), f"{name} row {row}: fused vs staged"
         check_topk_band(idx_h[row], res[row]["scores"], case.topk, f"{name} row {row}")
         check_attention(out[row], lse[row], res[row]["out"], res[row]["lse"], f"{name} row {row}")
+
+
+def _wide_range(t, seed, span=24):
+    """Each bf16 element scaled by 2^-e, e uniform in 0..span: every query head
+    then spans far more than 2^10 in magnitude (the split of a bf16 query
+    into two E4M3 terms under one power-of-two scale per head is exact only
+    down to ~2^-10 of the head's largest element)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    e = torch.randint(0, span + 1, tuple(t.shape), generator=g).float()
+    return (t.float().cpu() * torch.exp2(-e)).to(torch.bfloat16).to(t.device)
+
+
+def _head_range(t):
+    a = t.float().abs().cpu()
+    a = a.reshape(-1, a.shape[-1])
+    nz = torch.where(a > 0, a, torch.full_like(a, float("inf")))
+    return (a.max(dim=1).values / nz.min(dim=1).values).min().item()
+
+
+def test_query_heads_with_wide_dynamic_range(gpu):
+    case = _case("2x4_ragged_perm")
+    case.q_idx = _wide_range(case.q_idx, 1)
+    case.q_mla = _wide_range(case.q_mla, 2)
+    assert _head_range(case.q_idx) > 2.0**16 and _head_range(case.q_mla) > 2.0**16
+    scores = gpu_scores(case).cpu().numpy()
+    pos = case.positions().numpy()
+    for row in range(case.rows):
+        check_scores(scores[row, : pos[row] + 1], oracle.row_scores(case, row), f"wide-range scores row {row}")
+    idx = gpu_topk(torch.from_numpy(np.nan_to_num(scores, nan=0.0)).cuda(), row_len_of(case), case.topk)
+    out, lse = gpu_mla(case, idx)
+    out, lse, idx_h = out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
+    for row in range(case.rows):
+        ro, rl = oracle.dense_attend_row(case, row, idx_h[row])
+        check_attention(out[row], lse[row], ro, rl, f"wide-range attention row {row}")
+    f_out, f_lse, f_idx = gpu_decode(case)
+    f_idx = f_idx.cpu().numpy()
+    res = oracle.dsa_rows(case, idx=f_idx)
+    f_out, f_lse = f_out.float().cpu().numpy(), f_lse.cpu().numpy()
+    for row in range(case.rows):
+        check_topk_band(f_idx[row], res[row]["scores"], case.topk, f"wide-range fused row {row}")
+        check_attention(f_out[row], f_lse[row], res[row]["out"], res[row]["lse"], f"wide-range fused row {row}")
+
+
+def _kth_scores(case, k):
+    """Each row's k-th largest fp32 score on the GPU (-inf for rows of fewer than k)."""
+    s = gpu_scores(case, sentinel=float("-inf"))
+    n = s.shape[1]
+    return torch.topk(s, min(k, n), dim=1).values[:, -1].contiguous()
+
+
+@pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "1x1_8k"])
+def test_thresholded_decode_equals_decode_whatever_the_threshold(gpu, name):
+    """The filtered decode with caller-given thresholds: too high (+inf, NaN,
+    just above the k-th score: fewer than k candidates) and too low (-inf: more
+    candidates than fit) send rows to the exact fallback (full scores, whole-row
+    selection); exactly the k-th score decides from the candidates. Every
+    variant, and a per-row mix of them, selects dsa_decode's set."""
+    case = _case(name)
+    k = case.topk
+    ref_out, ref_lse, ref_idx = gpu_decode(case)
+    ref_idx = ref_idx.cpu().numpy()
+    kth = _kth_scores(case, k)
+    rows = case.rows
+    above = torch.nextafter(kth, torch.full_like(kth, float("inf")))
+    mix = torch.where(torch.arange(rows, device="cuda") % 3 == 0, above,
+                      torch.where(torch.arange(rows, device="cuda") % 3 == 1, kth, torch.full_like(kth, -1e30)))
+    variants = {
+        "+inf": torch.full((rows,), float("inf"), device="cuda"),
+        "-inf": torch.full((rows,), float("-inf"), device="cuda"),
+        "nan": torch.full((rows,), float("nan"), device="cuda"),
+        "kth": kth,
+        "above_kth": above,
+        "mixed": mix,
+    }
+    ro, rl = ref_out.float().cpu().numpy(), ref_lse.cpu().numpy()
+    for label, thr in variants.items():
+        print(f"[thresholded] {name} {label}", flush=True)
+        out, lse, idx = gpu_decode(case, threshold=thr)
+        idx = idx.cpu().numpy()
+        for row in range(rows):
+            assert set(idx[row].tolist()) == set(ref_idx[row].tolist()), f"{name} {label} row {row}"
+        check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"{name} {label}")
 
 
 def test_fused_decode_selection_is_deterministic(gpu):

@@ -95,6 +95,34 @@ def test_lse_combine_equals_attention_over_the_union():
         assert np.allclose(out, ro, rtol=1e-10, atol=1e-12) and np.allclose(lse, rl, rtol=1e-12)
 
 
+def test_shard_attend_owns_positions_mod_w_and_combines_to_attention():
+    """Shard w attends over exactly the selected positions p with p mod W == w
+    (token striping of decode context parallelism), and the LSE combine of
+    the W shards' partials is attention over the whole selection."""
+    H, D = 4, 576
+    table = RNG.standard_normal((6000, D)) * 0.3
+    for n, W in ((300, 8), (41, 3), (2048, 2), (5, 8)):
+        q = RNG.standard_normal((H, D))
+        positions = RNG.choice(6000, size=n, replace=False)
+        asked = []
+
+        def rows_hat_by_pos(p):
+            asked.append(np.asarray(p, np.int64).copy())
+            return table[np.asarray(p, np.int64)]
+
+        outs, lses = [], []
+        for w in range(W):
+            o, l = oracle.shard_attend(q, rows_hat_by_pos, positions, W, w, 1 / 24)
+            outs.append(o)
+            lses.append(l)
+        for w in range(W):
+            want = sorted(p for p in positions.tolist() if p % W == w)
+            assert sorted(asked[w].tolist()) == want, (n, W, w)
+        out, lse = oracle.lse_combine(outs, lses)
+        ro, rl = oracle.attend(q, table[positions], 1 / 24)
+        assert np.allclose(out, ro, rtol=1e-10, atol=1e-12) and np.allclose(lse, rl, rtol=1e-12)
+
+
 def test_lse_combine_of_nothing_is_empty_attention():
     out, lse = oracle.lse_combine(np.zeros((3, 2, 512)), np.full((3, 2), -np.inf))
     assert not out.any() and np.all(np.isneginf(lse))
@@ -102,7 +130,7 @@ def test_lse_combine_of_nothing_is_empty_attention():
 
 # ---------------------------------------------------------------- mutants
 
-_ORIG = {n: getattr(odcp, n) for n in ("dcp_select", "lse_combine")}
+_ORIG = {n: getattr(odcp, n) for n in ("dcp_select", "lse_combine", "shard_attend")}
 
 
 def _select_cutoff_off_by_one(scores, W, k, C=None):
@@ -129,17 +157,28 @@ def _combine_without_weights(outs, lses):
     return np.asarray(outs, np.float64).mean(axis=0), L
 
 
+def _shard_attend_shifted_owner(q, rows_hat_by_pos, positions, W, w, sm_scale):
+    return _ORIG["shard_attend"](q, rows_hat_by_pos, np.asarray(positions, np.int64) + 1, W, w, sm_scale)
+
+
+def _shard_attend_every_position(q, rows_hat_by_pos, positions, W, w, sm_scale):
+    return odcp.attend(q, rows_hat_by_pos(np.asarray(positions, np.int64)), sm_scale)
+
+
 MUTANTS = {
     "cutoff_off_by_one": ("dcp_select", _select_cutoff_off_by_one),
     "never_resends": ("dcp_select", _select_no_resend),
     "ties_to_higher_position": ("dcp_select", _select_ties_by_higher_position),
     "combine_unweighted": ("lse_combine", _combine_without_weights),
+    "shard_owner_shifted": ("shard_attend", _shard_attend_shifted_owner),
+    "shard_takes_every_position": ("shard_attend", _shard_attend_every_position),
 }
 
 PIN_TESTS = [
     lambda: test_merged_selection_equals_single_device_topk(8),
     test_resend_fires_only_for_a_shard_holding_too_many_winners,
     test_lse_combine_equals_attention_over_the_union,
+    test_shard_attend_owns_positions_mod_w_and_combines_to_attention,
 ]
 
 

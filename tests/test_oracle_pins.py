@@ -104,6 +104,13 @@ def test_scores_homogeneous_and_linear_in_weights():
                        s + oracle.index_scores(q, w2, k), rtol=1e-12)
     # a positive per-token scale factors out of the ReLU
     assert np.allclose(oracle.index_scores(q, w, 3.0 * k), 3.0 * s, rtol=1e-12)
+    # ... token by token, and a positive query-row scale likewise: applying
+    # both scales after the ReLU (as a kernel may) equals the definition,
+    # which applies them inside it
+    c = rng.uniform(0.01, 5.0, k.shape[0])
+    assert np.allclose(oracle.index_scores(0.7 * q, w, c[:, None] * k), 0.7 * c * s, rtol=1e-12)
+    # a negative scale does not factor out: the scales must be positive
+    assert not np.allclose(oracle.index_scores(q, w, -k), -s)
 
 
 def test_scores_opposed_key_is_zero():

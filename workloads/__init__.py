@@ -18,4 +18,5 @@ from .gen import (  # noqa: F401
     case_config,
     make_case,
     quantize_e4m3_rows,
+    structure_kwargs,
 )

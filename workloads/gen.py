@@ -118,6 +118,7 @@ def make_case(
     permute_blocks: bool = False,
     plant_frac: float = 0.0,
     plant_sigma: float = 3.0,
+    plant_window: Optional[int] = None,
     fp8_query: bool = False,
     topk: int = TOPK,
     name: str = "custom",
@@ -130,7 +131,9 @@ def make_case(
     permute_blocks scatters every request's pages over a random permutation of
     the pool. plant_frac > 0 plants structure: that fraction of each request's
     tokens gets plant_sigma added along the unit vector of the request's
-    head-weighted query sum before quantisation. fp8_query stores the indexer
+    head-weighted query sum before quantisation; with plant_window set, only
+    tokens among the request's last plant_window positions are planted (a
+    recency cluster: the row's highest scores sit in its most recent tokens). fp8_query stores the indexer
     queries as E4M3 codes with one fp32 scale per query row (prefill chunks).
     key_format "mxfp4" stores the index keys as MXFP4 instead (68 B per token:
     64 bytes of E2M1 pairs and four E8M0 block scales), drawn directly in
@@ -199,6 +202,8 @@ def make_case(
             wq = (w[b * R : (b + 1) * R].float()[:, :, None] * q_dir[b * R : (b + 1) * R]).sum(dim=(0, 1))
             u = wq / wq.norm()
             mask = torch.rand(ntok, generator=cpu) < plant_frac
+            if plant_window is not None:
+                mask &= torch.arange(ntok) >= lengths[b] - int(plant_window)
             planted[b, :ntok] = mask
             mask_d = mask.to(device)
         for t0 in range(0, ntok, CH):
@@ -249,10 +254,18 @@ def make_case(
 WORKLOADS = {
     "decode_1x1_8k": dict(B=1, R=1, lengths=[8192], seed=20260001),
     "decode_16x4_32k": dict(B=16, R=4, lengths=[32768] * 16, seed=20260002),
-    "decode_16x4_ragged_128k_256k": dict(B=16, R=4, lengths=None, seed=20260003, permute_blocks=True),
+    "decode_16x4_ragged_128k_256k": dict(B=16, R=4, lengths=None, seed=20260003, permute_blocks=True,
+                                         length_range=(131072, 262144)),
     "decode_16x8_32k": dict(B=16, R=8, lengths=[32768] * 16, seed=20260006),
     "decode_4x4_1m_planted": dict(B=4, R=4, lengths=[1 << 20] * 4, seed=20260004, plant_frac=0.01),
     "decode_4x4_1m_mxfp4": dict(B=4, R=4, lengths=[1 << 20] * 4, seed=20260007, key_format="mxfp4"),
+    # 10% of the last 32K positions planted at +12 sigma: nearly all of each row's top-2048 lies in
+    # its most recent 32K tokens (a recency cluster)
+    "decode_4x4_1m_recent": dict(B=4, R=4, lengths=[1 << 20] * 4, seed=20260008, plant_frac=0.1,
+                                 plant_window=32768, plant_sigma=12.0),
+    # 16 requests x 4 verification rows at U[256K, 1M] tokens each, permuted pages
+    "decode_16x4_256k_1m": dict(B=16, R=4, lengths=None, seed=20260009, permute_blocks=True,
+                                length_range=(262144, 1048576)),
     "prefill_4096_on_128k": dict(B=1, R=4096, lengths=[131072 + 4096], seed=20260005, fp8_query=True),
 }
 
@@ -262,8 +275,18 @@ def case_config(name: str, seed_offset: int = 0) -> dict:
     cfg = dict(WORKLOADS[name])
     cfg["seed"] = cfg["seed"] + seed_offset
     cfg["name"] = name
-    if cfg["lengths"] is None:  # ragged: U[128K, 256K] per request, seeded
+    lo_hi = cfg.pop("length_range", None)
+    if cfg["lengths"] is None:  # ragged: U[lo, hi] per request, seeded
         g = torch.Generator(device="cpu")
         g.manual_seed(cfg["seed"] + 7)
-        cfg["lengths"] = torch.randint(131072, 262144 + 1, (cfg["B"],), generator=g).tolist()
+        cfg["lengths"] = torch.randint(lo_hi[0], lo_hi[1] + 1, (cfg["B"],), generator=g).tolist()
     return cfg
+
+
+STRUCTURE_KEYS = ("permute_blocks", "plant_frac", "plant_window", "plant_sigma", "fp8_query", "key_format")
+
+
+def structure_kwargs(cfg: dict) -> dict:
+    """The make_case keyword arguments of a workload config that shape its
+    structure (page permutation, planted keys, query and key formats)."""
+    return {k: v for k, v in cfg.items() if k in STRUCTURE_KEYS}
