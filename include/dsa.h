@@ -219,6 +219,24 @@ int32_t dsa_sparse_mla_prefill(const dsa_batch* batch, const dsa_cache* cache, c
                                void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dsa_sparse_mla_decode without a workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. Same arguments and results as
+ * dsa_sparse_mla_decode, minus ws / ws_bytes. The split partials go to a
+ * 16 MiB array of the library's own device memory (a static device array:
+ * every GPU the library runs on holds one copy until the process ends),
+ * which covers every shape the decode variant accepts (its workspace is at
+ * most 16 MiB, at 255 rows); a larger need returns DSA_ERR_UNSUPPORTED.
+ * Nothing is allocated or freed. All calls on one GPU share that GPU's
+ * array and it keeps the last call's partials: calls that may overlap on
+ * one GPU (other streams, other host threads) race and must be serialised
+ * by the caller.
+ */
+int32_t dsa_sparse_mla_decode_noalloc(const dsa_batch* batch, const dsa_cache* cache, const void* q,
+                                      int32_t num_heads, const int32_t* idx, int32_t k, float softmax_scale,
+                                      void* out, float* lse, void* stream);
+
+/*
  * The whole decode step: Score (bf16 queries) -> Select (top-k) -> Attend, as
  * one call on one stream. The pages' problem statement: for every query row
  * the indexer scores one FP8 key per earlier token, the top k are kept, and

@@ -280,6 +280,16 @@ def dsa_sparse_mla_decode(batch, cache, q, idx, softmax_scale, out, lse=None, ws
          ws, stream)
 
 
+def dsa_sparse_mla_decode_noalloc(batch, cache, q, idx, softmax_scale, out, lse=None, stream=None):
+    """dsa_sparse_mla_decode with the library's own static scratch (no workspace, no allocation)."""
+    fn = load().dsa_sparse_mla_decode_noalloc
+
+    def call(b, c, qp, nh, ip, k, sm, op, lp, wp, wn, s):
+        return fn(b, c, qp, nh, ip, k, sm, op, lp, s)
+
+    _mla(call, "dsa_sparse_mla_decode_noalloc", batch, cache, q, idx, softmax_scale, out, lse, None, stream)
+
+
 def dsa_sparse_mla_prefill(batch, cache, q, idx, softmax_scale, out, lse=None, ws=None, stream=None):
     _mla(load().dsa_sparse_mla_prefill, "dsa_sparse_mla_prefill", batch, cache, q, idx, softmax_scale, out, lse,
          ws, stream)

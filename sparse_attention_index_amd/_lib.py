@@ -28,6 +28,7 @@ EXPORTS = (
     "dsa_topk",
     "dsa_sparse_mla_decode",
     "dsa_sparse_mla_prefill",
+    "dsa_sparse_mla_decode_noalloc",
     "dsa_decode",
     "dsa_decode_thresholded",
     "dsa_workspace_size",
@@ -92,6 +93,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsa_topk": (I32, [P, I64, P, I32, I32, P, P, SZ, P]),
         "dsa_sparse_mla_decode": (I32, [BP, CP, P, I32, P, I32, F, P, P, P, SZ, P]),
         "dsa_sparse_mla_prefill": (I32, [BP, CP, P, I32, P, I32, F, P, P, P, SZ, P]),
+        "dsa_sparse_mla_decode_noalloc": (I32, [BP, CP, P, I32, P, I32, F, P, P, P]),
         "dsa_decode": (I32, [BP, CP, P, P, P, I32, I32, F, P, P, P, P, SZ, P]),
         "dsa_decode_thresholded": (I32, [BP, CP, P, P, P, I32, I32, F, P, P, P, P, P, SZ, P]),
         "dsa_workspace_size": (SZ, [I32, I32, I64, I32, I32]),

@@ -260,6 +260,24 @@ int32_t dsa_sparse_mla_decode(const dsa_batch* batch, const dsa_cache* cache, co
   return mla_entry(true, batch, cache, q, num_heads, idx, k, softmax_scale, out, lse, ws, ws_bytes, stream);
 }
 
+int32_t dsa_sparse_mla_decode_noalloc(const dsa_batch* batch, const dsa_cache* cache, const void* q,
+                                      int32_t num_heads, const int32_t* idx, int32_t k, float softmax_scale,
+                                      void* out, float* lse, void* stream) {
+  g_err[0] = 0;
+  int32_t r = check_batch(batch);
+  if (r) return r;
+  if ((r = check_cache(cache, false, true))) return r;
+  if ((r = check_mla(num_heads, k, q, idx, out, true))) return r;
+  const int32_t rows = batch->num_requests * batch->rows_per_request;
+  const size_t need = mla_ws_bytes(rows, k, true);
+  if (need > mla_scratch_bytes())
+    return fail(DSA_ERR_UNSUPPORTED, "%d rows need %zu scratch bytes, more than the library's %zu", rows, need,
+                mla_scratch_bytes());
+  void* ws = nullptr;
+  if (need && (r = hip_status(mla_scratch(&ws), "scratch address"))) return r;
+  return run_mla(batch, cache, q, idx, k, softmax_scale, out, lse, ws, true, static_cast<hipStream_t>(stream));
+}
+
 int32_t dsa_sparse_mla_prefill(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t num_heads,
                                const int32_t* idx, int32_t k, float softmax_scale, void* out, float* lse, void* ws,
                                size_t ws_bytes, void* stream) {

@@ -117,6 +117,10 @@ struct MlaArgs {
 };
 
 size_t mla_ws_bytes(int rows, int k, bool split);
+// The library's own scratch for the no-allocation decode attention: its size
+// and its device address on the current device (looked up once per device).
+size_t mla_scratch_bytes();
+hipError_t mla_scratch(void** out);
 
 // Decode context parallelism over W virtual shards of one device.
 size_t dcp_topk_ws_bytes(int rows, int64_t ld, int k, int W, int C);

@@ -38,6 +38,8 @@
 // partial outputs, "TokenSpeed Kimi K3.1", section "Sharding long contexts").
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -494,5 +496,37 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int rows, bool split, void* ws, h
   return hipGetLastError();
 }
 
-}  // namespace dsa
+// ------------------------------------------------------------------ no-allocation scratch
 
+// The split partials of the no-allocation decode entry point live in this
+// array of the library's own device memory (one copy per GPU, held until
+// the process ends). 16 MiB is the most mla_ws_bytes asks for at any row
+// count (255 rows in two splits of k = 2048: 255 * 2 * 16 * 514 * 4 + 256
+// bytes); 256 rows and more take one split and no scratch.
+static constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+size_t mla_scratch_bytes() { return kScratchBytes; }
+
+// The device address of `scratch` on the current device, looked up once per
+// device (the host-side name is a stand-in, not a device address).
+hipError_t mla_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace dsa
