@@ -5,7 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -84,11 +84,12 @@ int32_t check_mla(int32_t num_heads, int32_t k, const void* q, const int32_t* id
 
 int64_t decode_ld(int32_t max_ctx) { return ((int64_t)max_ctx + 63) / 64 * 64; }
 
-// Candidate slots per row of the filtered decode: the sampled threshold
-// leaves about 1.25k to 3.4k of a row's scores plus a margin (at most
-// 12,288 can be selected from), split into one region per scoring workgroup
-// of the row's request; rows of few requests have the most workgroups.
-int32_t filter_cap(int32_t rows) { return rows <= 128 ? 65536 : 16384; }
+// Candidate slots per row of the filtered decode, split into one region per
+// scoring workgroup of the row's request: the sampled threshold leaves about
+// 3k to 10k of a row's scores (the selection holds up to 16,384 in LDS and
+// selects from larger runs where they are); a workgroup that passes its
+// region sends the row to the exact fallback.
+int32_t filter_cap(int32_t rows) { return rows <= 128 ? 65536 : 32768; }
 
 struct DecodeWs {
   float* scores;   // full scores: the stored path, and the filtered path's fallback
@@ -97,10 +98,10 @@ struct DecodeWs {
   int32_t* slots;  // physical cache rows of the selection
   void* topk;
   void* mla;
-  float* thr;      // filtered path: per-row score threshold
-  uint32_t* fail;  // filtered path: rows the candidates could not decide
-  uint32_t* fcnt;  // filtered path: [rows][kMaxFilterWg] candidates per scoring workgroup
-  uint2* fcand;    // filtered path: [rows][filter_cap] candidates
+  float* thr;       // filtered path: per-row score threshold
+  uint32_t* fcount; // filtered path: [rows][kMaxFilterWg] candidates per scoring workgroup
+  uint2* fcand;     // filtered path: [rows][filter_cap] candidates, one region per scoring workgroup
+  uint2* fcompact;  // filtered path: [rows][filter_cap] a row's candidates in one run (past LDS capacity)
 };
 
 size_t decode_ws_parts(int32_t rows, int64_t max_ctx, int32_t k, DecodeWs* out, void* base) {
@@ -113,9 +114,9 @@ size_t decode_ws_parts(int32_t rows, int64_t max_ctx, int32_t k, DecodeWs* out, 
       align256(topk_ws_bytes(rows, ld)),                              // topk
       align256(mla_ws_bytes(rows, k, true)),                          // mla
       align256((size_t)rows * sizeof(float)),                         // thr
-      align256((size_t)rows * sizeof(uint32_t)),                      // fail
-      align256((size_t)rows * kMaxFilterWg * sizeof(uint32_t)),       // fcnt
+      align256((size_t)rows * kMaxFilterWg * sizeof(uint32_t)),       // fcount
       align256((size_t)rows * filter_cap(rows) * sizeof(uint2)),      // fcand
+      align256((size_t)rows * filter_cap(rows) * sizeof(uint2)),      // fcompact
   };
   size_t total = 0;
   char* part[10];
@@ -131,9 +132,9 @@ size_t decode_ws_parts(int32_t rows, int64_t max_ctx, int32_t k, DecodeWs* out, 
     out->topk = part[4];
     out->mla = sizes[5] ? part[5] : nullptr;
     out->thr = reinterpret_cast<float*>(part[6]);
-    out->fail = reinterpret_cast<uint32_t*>(part[7]);
-    out->fcnt = reinterpret_cast<uint32_t*>(part[8]);
-    out->fcand = reinterpret_cast<uint2*>(part[9]);
+    out->fcount = reinterpret_cast<uint32_t*>(part[7]);
+    out->fcand = reinterpret_cast<uint2*>(part[8]);
+    out->fcompact = reinterpret_cast<uint2*>(part[9]);
   }
   return total;
 }
@@ -289,7 +290,7 @@ int32_t dsa_sparse_mla_prefill(const dsa_batch* batch, const dsa_cache* cache, c
 // batch on the stored-score path. The stored path is the faster one on
 // MI355X at every measured length, because the sampling pass costs more
 // than the score round trip it saves; dsa_decode_thresholded always filters.
-static constexpr int kFilterMinCtx = 0;
+static constexpr int kFilterMinCtx = 40960;
 
 // The decode step. thr_in (device, [rows]) set: the filtered path with the
 // caller's thresholds, whatever max_ctx is.
@@ -328,39 +329,26 @@ static int32_t decode_impl(const dsa_batch* batch, const dsa_cache* cache, const
   so.slots = p.slots;
   so.block_table = batch->block_table;
   so.max_blocks = batch->max_blocks;
-  const int grid =
-      index_score_grid_x(B, batch->rows_per_request, batch->max_ctx, cache->key_format == DSA_KEY_MXFP4);
-  const bool filtered = (thr_in || (kFilterMinCtx > 0 && batch->max_ctx > kFilterMinCtx)) &&
-                        grid - B + 1 <= kMaxFilterWg;
-  if (thr_in && !filtered) return fail(DSA_ERR_UNSUPPORTED, "too many scoring workgroups per request");
+  const int grid = filter_grid(B, batch->rows_per_request, batch->max_ctx, cache->key_format == DSA_KEY_MXFP4);
+  const bool fits = grid - B + 1 <= kMaxFilterWg;  // no request past kMaxFilterWg scoring workgroups
+  if (thr_in && !fits)
+    return fail(DSA_ERR_UNSUPPORTED, "a request would need more than %d scoring workgroups", kMaxFilterWg);
+  const bool filtered = thr_in || (kFilterMinCtx > 0 && batch->max_ctx > kFilterMinCtx && fits);
   if (filtered) {
-    // 1. each row's visible length and threshold (sampled, or the caller's)
-    if ((r = hip_status(launch_sample_threshold(a, rows, k, thr_in, p.thr, p.row_len, st), "decode threshold")))
-      return r;
-    // 2. score, keeping only the candidates at or above the threshold
     ScoreArgs f = a;
-    f.scores = nullptr;
     f.thr = p.thr;
     f.cand = p.fcand;
-    f.cnt = p.fcnt;
+    f.cand_count = p.fcount;
     f.cap = filter_cap(rows);
-    f.cnt_stride = kMaxFilterWg;
-    int gx = 0;
-    if ((r = hip_status(launch_index_score(f, B, batch->max_ctx, false, st, &gx), "decode filtered score")))
+    // 1. each row's visible length and threshold (sampled, or the caller's)
+    if ((r = hip_status(launch_sample_threshold(f, rows, k, thr_in, p.thr, p.row_len, st), "decode threshold")))
       return r;
-    // 3. exact selection from the candidates; rows they cannot decide are flagged
-    if ((r = hip_status(launch_candidate_select(p.fcand, p.fcnt, f.cap, kMaxFilterWg, gx, batch->ctx_len, B, p.thr,
-                                                p.row_len, rows, batch->rows_per_request, k, idx, p.fail, so, st),
+    // 2. score, keeping only the candidates at or above the threshold
+    if ((r = hip_status(launch_index_score(f, B, batch->max_ctx, false, st), "decode filtered score"))) return r;
+    // 3. exact selection from the candidates; a row they cannot decide is
+    //    scored again in full (into the score rows) and selected over all of it
+    if ((r = hip_status(launch_candidate_select(f, B, grid, p.thr, p.row_len, p.fcompact, rows, k, idx, so, st),
                         "decode candidate select")))
-      return r;
-    // 4. exact fallback for flagged rows: their full scores, then a whole-row
-    //    selection (both return at once for unflagged rows)
-    ScoreArgs fb = a;
-    fb.row_fail = p.fail;
-    if ((r = hip_status(launch_index_score(fb, B, batch->max_ctx, false, st), "decode fallback score"))) return r;
-    if ((r = hip_status(launch_topk_failed_rows(p.scores, ld, p.row_len, rows, batch->rows_per_request, k, idx,
-                                                p.fail, so, st),
-                        "decode fallback select")))
       return r;
   } else {
     const TopkWs tw = topk_ws_carve(p.topk, rows, ld);

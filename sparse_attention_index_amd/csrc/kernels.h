@@ -23,37 +23,34 @@ struct ScoreArgs {
   int64_t ld;
   // Filtered decode: in place of the scores, every (ordered key, position)
   // whose score is >= the row's threshold goes to the scoring workgroup's
-  // own region of the row's candidate buffer (cap / gridDim.x slots from
-  // blockIdx.x * (cap / gridDim.x)), and each workgroup writes its true
-  // count per row (also when it exceeds the region).
+  // own region of the row's candidate buffer (cap / W slots from
+  // j * (cap / W), for the request's W workgroups, j this one's index among
+  // them), and each workgroup writes its true count per row to
+  // cand_count[row * kMaxFilterWg + j] (also when it exceeds the region):
+  // no atomics and nothing to clear.
   const float* thr = nullptr;     // [rows] score threshold (-inf keeps every score, NaN none)
   uint2* cand = nullptr;          // [rows][cap]
-  uint32_t* cnt = nullptr;        // [rows][cnt_stride]
+  uint32_t* cand_count = nullptr; // [rows][kMaxFilterWg]
   int32_t cap = 0;
-  int32_t cnt_stride = 0;
-  // Scores only the row groups holding a row with row_fail[row] != 0 (the
-  // exact fallback of the filtered decode); null scores every group.
-  const uint32_t* row_fail = nullptr;
 };
 
 // Scores every (row, visible token). B requests, max_ctx bounds ctx_len.
 // With a.cand set (bf16 queries only) the scores are filtered into
-// candidates instead of stored; *grid_x (if given) receives the number of
-// workgroups per request and row group.
-hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st,
-                              int* grid_x = nullptr);
-// Most scoring workgroups per (request, row group) in the filtered decode.
+// candidates instead of stored.
+hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st);
+// Most scoring workgroups a request gets in the filtered decode.
 constexpr int kMaxFilterWg = 1024;
-// Workgroups per (request, row group) the scorer launches for B requests of R
-// rows (bf16 queries) at most max_ctx tokens.
-int index_score_grid_x(int B, int R, int max_ctx, bool mxfp4);
+// Workgroups per row group the scorer launches in the filtered decode for B
+// requests of R rows (bf16 queries) of at most max_ctx tokens; a request
+// gets at most grid - B + 1 of them.
+int filter_grid(int B, int R, int max_ctx, bool mxfp4);
 
 // Sampling pass of the filtered decode, one workgroup per row: the row's
 // visible length goes to row_len and its score threshold to thr (-inf for
 // rows of at most 8,192 tokens: everything is kept). A row of more tokens
-// scores 2,048 or 4,096 sampled keys (whole pages evenly spaced over its
-// full pages) and takes the top-k's sampled threshold over them. With
-// thr_in set, thr[row] = thr_in[row] and nothing is sampled.
+// scores 2,048 sampled keys (32 whole pages evenly spaced over its full
+// pages) and takes the top-k's sampled threshold over them. With thr_in set,
+// thr[row] = thr_in[row] and nothing is sampled.
 hipError_t launch_sample_threshold(const ScoreArgs& a, int rows, int k, const float* thr_in, float* thr,
                                    int32_t* row_len, hipStream_t st);
 
@@ -84,22 +81,17 @@ hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int ro
                        int32_t* idx, const TopkWs& w, hipStream_t st, const int32_t* ctx_len = nullptr, int R = 1,
                        const SlotOut& so = SlotOut{});
 
-// Filtered decode, selection: per row, the k largest of the candidates the
-// scoring workgroups of its request left (ScoreArgs::cand / cnt), when they are enough
-// and none overflowed its region: then row_fail[row] = 0 and idx (and the
-// slots) are written. Otherwise row_fail[row] = 1 and nothing else is
-// written for the row. Rows of at most k tokens take every position.
-// nw_total is the scorer's grid_x; ctx_len and B give its split over the
-// requests; thr holds the rows' thresholds.
-hipError_t launch_candidate_select(const uint2* cand, const uint32_t* cnt, int cap, int cnt_stride, int nw_total,
-                                   const int32_t* ctx_len, int B, const float* thr, const int32_t* row_len,
-                                   int rows, int R, int k, int32_t* idx, uint32_t* row_fail, const SlotOut& so,
-                                   hipStream_t st);
-// Fallback of the filtered decode: rows with row_fail[row] != 0 select over
-// their whole fp32 score row (written by the fallback scoring); the others
-// return at once.
-hipError_t launch_topk_failed_rows(const float* scores, int64_t ld, const int32_t* row_len, int rows, int R, int k,
-                                   int32_t* idx, const uint32_t* row_fail, const SlotOut& so, hipStream_t st);
+// Filtered decode, selection (one workgroup per row): the k largest of the
+// candidates the scorer kept for the row (a.cand / a.cand_count / a.cap; G
+// the scorer's grid, whose split over the B requests is recomputed from
+// ctx_len), exact whenever no workgroup region overflowed and at least k
+// arrived; otherwise the row is scored again in full into a.scores (row
+// stride a.ld) and selected over its whole row. Rows of at most k tokens
+// take every position. idx and the slots (if asked for) are written for
+// every row. compact: [rows][a.cap] room for a row's candidates past what
+// LDS holds.
+hipError_t launch_candidate_select(const ScoreArgs& a, int B, int G, const float* thr, const int32_t* row_len,
+                                   uint2* compact, int rows, int k, int32_t* idx, const SlotOut& so, hipStream_t st);
 
 struct MlaArgs {
   const uint16_t* q;        // bf16 [rows][16][576]

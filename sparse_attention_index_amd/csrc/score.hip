@@ -27,7 +27,10 @@
 // no SIMD) carries much more than the others.
 // Score stores use buffer descriptors sized to each row's visible prefix:
 // the hardware drops stores past it, which applies the causal mask without
-// branches.
+// branches. In the filtered decode nothing is stored but the candidates:
+// each wave compares its own rows' scores with their thresholds as it
+// reduces them and appends the few that pass to its workgroup's region of
+// the row's buffer.
 //
 // The dot products run on v_mfma_f32_32x32x64_f8f6f4 (the scaled form for
 // MXFP4 keys) with the raw key bytes as the B operand (no conversion).
@@ -57,6 +60,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "query.h"
 #include "select.h"
 
 namespace dsa {
@@ -77,11 +81,6 @@ static_assert(kCopies % kCopiers == 0, "copies split evenly");
 // lanes of each read phase hit distinct banks.
 DSA_DEV int key_chunk_off(int n, int j) { return n * kIdxDim + ((j ^ ((n >> 1) & 7)) << 4); }
 
-// max(x, 0) as one integer max on the bit pattern: non-negative floats
-// (+0 included) are non-negative integers, negative floats and -0 are
-// negative integers. The operands are finite MFMA sums.
-DSA_DEV float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
-
 // Wave priority from the workgroup's progress: 3 over its first quarter of
 // pages down to 0 over its last. Several workgroups share each SIMD and the
 // oldest wave wins ties, so without this the first workgroup placed on a CU
@@ -97,119 +96,6 @@ DSA_DEV void set_progress_priority(int i, int n) {
 
 // Byte offset past every row's visible prefix: buffer stores there are dropped.
 static constexpr uint32_t kPastEnd = 0x80000000u;
-
-DSA_DEV uint32_t e4m3x2_from_f32(float a, float b) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
-}
-
-
-// The E4M3 A operands of one query row: q * 2^e = hi + lo (bf16 queries) or
-// the query codes as they are, with the factor 2^-e (or the row scale) that
-// multiplies the head's dot products. fetch_query loads the lane's raw bytes;
-// finish_query converts them, later, while the first key pages are in flight.
-//
-// K order. With FP8 keys, byte i of lane half g's operand for step s is dim
-// 64g + 32s + i. With MXFP4 keys the FP4 B operand of lane half g holds K
-// indices 16g + [0, 16) in its first 16 nibbles and 32 + 16g + [0, 16) in
-// the next 16 (measured on gfx950), and its one E8M0 scale covers all 32;
-// so that those 32 values are one MX block (dims 64g + 32s + [0, 32), read
-// as 16 contiguous bytes), the query's byte i of lane half g, step s, must
-// be dim 32s + 16g + i (i < 16) or 64 + 32s + 16g + i - 16 (i >= 16).
-template <bool QFP8, bool KF4>
-struct QueryRaw {
-  u32x4 v[8];  // bf16 queries: 64 values per lane
-};
-template <bool KF4>
-struct QueryRaw<true, KF4> {
-  u32x4 p[4];  // E4M3 codes: 64 per lane
-  float scale;
-};
-
-template <bool QFP8, bool KF4>
-DSA_DEV void fetch_query(const ScoreArgs& a, size_t row, int n, int g, QueryRaw<QFP8, KF4>& r) {
-  if constexpr (QFP8) {
-    const uint8_t* q8 = reinterpret_cast<const uint8_t*>(a.q) + (row * kIdxHeads + n) * kIdxDim;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)  // MXFP4 keys: dims 32c + 16g + [0, 16); FP8 keys: dims 64g + 16c + [0, 16)
-      r.p[c] = *reinterpret_cast<const u32x4*>(q8 + (KF4 ? 32 * c + 16 * g : 64 * g + 16 * c));
-    r.scale = a.q_scale[row];
-  } else {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.q) +
-                                                     (row * kIdxHeads + n) * kIdxDim);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      // piece c of 8 values: FP8 keys: dims 64g + 8c; MXFP4 keys: dims
-      // 16g + 32u + 8(c & 1) for u = 0, 2, 1, 3 (c >> 1 = 0..3)
-      const int u = (c >> 1) == 1 ? 2 : ((c >> 1) == 2 ? 1 : (c >> 1));
-      r.v[c] = KF4 ? qp[(16 * g + 32 * u) / 8 + (c & 1)] : qp[8 * g + c];
-    }
-  }
-}
-
-// Keeps the code that reads r after this point of the program (the raw
-// registers pass through an empty asm statement).
-template <bool QFP8, bool KF4>
-DSA_DEV void hold_query(QueryRaw<QFP8, KF4>& r) {
-  if constexpr (QFP8) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(r.p[c]));
-    asm volatile("" : "+v"(r.scale));
-  } else {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(r.v[c]));
-  }
-}
-
-template <bool QFP8, bool KF4>
-DSA_DEV float finish_query(const QueryRaw<QFP8, KF4>& r, i32x8 (&A)[QFP8 ? 1 : 2][2]) {
-  if constexpr (QFP8) {
-    auto cat = [](const u32x4& x, const u32x4& y) {
-      return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
-    };
-    A[0][0] = KF4 ? cat(r.p[0], r.p[2]) : cat(r.p[0], r.p[1]);
-    A[0][1] = KF4 ? cat(r.p[1], r.p[3]) : cat(r.p[2], r.p[3]);
-    return r.scale;
-  } else {
-    // x[32s + i]: the value at byte i of step s
-    float x[64];
-    float amax = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const bf16x8 v = __builtin_bit_cast(bf16x8, r.v[c]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[8 * c + e] = (float)v[e];
-        amax = fmaxf(amax, fabsf(x[8 * c + e]));
-      }
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 32));  // whole head: both lane halves
-    int ex = 0;
-    if (amax > 0.f) {
-      int e2;
-      const float m = frexpf(amax, &e2);  // amax = m * 2^e2, m in [0.5, 1)
-      ex = (m <= 0.875f ? 9 : 8) - e2;    // amax * 2^ex in (224, 448]
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        uint32_t hw = 0, lw = 0;
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const float x0 = ldexpf(x[32 * s + 4 * d + e], ex), x1 = ldexpf(x[32 * s + 4 * d + e + 1], ex);
-          const uint32_t hb = e4m3x2_from_f32(x0, x1);
-          const auto hf = __builtin_amdgcn_cvt_pk_f32_fp8(hb, false);
-          const uint32_t lb = e4m3x2_from_f32(x0 - hf[0], x1 - hf[1]);
-          hw |= hb << (8 * e);
-          lw |= lb << (8 * e);
-        }
-        A[0][s][d] = (int)hw;
-        A[1][s][d] = (int)lw;
-      }
-    }
-    return ldexpf(1.0f, -ex);
-  }
-}
 
 // Roles of the waves: every wave scores RPW rows and writes its scores to
 // LDS; waves 0-2 also move the pages into LDS, wave 3 stores the scores.
@@ -244,11 +130,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int pos0 = L - R + r0;                // position of the group's first row
   const int blk_lim = ((pos0 + nr - 1) >> 6) + 1;  // pages any row of the group sees
   const size_t row0 = (size_t)b * R + r0;
-  if (a.row_fail) {  // fallback scoring: only groups holding a row the selection could not finish
-    bool any = false;
-    for (int gr = 0; gr < nr; ++gr) any |= a.row_fail[row0 + gr] != 0u;
-    if (!any) return;  // every thread read the same flags
-  }
 
   // this workgroup's pages: jx, jx + stride, ... below blk_lim
   const int jx = blockIdx.x - wgr.first;
@@ -318,10 +199,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     fetch_query<QFP8, KF4>(a, row, n, g, qraw[rr]);
     wbits[rr] = a.w[row * kIdxHeads + n];
   }
-  // filtered decode: each row's threshold, loaded with the queries
-  float thr_f[ROWS];
+  // filtered decode: the threshold of each of the wave's rows, loaded with the queries
+  float thr_w[RPW];
 #pragma unroll
-  for (int gr = 0; gr < ROWS; ++gr) thr_f[gr] = FILT && gr < nr ? a.thr[row0 + gr] : 0.f;
+  for (int rr = 0; rr < RPW; ++rr) thr_w[rr] = FILT ? a.thr[row0 + min(wr0 + rr, nr - 1)] : 0.f;
   {
     const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
     for (int i = tid; i < n_my; i += kThreads) tbl_s[i] = table[jx + i * stride];
@@ -346,16 +227,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
   for (int i = 0; i < 16; ++i) wv[i] = w_s[wr0][8 * (i >> 2) + 4 * g + (i & 3)];
 
-  // filtered decode: the workgroup's candidate region per row and its
-  // running counts
-  uint2* fregion[ROWS];
-  uint32_t fcnt[ROWS];
-  const uint32_t fsub = FILT ? (uint32_t)(a.cap / stride) : 0u;
+  // filtered decode: the candidates each of the wave's rows has kept so far
+  // (uniform), and the size of this workgroup's region of a row's buffer
+  uint32_t fcnt[RPW];
 #pragma unroll
-  for (int gr = 0; gr < ROWS; ++gr) {
-    fcnt[gr] = 0;
-    fregion[gr] = FILT ? a.cand + (row0 + min(gr, nr - 1)) * (size_t)a.cap + (size_t)jx * fsub : nullptr;
-  }
+  for (int rr = 0; rr < RPW; ++rr) fcnt[rr] = 0;
+  const uint32_t fsub = FILT ? (uint32_t)(a.cap / stride) : 0u;
 
   auto run = [&](auto role_tag) {
     constexpr WaveRole role = decltype(role_tag)::value;
@@ -387,7 +264,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const float v = halves_sum_pair(p[0], p[G - 1]) * ks;
       // both lane halves write; with one row per group they write the same value
       const int rr = gi * G + (G == 2 ? g : 0);
-      if (i >= 0) sc_s[i % (LAG + 1)][wr0 + rr][32 * h + n] = v;
+      if constexpr (FILT) {
+        // filtered decode: keep (key, position) of a score that reaches its
+        // row's threshold in this workgroup's region of the row's buffer (a
+        // few per page at long contexts); with one row per group only the
+        // lower lane half keeps
+        if (i >= 0) {
+          const int pos = (jx + i * stride) * kBlock + 32 * h + n;
+          const bool keep = (G == 2 || g == 0) && wr0 + rr < nr && pos <= pos0 + wr0 + rr && v >= thr_w[rr];
+          const uint64_t m = __ballot(keep);
+          if (m) {
+            const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+            const uint32_t rank = g == 0 ? __builtin_amdgcn_mbcnt_lo(mlo, 0u) : __builtin_amdgcn_mbcnt_hi(mhi, 0u);
+            const uint32_t slot = (g == 0 ? fcnt[gi * G] : fcnt[gi * G + G - 1]) + rank;
+            if (keep && slot < fsub)
+              a.cand[(row0 + wr0 + rr) * (size_t)a.cap + (size_t)jx * fsub + slot] =
+                  make_uint2(ordered_key(v), (uint32_t)pos);
+            fcnt[gi * G] += (uint32_t)__popc(mlo);
+            if constexpr (G == 2) fcnt[gi * G + 1] += (uint32_t)__popc(mhi);
+          }
+        }
+      } else {
+        if (i >= 0) sc_s[i % (LAG + 1)][wr0 + rr][32 * h + n] = v;
+      }
     };
     // wave 3: store the group's scores of page i (complete once barrier i + LAG passed);
     // in the filtered decode, keep the (key, position) of each score >= its
@@ -395,21 +294,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // page at long contexts)
     auto flush = [&](int i) {
       if constexpr (FILT) {
-        const int p = (jx + i * stride) * kBlock + lane;
-#pragma unroll
-        for (int gr = 0; gr < ROWS; ++gr) {
-          if (gr < nr) {
-            const float v = sc_s[i % (LAG + 1)][gr][lane];
-            const bool keep = p <= pos0 + gr && v >= thr_f[gr];
-            const uint64_t m = __ballot(keep);
-            if (m) {
-              const uint32_t slot = fcnt[gr] + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-              if (keep && slot < fsub) fregion[gr][slot] = make_uint2(ordered_key(v), (uint32_t)p);
-              fcnt[gr] += (uint32_t)__popcll(m);
-            }
-          }
-        }
+        (void)i;  // filtered decode: the waves kept their candidates themselves
       } else {
         const uint32_t off = 4u * (uint32_t)((jx + i * stride) * kBlock + lane);
 #pragma unroll
@@ -522,144 +407,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __syncthreads();  // the last scores are in LDS
     if constexpr (role == kFlusher) {
       for (int i = max(0, n_my - LAG); i < n_my; ++i) flush(i);
-      if constexpr (FILT) {  // this workgroup's true count per row (also past its region)
+    }
+    if constexpr (FILT) {  // this workgroup's true count per row (also past its region)
 #pragma unroll
-        for (int gr = 0; gr < ROWS; ++gr)
-          if (gr < nr && lane == 0) a.cnt[(row0 + gr) * a.cnt_stride + jx] = fcnt[gr];
-      }
+      for (int rr = 0; rr < RPW; ++rr)
+        if (wr0 + rr < nr && lane == 0) a.cand_count[(row0 + wr0 + rr) * kMaxFilterWg + jx] = fcnt[rr];
     }
   };
   if (wave < kCopiers) run(std::integral_constant<WaveRole, kCopier>{});
   else run(std::integral_constant<WaveRole, kFlusher>{});
-}
-
-// ------------------------------------------------------------------ sampling pass
-
-static constexpr int kSampleThreads = 512;  // 8 waves
-static constexpr int kSamplePpw = 4;        // pages each wave has in flight
-
-// Filtered decode, step 1, one workgroup per query row. The row's visible
-// length n goes to row_len. A row of more than kTakeAll tokens scores
-// ns = 2,048 (n <= 2^18) or 4,096 sampled keys -- ns / 64 whole pages evenly
-// spaced over the pages it sees in full -- with the scorer's arithmetic
-// (the same query split, MFMAs and head-weighted ReLU reduction; the keys go
-// from global memory straight into MFMA operands), and takes the top-k's
-// sampled threshold over those scores (sample_select), written to thr as
-// the float a kept score must reach. Shorter rows keep every score (-inf).
-template <bool KF4>
-__global__ __launch_bounds__(kSampleThreads) void sample_threshold_kernel(ScoreArgs a, int k, const float* thr_in,
-                                                                         float* thr, int32_t* row_len) {
-  constexpr int NT = kSampleThreads, NW = NT / 64, PPW = kSamplePpw;
-  static_assert((2048 / kBlock) % (NW * PPW) == 0, "sampled pages split evenly over the waves");
-  __shared__ float samp[kSample];
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ ScanLds<NT> scan;
-  __shared__ float wsc[NW][kIdxHeads];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, n = lane & 31;
-  const int row = blockIdx.x, R = a.R, b = row / R;
-  const int vis = a.ctx_len[b] - R + row % R + 1;
-  const int64_t nvis = vis > 0 ? vis : 0;
-  if (t == 0) row_len[row] = (int32_t)nvis;
-  if (thr_in) {  // the caller's threshold
-    if (t == 0) thr[row] = thr_in[row];
-    return;
-  }
-  if (nvis <= kTakeAll) {
-    if (t == 0) thr[row] = -INFINITY;
-    return;
-  }
-  const int ns = nvis > (1 << 18) ? 4096 : 2048;
-  const int S = ns / kBlock;              // sampled pages
-  const int full = (int)(nvis / kBlock);  // pages whose 64 keys the row all sees (> 128)
-  const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
-
-  QueryRaw<false, KF4> qraw;
-  fetch_query<false, KF4>(a, row, n, g, qraw);
-  const uint32_t wbits = a.w[(size_t)row * kIdxHeads + n];
-  i32x8 A[2][2];
-  const float head_scale = finish_query(qraw, A);
-  if (g == 0) wsc[wave][n] = __uint_as_float(wbits << 16) * head_scale;
-  __syncthreads();
-  float wv[16];  // the weights of the 16 heads this lane reduces (as in the scorer)
-#pragma unroll
-  for (int i = 0; i < 16; ++i) wv[i] = wsc[wave][8 * (i >> 2) + 4 * g + (i & 3)];
-
-  for (int j0 = wave * PPW; j0 < S; j0 += NW * PPW) {
-    int32_t pid[PPW];
-#pragma unroll
-    for (int q = 0; q < PPW; ++q) pid[q] = table[(int64_t)(j0 + q) * full / S];
-    // B operands of keys 32h + n (lane half g, step s: dims 64g + 32s + [0, 32);
-    // MXFP4: the 16-byte MX block 2g + s and its E8M0 scale) and key scales
-    i32x8 Bk[PPW][2][2];
-    int SB[PPW][2][2];
-    float ks[PPW][2];
-#pragma unroll
-    for (int q = 0; q < PPW; ++q) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const size_t key = (size_t)pid[q] * kBlock + 32 * h + n;
-        if constexpr (KF4) {
-          const uint8_t* kp = a.key_fp4 + key * (kIdxDim / 2);
-          const uint32_t sw = *reinterpret_cast<const uint32_t*>(a.key_e8m0 + key * 4);
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(kp + 16 * (2 * g + st));
-            Bk[q][h][st] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-            SB[q][h][st] = (int)((sw >> (8 * (2 * g + st))) & 0xffu);
-          }
-          ks[q][h] = 1.f;
-        } else {
-          const uint8_t* kp = a.key_fp8 + key * kIdxDim + 64 * g;
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kp + 32 * st);
-            const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kp + 32 * st + 16);
-            Bk[q][h][st] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                                 (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-            SB[q][h][st] = 127;
-          }
-          ks[q][h] = a.key_scale[key];
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < PPW; ++q) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-            acc = KF4 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[tt][st], Bk[q][h][st], acc, 0, 4, 0, 127,
-                                                                       0, SB[q][h][st])
-                      : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[tt][st], Bk[q][h][st], acc, 0, 0, 0, 0,
-                                                                       0, 0);
-        float sum = 0.f;
-#pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) sum = __builtin_fmaf(wv[i2], relu(acc[i2]), sum);
-        const float v = halves_sum_pair(sum, sum) * ks[q][h];
-        if (g == 0) samp[(j0 + q) * kBlock + 32 * h + n] = v;
-      }
-    }
-  }
-  __syncthreads();
-  uint32_t raw[kSample / NT];
-#pragma unroll
-  for (int i = 0; i < kSample / NT; ++i) raw[i] = t + NT * i < ns ? __float_as_uint(samp[t + NT * i]) : 0u;
-  const uint32_t T = sample_select<NT>(raw, nvis, k, hist, scan);
-  if (t == 0) thr[row] = key_threshold_float(T);
-}
-
-hipError_t launch_sample_threshold(const ScoreArgs& a, int rows, int k, const float* thr_in, float* thr,
-                                   int32_t* row_len, hipStream_t st) {
-  if (a.key_fp4)
-    hipLaunchKernelGGL(sample_threshold_kernel<true>, dim3(rows), dim3(kSampleThreads), 0, st, a, k, thr_in, thr,
-                       row_len);
-  else
-    hipLaunchKernelGGL(sample_threshold_kernel<false>, dim3(rows), dim3(kSampleThreads), 0, st, a, k, thr_in, thr,
-                       row_len);
-  return hipGetLastError();
 }
 
 // Workgroups of a variant that fit one CU at once (registers, LDS), from
@@ -706,45 +462,45 @@ static long long grid_x(int B, int R, int max_ctx) {
 }
 
 template <int RPW, bool QFP8, bool KF4, bool FILT>
-static void launch_variant(const ScoreArgs& a, int B, int max_ctx, hipStream_t st, int* gx) {
+static void launch_variant(const ScoreArgs& a, int B, int max_ctx, hipStream_t st) {
   const int groups = (a.R + 4 * RPW - 1) / (4 * RPW);
   const long long G = grid_x<RPW, QFP8, KF4, FILT>(B, a.R, max_ctx);
-  if (gx) *gx = (int)G;
   hipLaunchKernelGGL((score_kernel<RPW, QFP8, KF4, FILT>), dim3((unsigned)G, 1, groups), dim3(kThreads), 0, st, a,
                      B);
 }
 
 template <bool KF4>
-static void launch_format(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st, int* gx) {
+static void launch_format(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st) {
   // Rows per wave: one for decode-sized requests; more when a request brings
   // many FP8 query rows (prefill chunks), so that more rows share each page.
   if (q_fp8) {
-    if (a.R > 16) launch_variant<4, true, KF4, false>(a, B, max_ctx, st, gx);
-    else if (a.R > 4) launch_variant<2, true, KF4, false>(a, B, max_ctx, st, gx);
-    else launch_variant<1, true, KF4, false>(a, B, max_ctx, st, gx);
+    if (a.R > 16) launch_variant<4, true, KF4, false>(a, B, max_ctx, st);
+    else if (a.R > 4) launch_variant<2, true, KF4, false>(a, B, max_ctx, st);
+    else launch_variant<1, true, KF4, false>(a, B, max_ctx, st);
   } else if (a.cand) {  // filtered decode
-    if (a.R > 4) launch_variant<2, false, KF4, true>(a, B, max_ctx, st, gx);
-    else launch_variant<1, false, KF4, true>(a, B, max_ctx, st, gx);
+    if (a.R > 4) launch_variant<2, false, KF4, true>(a, B, max_ctx, st);
+    else launch_variant<1, false, KF4, true>(a, B, max_ctx, st);
   } else {
     // up to 8 verification rows read each page once
-    if (a.R > 4) launch_variant<2, false, KF4, false>(a, B, max_ctx, st, gx);
-    else launch_variant<1, false, KF4, false>(a, B, max_ctx, st, gx);
+    if (a.R > 4) launch_variant<2, false, KF4, false>(a, B, max_ctx, st);
+    else launch_variant<1, false, KF4, false>(a, B, max_ctx, st);
   }
 }
 
-hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st, int* gx) {
-  if (a.key_fp4) launch_format<true>(a, B, max_ctx, q_fp8, st, gx);
-  else launch_format<false>(a, B, max_ctx, q_fp8, st, gx);
+hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st) {
+  if (a.key_fp4) launch_format<true>(a, B, max_ctx, q_fp8, st);
+  else launch_format<false>(a, B, max_ctx, q_fp8, st);
   return hipGetLastError();
 }
 
+
 template <bool KF4>
-static int filter_grid_x(int B, int R, int max_ctx) {
+static int filter_grid_fmt(int B, int R, int max_ctx) {
   return (int)(R > 4 ? grid_x<2, false, KF4, true>(B, R, max_ctx) : grid_x<1, false, KF4, true>(B, R, max_ctx));
 }
 
-int index_score_grid_x(int B, int R, int max_ctx, bool mxfp4) {
-  return mxfp4 ? filter_grid_x<true>(B, R, max_ctx) : filter_grid_x<false>(B, R, max_ctx);
+int filter_grid(int B, int R, int max_ctx, bool mxfp4) {
+  return mxfp4 ? filter_grid_fmt<true>(B, R, max_ctx) : filter_grid_fmt<false>(B, R, max_ctx);
 }
 
 }  // namespace dsa

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "common.h"
+#include "kernels.h"
 
 namespace dsa {
 
@@ -252,10 +253,11 @@ DSA_DEV void sample_load(const float* __restrict__ s, int64_t n, uint32_t (&raw)
 // is kept (T = 0) for rows of at most kTakeAll elements.
 template <int NT>
 DSA_DEV uint32_t sample_select(const uint32_t (&raw)[kSample / NT], int64_t n, int k, uint32_t* hist,
-                               ScanLds<NT>& scan) {
+                               ScanLds<NT>& scan, int ns_given = 0) {
   const int t = threadIdx.x;
   if (n <= kTakeAll) return 0u;
-  const int ns = n > (1 << 18) ? 4096 : 2048;
+  // ns_given: the number of samples when the caller drew its own
+  const int ns = ns_given > 0 ? ns_given : (n > (1 << 18) ? 4096 : 2048);
   const int per = ns / NT;
   uint32_t key[kSample / NT];
 #pragma unroll
@@ -319,6 +321,208 @@ DSA_DEV uint32_t sample_select(const uint32_t (&raw)[kSample / NT], int64_t n, i
 // every number's key, where every score passes.
 DSA_DEV float key_threshold_float(uint32_t T) {
   return T <= ordered_key(-INFINITY) ? -INFINITY : __uint_as_float((T & 0x80000000u) ? (T & 0x7fffffffu) : ~T);
+}
+
+// ------------------------------------------------------------------ exact selection
+
+static constexpr int kTF = 1024;  // threads of a selecting workgroup
+
+static constexpr int kBinLds = 2048;  // threshold-bin elements kept for the last steps
+
+// LDS of select_top (one workgroup of kTF threads).
+struct SelectLds {
+  ScanLds<kTF> scan;
+  MinMaxLds<kTF> mm;
+  uint32_t emitted;
+  uint32_t nbin;
+  uint32_t hist[kHistBins];
+  uint64_t bin[kBinLds];
+};
+
+
+// Emit the positions of the k largest composites among `count` elements
+// (comp_at(i) gives element i's composite).
+//  1. The radix digits start below the bits every element shares (the
+//     survivors of one row have close scores: their top bits would all fall
+//     in one bin).
+//  2. One 11-bit step finds the bin b holding the k-th largest; a second
+//     pass emits everything above b and gathers b's elements into LDS.
+//  3. Further 11-bit steps over the gathered elements resolve the rest
+//     (without the gather, when b holds more than kBinLds elements).
+// Where the i-th selected position goes: out[i], and with a page table also
+// its physical cache slot (page id * 64 + offset) to slots[i].
+struct Emit {
+  int32_t* out;
+  int32_t* slots;      // or null
+  const int32_t* tbl;  // page ids of the row's request (LDS), when slots is set
+  DSA_DEV void operator()(uint32_t i, uint32_t pos) const {
+    out[i] = (int32_t)pos;
+    if (slots) slots[i] = tbl[pos >> 6] * kBlock + (int32_t)(pos & 63);
+  }
+};
+
+// With have_bounds, [lo0, hi0] is given to hold every composite (the pass
+// that finds the exact extremes is skipped).
+template <class CompAt>
+DSA_DEV void select_top(SelectLds& L, int64_t count, int k, const Emit& out, CompAt comp_at,
+                        bool have_bounds = false, uint64_t lo0 = 0, uint64_t hi0 = 0) {
+  const int t = threadIdx.x;
+  uint64_t lo = lo0, hi = hi0;
+  if (!have_bounds) {
+    lo = ~0ull;
+    hi = 0;
+    for (int64_t i = t; i < count; i += kTF) {
+      const uint64_t c = comp_at(i);
+      lo = c < lo ? c : lo;
+      hi = c > hi ? c : hi;
+    }
+    block_minmax<kTF>(lo, hi, L.mm);
+  }
+  if (t == 0) {
+    L.emitted = 0;
+    L.nbin = 0;
+  }
+  // the composites are distinct, so lo == hi only for a single element
+  if (lo == hi) {
+    if (t == 0) out(0, ~(uint32_t)hi);
+    return;
+  }
+  int shift = 64 - __clzll((long long)(lo ^ hi));  // bits below the shared prefix
+  uint64_t prefix = shift == 64 ? 0 : hi >> shift;
+  uint32_t need = (uint32_t)k;
+
+  // step over all elements
+  int width = shift < 11 ? shift : 11;
+  int lo_bit = shift - width;
+  for (int i = t; i < kHistBins; i += kTF) L.hist[i] = 0;
+  __syncthreads();
+  for (int64_t i = t; i < count; i += kTF)
+    atomicAdd(&L.hist[(comp_at(i) >> lo_bit) & ((1ull << width) - 1)], 1u);
+  __syncthreads();
+  uint32_t cnt[kHistBins / kTF];
+  load_bins<kTF>(L.hist, cnt);
+  Thresh th = block_threshold<kTF>(cnt, need, L.scan);
+  const uint64_t b = (shift == 64 ? 0 : prefix << width) | (uint64_t)th.digit;  // top (64 - b_shift) bits
+  const int b_shift = lo_bit;
+  const bool gather = th.at <= (uint32_t)kBinLds;
+  // emit everything above b; gather b. Each thread counts its elements of
+  // both kinds first, so that a wave reserves its slots with one atomic per
+  // kind instead of one per pass over 1024 elements.
+  {
+    uint32_t na = 0, nb = 0;
+    for (int64_t i = t; i < count; i += kTF) {
+      const uint64_t c = comp_at(i);
+      na += (uint32_t)((c >> b_shift) > b);
+      nb += (uint32_t)(gather && (c >> b_shift) == b);
+    }
+    const uint32_t ia = wave_incl_sum(na), ib = wave_incl_sum(nb);
+    uint32_t sa = wave_reserve(&L.emitted, __builtin_amdgcn_readlane(ia, 63)) + ia - na;
+    uint32_t sb = wave_reserve(&L.nbin, __builtin_amdgcn_readlane(ib, 63)) + ib - nb;
+    for (int64_t i = t; i < count; i += kTF) {
+      const uint64_t c = comp_at(i);
+      if ((c >> b_shift) > b) {
+        if (sa < (uint32_t)k) out(sa, ~(uint32_t)c);
+        ++sa;
+      } else if (gather && (c >> b_shift) == b) {
+        if (sb < (uint32_t)kBinLds) L.bin[sb] = c;
+        ++sb;
+      }
+    }
+  }
+  __syncthreads();
+  need -= th.above;
+  const uint32_t emitted0 = th.above;
+  if (th.at == need) {  // all of b is selected
+    if (gather) {
+      for (uint32_t i = t; i < th.at && emitted0 + i < (uint32_t)k; i += kTF)
+        out(emitted0 + i, ~(uint32_t)L.bin[i]);
+    } else {
+      if (t == 0) L.emitted = 0;
+      __syncthreads();
+      for (int64_t base = 0; base < count; base += kTF) {
+        const int64_t i = base + t;
+        bool take = false;
+        uint64_t c = 0;
+        if (i < count) {
+          c = comp_at(i);
+          take = (c >> b_shift) == b;
+        }
+        const uint32_t slot = wave_append(&L.emitted, take);
+        if (take && emitted0 + slot < (uint32_t)k) out(emitted0 + slot, ~(uint32_t)c);
+      }
+    }
+    return;
+  }
+  // resolve within b: element j of the bin is bin_at(j)
+  const int64_t nb = gather ? (int64_t)th.at : count;
+  auto bin_at = [&](int64_t j) -> uint64_t { return gather ? L.bin[j] : comp_at(j); };
+  prefix = b;
+  shift = lo_bit;
+  while (true) {
+    width = shift < 11 ? shift : 11;
+    lo_bit = shift - width;
+    for (int i = t; i < kHistBins; i += kTF) L.hist[i] = 0;
+    __syncthreads();
+    for (int64_t j = t; j < nb; j += kTF) {
+      const uint64_t c = bin_at(j);
+      if ((c >> shift) == prefix) atomicAdd(&L.hist[(c >> lo_bit) & ((1ull << width) - 1)], 1u);
+    }
+    __syncthreads();
+    load_bins<kTF>(L.hist, cnt);
+    th = block_threshold<kTF>(cnt, need, L.scan);
+    need -= th.above;
+    prefix = (prefix << width) | (uint64_t)th.digit;
+    shift = lo_bit;
+    if (th.at == need || shift == 0) break;
+  }
+  if (t == 0) L.emitted = 0;
+  __syncthreads();
+  // elements of b whose top (64 - shift) bits are at least the resolved prefix
+  for (int64_t base = 0; base < nb; base += kTF) {
+    const int64_t j = base + t;
+    bool take = false;
+    uint64_t c = 0;
+    if (j < nb) {
+      c = bin_at(j);
+      take = (gather || (c >> b_shift) == b) && (c >> shift) >= prefix;
+    }
+    const uint32_t slot = wave_append(&L.emitted, take);
+    if (take && emitted0 + slot < (uint32_t)k) out(emitted0 + slot, ~(uint32_t)c);
+  }
+}
+
+// Rows of at most k visible positions: all of them, then -1 padding (and
+// their physical slots when asked for).
+DSA_DEV void emit_all_positions(int row, int R, int64_t n, int k, int32_t* out, const SlotOut& so) {
+  const int t = threadIdx.x;
+  for (int64_t i = t; i < k; i += kTF) out[i] = i < n ? (int32_t)i : -1;
+  if (so.slots) {
+    const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
+    for (int i = t; i < k; i += kTF)
+      so.slots[(size_t)row * k + i] = i < n && (i >> 6) < so.max_blocks ? table[i >> 6] * kBlock + (i & 63) : -1;
+  }
+}
+
+// Physical slots of a row's written selection (rows this long have too many
+// pages to stage their table in LDS): every thread translates its entries
+// with all its loads in flight. The caller makes `out` workgroup-visible.
+DSA_DEV void emit_slots(int row, int R, int k, const int32_t* out, const SlotOut& so) {
+  const int t = threadIdx.x;
+  const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
+  constexpr int kPer = (kMaxTopk + kTF - 1) / kTF;
+  int32_t pos[kPer], page[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = t + j * kTF;
+    pos[j] = i < k ? out[i] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) page[j] = pos[j] >= 0 && (pos[j] >> 6) < so.max_blocks ? table[pos[j] >> 6] : -1;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = t + j * kTF;
+    if (i < k) so.slots[(size_t)row * k + i] = page[j] >= 0 ? page[j] * kBlock + (pos[j] & 63) : -1;
+  }
 }
 
 // ------------------------------------------------------------------ scorer work split

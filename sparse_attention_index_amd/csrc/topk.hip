@@ -33,7 +33,6 @@
 
 namespace dsa {
 
-static constexpr int kTF = 1024;         // threads per final workgroup
 static constexpr int kFinalLds = 12288;  // candidates the final kernel holds in LDS
 static constexpr int kMaxSlices = 64;    // filter workgroups per row at most
 
@@ -74,18 +73,6 @@ TopkWs topk_ws_carve(void* ws, int rows, int64_t max_len) {
 
 // ------------------------------------------------------------------ final
 
-static constexpr int kBinLds = 2048;  // threshold-bin elements kept for the last steps
-
-// LDS of select_top (one workgroup of kTF threads).
-struct SelectLds {
-  ScanLds<kTF> scan;
-  MinMaxLds<kTF> mm;
-  uint32_t emitted;
-  uint32_t nbin;
-  uint32_t hist[kHistBins];
-  uint64_t bin[kBinLds];
-};
-
 struct FinalLds {
   SelectLds s;
   uint32_t off[kMaxSlices];
@@ -93,157 +80,6 @@ struct FinalLds {
   uint32_t bad;
   uint2 elems[kFinalLds];
 };
-
-// Emit the positions of the k largest composites among `count` elements
-// (comp_at(i) gives element i's composite).
-//  1. The radix digits start below the bits every element shares (the
-//     survivors of one row have close scores: their top bits would all fall
-//     in one bin).
-//  2. One 11-bit step finds the bin b holding the k-th largest; a second
-//     pass emits everything above b and gathers b's elements into LDS.
-//  3. Further 11-bit steps over the gathered elements resolve the rest
-//     (without the gather, when b holds more than kBinLds elements).
-// Where the i-th selected position goes: out[i], and with a page table also
-// its physical cache slot (page id * 64 + offset) to slots[i].
-struct Emit {
-  int32_t* out;
-  int32_t* slots;      // or null
-  const int32_t* tbl;  // page ids of the row's request (LDS), when slots is set
-  DSA_DEV void operator()(uint32_t i, uint32_t pos) const {
-    out[i] = (int32_t)pos;
-    if (slots) slots[i] = tbl[pos >> 6] * kBlock + (int32_t)(pos & 63);
-  }
-};
-
-// With have_bounds, [lo0, hi0] is given to hold every composite (the pass
-// that finds the exact extremes is skipped).
-template <class CompAt>
-DSA_DEV void select_top(SelectLds& L, int64_t count, int k, const Emit& out, CompAt comp_at,
-                        bool have_bounds = false, uint64_t lo0 = 0, uint64_t hi0 = 0) {
-  const int t = threadIdx.x;
-  uint64_t lo = lo0, hi = hi0;
-  if (!have_bounds) {
-    lo = ~0ull;
-    hi = 0;
-    for (int64_t i = t; i < count; i += kTF) {
-      const uint64_t c = comp_at(i);
-      lo = c < lo ? c : lo;
-      hi = c > hi ? c : hi;
-    }
-    block_minmax<kTF>(lo, hi, L.mm);
-  }
-  if (t == 0) {
-    L.emitted = 0;
-    L.nbin = 0;
-  }
-  // the composites are distinct, so lo == hi only for a single element
-  if (lo == hi) {
-    if (t == 0) out(0, ~(uint32_t)hi);
-    return;
-  }
-  int shift = 64 - __clzll((long long)(lo ^ hi));  // bits below the shared prefix
-  uint64_t prefix = shift == 64 ? 0 : hi >> shift;
-  uint32_t need = (uint32_t)k;
-
-  // step over all elements
-  int width = shift < 11 ? shift : 11;
-  int lo_bit = shift - width;
-  for (int i = t; i < kHistBins; i += kTF) L.hist[i] = 0;
-  __syncthreads();
-  for (int64_t i = t; i < count; i += kTF)
-    atomicAdd(&L.hist[(comp_at(i) >> lo_bit) & ((1ull << width) - 1)], 1u);
-  __syncthreads();
-  uint32_t cnt[kHistBins / kTF];
-  load_bins<kTF>(L.hist, cnt);
-  Thresh th = block_threshold<kTF>(cnt, need, L.scan);
-  const uint64_t b = (shift == 64 ? 0 : prefix << width) | (uint64_t)th.digit;  // top (64 - b_shift) bits
-  const int b_shift = lo_bit;
-  const bool gather = th.at <= (uint32_t)kBinLds;
-  // emit everything above b; gather b. Each thread counts its elements of
-  // both kinds first, so that a wave reserves its slots with one atomic per
-  // kind instead of one per pass over 1024 elements.
-  {
-    uint32_t na = 0, nb = 0;
-    for (int64_t i = t; i < count; i += kTF) {
-      const uint64_t c = comp_at(i);
-      na += (uint32_t)((c >> b_shift) > b);
-      nb += (uint32_t)(gather && (c >> b_shift) == b);
-    }
-    const uint32_t ia = wave_incl_sum(na), ib = wave_incl_sum(nb);
-    uint32_t sa = wave_reserve(&L.emitted, __builtin_amdgcn_readlane(ia, 63)) + ia - na;
-    uint32_t sb = wave_reserve(&L.nbin, __builtin_amdgcn_readlane(ib, 63)) + ib - nb;
-    for (int64_t i = t; i < count; i += kTF) {
-      const uint64_t c = comp_at(i);
-      if ((c >> b_shift) > b) {
-        if (sa < (uint32_t)k) out(sa, ~(uint32_t)c);
-        ++sa;
-      } else if (gather && (c >> b_shift) == b) {
-        if (sb < (uint32_t)kBinLds) L.bin[sb] = c;
-        ++sb;
-      }
-    }
-  }
-  __syncthreads();
-  need -= th.above;
-  const uint32_t emitted0 = th.above;
-  if (th.at == need) {  // all of b is selected
-    if (gather) {
-      for (uint32_t i = t; i < th.at && emitted0 + i < (uint32_t)k; i += kTF)
-        out(emitted0 + i, ~(uint32_t)L.bin[i]);
-    } else {
-      if (t == 0) L.emitted = 0;
-      __syncthreads();
-      for (int64_t base = 0; base < count; base += kTF) {
-        const int64_t i = base + t;
-        bool take = false;
-        uint64_t c = 0;
-        if (i < count) {
-          c = comp_at(i);
-          take = (c >> b_shift) == b;
-        }
-        const uint32_t slot = wave_append(&L.emitted, take);
-        if (take && emitted0 + slot < (uint32_t)k) out(emitted0 + slot, ~(uint32_t)c);
-      }
-    }
-    return;
-  }
-  // resolve within b: element j of the bin is bin_at(j)
-  const int64_t nb = gather ? (int64_t)th.at : count;
-  auto bin_at = [&](int64_t j) -> uint64_t { return gather ? L.bin[j] : comp_at(j); };
-  prefix = b;
-  shift = lo_bit;
-  while (true) {
-    width = shift < 11 ? shift : 11;
-    lo_bit = shift - width;
-    for (int i = t; i < kHistBins; i += kTF) L.hist[i] = 0;
-    __syncthreads();
-    for (int64_t j = t; j < nb; j += kTF) {
-      const uint64_t c = bin_at(j);
-      if ((c >> shift) == prefix) atomicAdd(&L.hist[(c >> lo_bit) & ((1ull << width) - 1)], 1u);
-    }
-    __syncthreads();
-    load_bins<kTF>(L.hist, cnt);
-    th = block_threshold<kTF>(cnt, need, L.scan);
-    need -= th.above;
-    prefix = (prefix << width) | (uint64_t)th.digit;
-    shift = lo_bit;
-    if (th.at == need || shift == 0) break;
-  }
-  if (t == 0) L.emitted = 0;
-  __syncthreads();
-  // elements of b whose top (64 - shift) bits are at least the resolved prefix
-  for (int64_t base = 0; base < nb; base += kTF) {
-    const int64_t j = base + t;
-    bool take = false;
-    uint64_t c = 0;
-    if (j < nb) {
-      c = bin_at(j);
-      take = (gather || (c >> b_shift) == b) && (c >> shift) >= prefix;
-    }
-    const uint32_t slot = wave_append(&L.emitted, take);
-    if (take && emitted0 + slot < (uint32_t)k) out(emitted0 + slot, ~(uint32_t)c);
-  }
-}
 
 // ------------------------------------------------------------------ short rows
 
@@ -500,40 +336,6 @@ __global__ __launch_bounds__(kT) void topk_slice_kernel(const float* __restrict_
   }
 }
 
-// Rows of at most k visible positions: all of them, then -1 padding (and
-// their physical slots when asked for).
-DSA_DEV void emit_all_positions(int row, int R, int64_t n, int k, int32_t* out, const SlotOut& so) {
-  const int t = threadIdx.x;
-  for (int64_t i = t; i < k; i += kTF) out[i] = i < n ? (int32_t)i : -1;
-  if (so.slots) {
-    const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
-    for (int i = t; i < k; i += kTF)
-      so.slots[(size_t)row * k + i] = i < n && (i >> 6) < so.max_blocks ? table[i >> 6] * kBlock + (i & 63) : -1;
-  }
-}
-
-// Physical slots of a row's written selection (rows this long have too many
-// pages to stage their table in LDS): every thread translates its entries
-// with all its loads in flight. The caller makes `out` workgroup-visible.
-DSA_DEV void emit_slots(int row, int R, int k, const int32_t* out, const SlotOut& so) {
-  const int t = threadIdx.x;
-  const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
-  constexpr int kPer = (kMaxTopk + kTF - 1) / kTF;
-  int32_t pos[kPer], page[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = t + j * kTF;
-    pos[j] = i < k ? out[i] : -1;
-  }
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) page[j] = pos[j] >= 0 && (pos[j] >> 6) < so.max_blocks ? table[pos[j] >> 6] : -1;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = t + j * kTF;
-    if (i < k) so.slots[(size_t)row * k + i] = page[j] >= 0 ? page[j] * kBlock + (pos[j] & 63) : -1;
-  }
-}
-
 // One workgroup per row gathers the slices' survivors (a kernel boundary
 // orders the slice workgroups' writes before these reads; a device-scope fence
 // per workgroup would write back each XCD's L2). Every survivor lies in
@@ -606,140 +408,6 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
     __syncthreads();  // the selection is written (workgroup-visible)
     emit_slots(row, R, k, out, so);
   }
-}
-
-// ------------------------------------------------------------------ filtered decode
-
-// The decode scorer (filter mode) leaves, per row and scoring workgroup, the
-// (ordered key, position) of every score >= the row's sampled threshold T in
-// the workgroup's own region of the row's candidate buffer, with its true
-// count. One workgroup per row here gathers them into LDS and selects the k
-// largest composites. The selection is exact whenever no region overflowed
-// and at least k candidates arrived: the k-th largest score is then >= T, so
-// every element of the top k was kept. Otherwise the row is flagged for the
-// fallback (whole-row scoring and selection) and nothing else is written.
-struct CandLds {
-  SelectLds s;
-  uint32_t off[kMaxFilterWg];
-  uint32_t wsum[kTF / 64];
-  uint32_t wmax[kTF / 64];
-  uint2 elems[kFinalLds];
-};
-
-__global__ __launch_bounds__(kTF) void candidate_select_kernel(const uint2* __restrict__ cand,
-                                                               const uint32_t* __restrict__ cnt, int cap,
-                                                               int cnt_stride, const int32_t* __restrict__ ctx_len,
-                                                               int B, int G, const float* __restrict__ thr,
-                                                               const int32_t* __restrict__ row_len, int R, int k,
-                                                               int32_t* __restrict__ idx, uint32_t* row_fail,
-                                                               SlotOut so) {
-  __shared__ CandLds L;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int row = blockIdx.x;
-  const int64_t n = row_len[row];  // published by the sampling pass
-  int32_t* out = idx + (size_t)row * k;
-  if (n <= k) {  // every visible position is selected; the rest is padding
-    emit_all_positions(row, R, n, k, out, so);
-    if (t == 0) row_fail[row] = 0u;
-    return;
-  }
-  // the scoring workgroups of this row's request, as the scorer split them
-  const WgRange wr = wg_range(ctx_len, B, G, 0, row / R);
-  const int nw = wr.count;  // <= kMaxFilterWg (checked by the host)
-  const uint32_t sub = (uint32_t)(cap / nw);
-  const uint32_t c = t < nw ? cnt[(size_t)row * cnt_stride + t] : 0u;
-  const uint32_t incl = wave_incl_sum(c);
-  if (lane == 63) L.wsum[wave] = incl;
-  const int bad = __syncthreads_or(c > sub);
-  uint32_t before = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < kTF / 64; ++w) {
-    const uint32_t x = L.wsum[w];
-    before += w < wave ? x : 0u;
-    total += x;
-  }
-  if (t < nw) L.off[t] = before + incl - c;
-  // every candidate v has v >= thr, so its key is >= ordered_key(thr)
-  const uint32_t T = ordered_key(thr[row]);
-  __syncthreads();
-  const bool ok = !bad && total >= (uint32_t)k && total <= (uint32_t)kFinalLds;
-  if (t == 0) row_fail[row] = ok ? 0u : 1u;
-  if (!ok) return;  // uniform
-  // element i sits in the last workgroup region whose offset is <= i; eight
-  // loads in flight per lane
-  const uint2* base = cand + (size_t)row * cap;
-  uint32_t kmax = 0;
-  for (uint32_t b0 = 0; b0 < total; b0 += 8 * kTF) {
-    uint2 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t i = b0 + t + j * kTF;
-      v[j] = make_uint2(0u, 0u);
-      if (i < total) {
-        int sl = 0;
-#pragma unroll
-        for (int step = kMaxFilterWg / 2; step >= 1; step >>= 1)
-          if (sl + step < nw && L.off[sl + step] <= i) sl += step;
-        v[j] = base[(size_t)sl * sub + (i - L.off[sl])];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t i = b0 + t + j * kTF;
-      if (i < total) {
-        L.elems[i] = v[j];
-        kmax = max(kmax, v[j].x);
-      }
-    }
-  }
-  const uint32_t wm = wave_max32(kmax);
-  if (lane == 0) L.wmax[wave] = wm;
-  __syncthreads();
-  kmax = wave_max32(lane < kTF / 64 ? L.wmax[lane] : 0u);
-  const Emit emit{out, nullptr, nullptr};
-  select_top(
-      L.s, total, k, emit, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); }, true,
-      (uint64_t)T << 32, ((uint64_t)kmax << 32) | 0xffffffffull);
-  if (so.slots) {
-    __syncthreads();  // the selection is written (workgroup-visible)
-    emit_slots(row, R, k, out, so);
-  }
-}
-
-// Fallback of the filtered decode: a flagged row selects over its whole
-// score row (written by the fallback scoring); other rows return at once.
-__global__ __launch_bounds__(kTF) void topk_failed_rows_kernel(const float* __restrict__ scores, int64_t ld,
-                                                               const int32_t* __restrict__ row_len, int R, int k,
-                                                               int32_t* __restrict__ idx,
-                                                               const uint32_t* __restrict__ row_fail, SlotOut so) {
-  __shared__ SelectLds L;
-  const int row = blockIdx.x;
-  if (row_fail[row] == 0u) return;
-  const int64_t n = visible_len(row_len, nullptr, 1, row, ld);
-  int32_t* out = idx + (size_t)row * k;
-  const float* s = scores + (size_t)row * ld;
-  const Emit emit{out, nullptr, nullptr};
-  select_top(L, n, k, emit, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
-  if (so.slots) {
-    __syncthreads();
-    emit_slots(row, R, k, out, so);
-  }
-}
-
-hipError_t launch_candidate_select(const uint2* cand, const uint32_t* cnt, int cap, int cnt_stride, int nw_total,
-                                   const int32_t* ctx_len, int B, const float* thr, const int32_t* row_len,
-                                   int rows, int R, int k, int32_t* idx, uint32_t* row_fail, const SlotOut& so,
-                                   hipStream_t st) {
-  hipLaunchKernelGGL(candidate_select_kernel, dim3(rows), dim3(kTF), 0, st, cand, cnt, cap, cnt_stride, ctx_len, B,
-                     nw_total, thr, row_len, R, k, idx, row_fail, so);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_failed_rows(const float* scores, int64_t ld, const int32_t* row_len, int rows, int R, int k,
-                                   int32_t* idx, const uint32_t* row_fail, const SlotOut& so, hipStream_t st) {
-  hipLaunchKernelGGL(topk_failed_rows_kernel, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, R, k, idx, row_fail,
-                     so);
-  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ launcher

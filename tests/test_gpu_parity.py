@@ -39,6 +39,9 @@ FUSED_ONLY = {
     # scoring workgroups split in proportion to the lengths
     "5x3_filtered_ragged": dict(B=5, R=3, lengths=[41000, 60000, 1900, 45000, 90000], seed=113,
                                 permute_blocks=True),
+    # 160 rows: the smaller candidate buffer per row, few scoring workgroups
+    # per request (a -inf threshold overflows their regions)
+    "40x4_many_rows": dict(B=40, R=4, lengths=[45000 + 97 * b for b in range(40)], seed=114, device="cuda"),
 }
 
 
@@ -296,16 +299,20 @@ def _kth_scores(case, k):
     return torch.topk(s, min(k, n), dim=1).values[:, -1].contiguous()
 
 
-@pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "1x1_8k"])
-def test_thresholded_decode_equals_decode_whatever_the_threshold(gpu, name):
-    """The filtered decode with caller-given thresholds: too high (+inf, NaN,
-    just above the k-th score: fewer than k candidates) and too low (-inf: more
-    candidates than fit) send rows to the exact fallback (full scores, whole-row
-    selection); exactly the k-th score decides from the candidates. Every
-    variant, and a per-row mix of them, selects dsa_decode's set."""
+@pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "1x1_8k", "40x4_many_rows"])
+def test_thresholded_decode_equals_the_staged_path_whatever_the_threshold(gpu, name):
+    """The filtered decode with caller-given thresholds against the stored
+    path (dsa_index_score -> dsa_topk -> dsa_sparse_mla_decode). Too high a
+    threshold (+inf, NaN, just above the k-th score: fewer than k
+    candidates) sends rows to the exact fallback (full scores, whole-row
+    selection); -inf keeps every score (selected from a compacted copy past
+    what LDS holds, or, where a workgroup's region overflows, by the
+    fallback); exactly the k-th score decides from the candidates. Every
+    variant, and a per-row mix of them, selects the staged set."""
     case = _case(name)
     k = case.topk
-    ref_out, ref_lse, ref_idx = gpu_decode(case)
+    ref_idx = gpu_topk(gpu_scores(case, sentinel=0.0), row_len_of(case), k)
+    ref_out, ref_lse = gpu_mla(case, ref_idx)
     ref_idx = ref_idx.cpu().numpy()
     kth = _kth_scores(case, k)
     rows = case.rows
