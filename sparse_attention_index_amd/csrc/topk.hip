@@ -22,6 +22,7 @@
 //          candidate buffer, with its count in its own slot: no global
 //          atomics and nothing to clear first;
 //  final   one workgroup per row gathers the slices' candidates into LDS
+//          (a slice that overflowed its region is read again from the row)
 //          and radix-selects the k largest composites. The answer is exact
 //          whenever at least k candidates were collected, because every
 //          element of the top k is then >= T; if fewer than k or more than
@@ -75,9 +76,10 @@ TopkWs topk_ws_carve(void* ws, int rows, int64_t max_len) {
 
 struct FinalLds {
   SelectLds s;
-  uint32_t off[kMaxSlices];
-  uint32_t total;
-  uint32_t bad;
+  uint32_t off[kMaxSlices + 1];  // each slice's first survivor in the row's run; the total last
+  uint32_t cnt[kMaxSlices];      // each slice's survivors
+  uint32_t fill;                 // survivors of an overflowed slice found again so far
+  uint32_t kmax;                 // the row's largest key
   uint2 elems[kFinalLds];
 };
 
@@ -338,14 +340,19 @@ __global__ __launch_bounds__(kT) void topk_slice_kernel(const float* __restrict_
 
 // One workgroup per row gathers the slices' survivors (a kernel boundary
 // orders the slice workgroups' writes before these reads; a device-scope fence
-// per workgroup would write back each XCD's L2). Every survivor lies in
-// [T << 32, (largest key << 32) | ~0], which saves select_top a pass.
+// per workgroup would write back each XCD's L2). A slice whose survivors
+// overflowed its region (they cluster where the row's high scores do, for
+// instance among the most recent positions) is read again from the score row
+// with the slice pass's own test, so the run holds every survivor either way.
+// Every survivor lies in [T << 32, (largest key << 32) | ~0], which saves
+// select_top a pass.
+template <bool VEC>
 __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict__ scores, int64_t ld,
-                                                       const int32_t* __restrict__ row_len, int R, int slices, int k,
-                                                       int32_t* __restrict__ idx, TopkWs w, SlotOut so) {
+                                                       const int32_t* __restrict__ row_len, int R, int slices,
+                                                       int slice, int k, int32_t* __restrict__ idx, TopkWs w,
+                                                       SlotOut so) {
   __shared__ FinalLds L;
-  __shared__ uint32_t kmax_s;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int row = blockIdx.x;
   const int64_t n = visible_len(row_len, nullptr, 1, row, ld);  // published by the slice pass
   int32_t* out = idx + (size_t)row * k;
@@ -354,54 +361,96 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
     return;
   }
   const Emit emit{out, nullptr, nullptr};
-  // slices' counts and their offsets in LDS: lane t of wave 0 owns slice t
+  // slices' true counts and their offsets in LDS: lane t of wave 0 owns slice t
   const uint32_t sub = (uint32_t)(w.cap / slices);
   if (t < 64) {
     const uint32_t c = t < slices ? w.cnt[(size_t)row * kMaxSlices + t] : 0u;
     const uint32_t km = t < slices ? w.tmax[(size_t)row * kMaxSlices + t] : 0u;
-    const uint64_t bad = __ballot(c > sub);
     const uint32_t incl = wave_incl_sum(c);
     const uint32_t kmax = wave_max32(km);
-    L.off[t] = incl - c;
-    if (t == 63) L.total = incl;
+    if (t < slices) {
+      L.off[t] = incl - c;
+      L.cnt[t] = c;
+    }
+    if (t == 63) L.off[slices] = incl;
     if (t == 0) {
-      L.bad = bad != 0;
-      kmax_s = kmax;
+      L.kmax = kmax;
+      L.fill = 0;
     }
   }
   const uint32_t T = w.thr[row];
+  const float Tf = key_threshold_float(T);
   __syncthreads();
-  const uint32_t count = L.total;
-  if (!L.bad && count >= (uint32_t)k && count <= (uint32_t)kFinalLds) {
-    // element i sits in the last slice whose offset is <= i; eight loads in
-    // flight per lane
-    const uint2* base = w.cand + (size_t)row * w.cap;
-    for (uint32_t b0 = 0; b0 < count; b0 += 8 * kTF) {
-      uint2 v[8];
+  const uint32_t count = L.off[slices];
+  const float* s = scores + (size_t)row * ld;
+  if (count >= (uint32_t)k && count <= (uint32_t)kFinalLds) {
+    // regions that hold their slice's survivors: wave w copies slices w,
+    // w + 16, ..., four loads in flight per lane
+    const uint2* regions = w.cand + (size_t)row * w.cap;
+    for (int r = wave; r < slices; r += kTF / 64) {
+      const uint32_t o = L.off[r], cr = L.cnt[r];
+      if (cr > sub) continue;  // read again below (wave-uniform)
+      for (uint32_t j0 = 0; j0 < cr; j0 += 256) {
+        uint2 v[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t i = b0 + t + j * kTF;
-        v[j] = make_uint2(0u, 0u);
-        if (i < count) {
-          int sl = 0;
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t j = j0 + 64 * u + lane;
+          v[u] = j < cr ? regions[(size_t)r * sub + j] : make_uint2(0u, 0u);
+        }
 #pragma unroll
-          for (int step = kMaxSlices / 2; step >= 1; step >>= 1)
-            if (sl + step < slices && L.off[sl + step] <= i) sl += step;
-          v[j] = base[(size_t)sl * sub + (i - L.off[sl])];
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t j = j0 + 64 * u + lane;
+          if (j < cr) L.elems[o + j] = v[u];
         }
       }
+    }
+    // overflowed slices: the whole workgroup streams the slice again (16
+    // scores per thread and step) and keeps score >= Tf, as the slice pass
+    // did; at most cr survivors are written
+    for (int r = 0; r < slices; ++r) {
+      const uint32_t cr = L.cnt[r];
+      if (cr <= sub) continue;  // uniform
+      const uint32_t o = L.off[r];
+      const int64_t a0 = (int64_t)r * slice;
+      const int64_t a1 = a0 + slice < n ? a0 + slice : n;
+      for (int64_t base = a0; base < a1; base += 16 * kTF) {
+        float v[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t i = b0 + t + j * kTF;
-        if (i < count) L.elems[i] = v[j];
+        for (int q = 0; q < 4; ++q) {
+          const int64_t p = base + 4 * kTF * q + 4 * t;
+          if (VEC && p + 3 < a1) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(s + p);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = p + e < a1 ? s[p + e] : __builtin_nanf("");
+          }
+        }
+        uint32_t cmask = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) cmask |= (uint32_t)(v[j] >= Tf) << j;  // NaN is never kept
+        uint32_t tc;
+        const uint32_t pc = wave_prefix_small<5>((uint32_t)__popc(cmask), tc);
+        uint32_t slot = wave_reserve(&L.fill, tc) + pc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (cmask & (1u << j)) {
+            const int64_t p = base + 4 * kTF * (j >> 2) + 4 * t + (j & 3);
+            if (slot < cr) L.elems[o + slot] = make_uint2(ordered_key(v[j]), (uint32_t)p);
+            ++slot;
+          }
+        }
       }
+      __syncthreads();  // every wave has reserved from the counter
+      if (t == 0) L.fill = 0;
+      __syncthreads();
     }
     __syncthreads();
     select_top(
         L.s, count, k, emit, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); }, true,
-        (uint64_t)T << 32, ((uint64_t)kmax_s << 32) | 0xffffffffull);
+        (uint64_t)T << 32, ((uint64_t)L.kmax << 32) | 0xffffffffull);
   } else {  // the sample missed: select over the whole row
-    const float* s = scores + (size_t)row * ld;
     select_top(L.s, n, k, emit, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
   }
   if (so.slots) {
@@ -447,7 +496,12 @@ hipError_t launch_topk(const float* scores, int64_t ld, int32_t* row_len, int ro
                        (int)slice, k, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_final_kernel, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, R, ns, k, idx, w, so);
+  if (vec)
+    hipLaunchKernelGGL(topk_final_kernel<true>, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, R, ns, (int)slice,
+                       k, idx, w, so);
+  else
+    hipLaunchKernelGGL(topk_final_kernel<false>, dim3(rows), dim3(kTF), 0, st, scores, ld, row_len, R, ns,
+                       (int)slice, k, idx, w, so);
   return hipGetLastError();
 }
 

@@ -179,6 +179,52 @@ def test_topk_vector_path_reads_a_partial_last_vector(gpu):
         check_topk_exact(idx_h[i], s32[i, : len(r)], k, f"dcp tail row {i}")
 
 
+@pytest.mark.parametrize("aligned", [True, False])
+def test_topk_survivors_clustered_in_few_slices(gpu, aligned):
+    """Long rows whose high scores crowd into a few slices of the row: the
+    survivors of those slices pass the slice workgroups' own candidate
+    regions, and the final pass reads those slices again from the row. The
+    clusters: the most recent 32,768 positions (the decode case), the first
+    20,000, one across the middle, one of exact ties, and one dense enough to
+    hold the whole top k. `aligned` False gives rows with an odd stride that
+    start 4 bytes into the allocation (scalar loads)."""
+    rng = np.random.default_rng(53)
+    L = 1 << 20
+    rows = []
+
+    def planted(lo, hi, frac, value=None):
+        r = rng.standard_normal(L)
+        hit = lo + np.flatnonzero(rng.random(hi - lo) < frac)
+        r[hit] = value if value is not None else 5.0 + rng.random(hit.size)
+        return r
+
+    rows.append(planted(L - 32768, L, 0.1))
+    rows.append(planted(0, 20000, 0.1))
+    rows.append(planted(L // 2 - 9000, L // 2 + 9000, 0.15))
+    rows.append(planted(L - 32768, L, 0.1, value=7.0))
+    rows.append(planted(L - 8192, L, 0.5))
+    lens = [L, L, L - 1, L - 3, L]
+    nrows = len(rows)
+    if aligned:
+        scores = torch.as_tensor(np.stack(rows), dtype=torch.float32).cuda()
+        assert scores.data_ptr() % 16 == 0 and scores.stride(0) % 4 == 0
+    else:
+        base = torch.zeros((nrows, L + 3), dtype=torch.float32)
+        base[:, 1 : L + 1] = torch.as_tensor(np.stack(rows), dtype=torch.float32)
+        scores = base.cuda()[:, 1 : L + 1]
+        assert scores.stride(0) % 2 == 1
+    row_len = torch.tensor(lens, dtype=torch.int32).cuda()
+    print(f"\n[case] topk clustered survivors aligned={aligned}", lens, flush=True)
+    s32 = scores.cpu().numpy()
+    for k in (2048, 500):
+        ws = dsa.workspace(dsa.dsa_workspace_size(dsa.DSA_WS_TOPK, nrows, scores.stride(0), k))
+        idx = torch.full((nrows, k), -7, dtype=torch.int32, device="cuda")
+        dsa.dsa_topk(scores, row_len, k, idx, ws)
+        idx_h = idx.cpu().numpy()
+        for i, n in enumerate(lens):
+            check_topk_exact(idx_h[i], s32[i, :n], k, f"clustered row {i} k {k}")
+
+
 @pytest.mark.parametrize("min_ld", [0, 2 * SHORT_MAX])
 def test_topk_all_ties_pick_lowest_positions(gpu, min_ld):
     scores, row_len = _rows_tensor([np.ones(9000), np.ones(2500)], min_ld=min_ld)
