@@ -37,6 +37,18 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 MALL_BYTES = 256 << 20
+# dsa_decode filters the scores of batches with max_ctx above FILTER_MIN_CTX
+# (csrc/api.hip); the top-k selects rows of at most SHORT_TOPK_MAX scores in
+# one workgroup each (csrc/topk.hip)
+FILTER_MIN_CTX = 40960
+SHORT_TOPK_MAX = 40960
+
+
+def score_rpw(R, q_fp8=False):
+    """Query rows per wave of the scorer variant a row group of R rows takes (csrc/score.hip)."""
+    if q_fp8:
+        return 4 if R > 16 else 2 if R > 4 else 1
+    return 2 if R > 4 else 1
 METRIC = "DSA decode: context tokens scanned/s + query rows/s; % of HBM roofline"
 
 
@@ -52,52 +64,48 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash(names):
+def kernel_source_hash(name):
+    """Hash of a kernel's source file and every header beside it (what it may include)."""
+    csrc = os.path.join(ROOT, "sparse_attention_index_amd", "csrc")
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "sparse_attention_index_amd", "csrc", n), "rb") as f:
+    for n in [name] + sorted(f for f in os.listdir(csrc) if f.endswith(".h")):
+        with open(os.path.join(csrc, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def counters_for(kernel_file, workload):
-    """HBM bytes per launch of a kernel, from the committed rocprofv3 counter summary.
-
-    profiles/hbm_counters.txt holds one line per (kernel source, workload):
-    `<file> <workload> <kernel> <source hash> <fetch bytes> <write bytes>` (already scaled by
-    the copy-kernel calibration). The entry counts only while the kernel source is unchanged.
-    """
+def _counter_lines(workload):
     path = os.path.join(ROOT, "profiles", "hbm_counters.txt")
     if not os.path.exists(path):
-        return None
-    want = kernel_source_hash([kernel_file, "common.h"])
+        return []
     with open(path) as f:
-        for line in f:
-            parts = line.split()
-            if len(parts) == 6 and not line.startswith("#") and parts[0] == kernel_file and parts[1] == workload:
-                if parts[3] != want:
-                    return None
-                return float(parts[4]) + float(parts[5])
+        return [p for p in (line.split() for line in f if not line.startswith("#")) if len(p) == 6 and p[1] == workload]
+
+
+def counters_for(kernel, workload):
+    """HBM bytes per launch of a kernel, from the committed rocprofv3 counter summary.
+
+    profiles/hbm_counters.txt holds one line per (kernel, workload):
+    `<file> <workload> <kernel> <source hash> <fetch bytes> <write bytes>` (already scaled by
+    the copy-kernel calibration). The entry counts only while the kernel's sources are unchanged.
+    """
+    for p in _counter_lines(workload):
+        if p[2] == kernel:
+            return float(p[4]) + float(p[5]) if p[3] == kernel_source_hash(p[0]) else None
     return None
 
 
-def measured_step_bytes(workload):
-    """HBM bytes of one whole step as rocprofv3 counted them: the sum over every
-    kernel that profiles/hbm_counters.txt lists for the workload, or None if
-    there are none or any kernel's source has changed since."""
-    path = os.path.join(ROOT, "profiles", "hbm_counters.txt")
-    if not os.path.exists(path):
-        return None
-    total, seen = 0.0, False
-    with open(path) as f:
-        for line in f:
-            parts = line.split()
-            if len(parts) == 6 and not line.startswith("#") and parts[1] == workload:
-                if parts[3] != kernel_source_hash([parts[0], "common.h"]):
-                    return None
-                total += float(parts[4]) + float(parts[5])
-                seen = True
-    return total if seen else None
+def measured_step_bytes(workload, kernels):
+    """HBM bytes of one whole step as rocprofv3 counted them: the sum over the
+    step's kernels, or None if one is missing or its sources have changed since."""
+    got = {p[2]: p for p in _counter_lines(workload)}
+    total = 0.0
+    for kname in kernels:
+        p = got.get(kname)
+        if p is None or p[3] != kernel_source_hash(p[0]):
+            return None
+        total += float(p[4]) + float(p[5])
+    return total
 
 
 def _blas_threads():
@@ -197,14 +205,16 @@ def stage_times(torch, stages, n):
     return {s: 1e3 * sum(a.elapsed_time(b) for a, b in v) / n for s, v in evs.items()}
 
 
-def step_hbm_fields(traffic, lens, R, k, kfmt, step_bytes, sec, workload):
-    """The step's algorithmic bytes over its time; the same without the fp32
-    score round trip (written by the scorer, read by the selection); and the
-    rocprofv3-counted bytes of the step's kernels over the same time."""
-    vis = traffic.visible(lens, R)
-    no_rt = step_bytes - 2 * traffic.SCORE_BYTES * sum(vis)
-    meas = measured_step_bytes(workload)
+def step_hbm_fields(traffic, lens, R, k, kfmt, sec, workload, kernels, filtered):
+    """The step's algorithmic bytes over its time (keys once, selected latents,
+    and on the stored-score path the fp32 score round trip); the same without
+    that round trip; and the rocprofv3-counted bytes of the step's kernels
+    over the same time."""
+    step_bytes = traffic.decode_step_bytes(lens, R, k, kfmt, round_trip=not filtered)
+    no_rt = traffic.decode_step_bytes(lens, R, k, kfmt, round_trip=False)
+    meas = measured_step_bytes(workload, kernels)
     return {
+        "path": "filtered" if filtered else "stored scores",
         "bytes": step_bytes,
         "achieved_GBs": step_bytes / sec / 1e9,
         "frac": step_bytes / sec / 1e9 / HBM_PEAK_GBS,
@@ -222,6 +232,7 @@ def run_decode(args, torch, dsa, traffic, cfg):
     rows = B * R
     kfmt = cfg.get("key_format", "fp8")
     step_bytes = traffic.decode_step_bytes(lens, R, k, kfmt)
+    filtered = max(lens) > FILTER_MIN_CTX
     set_bytes = sum(lens) * (traffic.key_bytes(kfmt) + traffic.LAT_ROW_BYTES)
     nsets = args.sets or max(2, math.ceil(3 * MALL_BYTES / min(step_bytes, set_bytes)))
     nsets = min(nsets, max(2, int(40e9 // set_bytes)))
@@ -295,11 +306,45 @@ def run_decode(args, torch, dsa, traffic, cfg):
         j = i % nsets
         dsa.dsa_sparse_mla_decode(batches[j], caches[j], cases[j].q_mla, idx, cases[j].sm_scale, out, lse, mla_ws)
 
-    stage_us = stage_times(torch, [("score", score), ("topk", topk), ("attend", attend)], n_stage)
+    stored = stage_times(torch, [("score", score), ("topk", topk), ("attend", attend)], n_stage)
+    if filtered:
+        # the filtered path's stages, one workspace per input set (each keeps
+        # its own thresholds and candidates from one stage to the next)
+        wss = [ws] + [dsa.workspace(ws.numel()) for _ in range(nsets - 1)]
 
-    # ---- dominant kernel: the indexer scorer (its share of the step grows with context)
-    score_us = kernel_time(torch, score, nsets)
-    dom_bytes = traffic.scorer_bytes(lens, R, kfmt)
+        def f_thr(i):
+            j = i % nsets
+            dsa.dsa_filter_threshold(batches[j], caches[j], cases[j].q_idx, cases[j].w, k, wss[j])
+
+        def f_score(i):
+            j = i % nsets
+            dsa.dsa_filter_score(batches[j], caches[j], cases[j].q_idx, cases[j].w, k, wss[j])
+
+        def f_select(i):
+            j = i % nsets
+            dsa.dsa_filter_select(batches[j], caches[j], cases[j].q_idx, cases[j].w, k, idx, wss[j])
+
+        stage_us = stage_times(torch, [("threshold", f_thr), ("score", f_score), ("select", f_select),
+                                       ("attend", attend)], n_stage)
+        stage_us["stored_path"] = {"score": stored["score"], "topk": stored["topk"]}
+        # ---- dominant kernel: the filtered scorer (every set's thresholds in place)
+        for j in range(nsets):
+            f_thr(j)
+        score_us = kernel_time(torch, f_score, nsets)
+        dom_bytes = traffic.filter_scorer_bytes(lens, R, kfmt)
+        dom_kernel = f"score_kernel<{score_rpw(R)},false,{str(kfmt == 'mxfp4').lower()},true>"
+        step_kernels = ["sample_threshold_kernel<%s>" % str(kfmt == "mxfp4").lower(), dom_kernel,
+                        "candidate_select_kernel<%s>" % str(kfmt == "mxfp4").lower()]
+    else:
+        stage_us = stored
+        # ---- dominant kernel: the indexer scorer (its share of the step grows with context)
+        score_us = kernel_time(torch, score, nsets)
+        dom_bytes = traffic.scorer_bytes(lens, R, kfmt)
+        dom_kernel = f"score_kernel<{score_rpw(R)},false,{str(kfmt == 'mxfp4').lower()},false>"
+        step_kernels = [dom_kernel, "topk_short_kernel<true>" if max_ctx <= SHORT_TOPK_MAX else "topk_slice_kernel<true>"]
+        if max_ctx > SHORT_TOPK_MAX:
+            step_kernels.append("topk_final_kernel<true>")
+    step_kernels += ["sparse_mla_kernel"] + (["mla_combine_kernel"] if mla_ws_n else [])
     achieved = dom_bytes / (score_us * 1e-6) / 1e9
 
     tokens = sum(lens)
@@ -330,17 +375,17 @@ def run_decode(args, torch, dsa, traffic, cfg):
             "launch": "eager" if graph is None else "hip graph",
         },
         "rows_per_s": rows / sec,
-        "step_hbm": step_hbm_fields(traffic, lens, R, k, kfmt, step_bytes, sec, args.workload),
+        "step_hbm": step_hbm_fields(traffic, lens, R, k, kfmt, sec, args.workload, step_kernels, filtered),
         "stages_us": stage_us,
         "wall_s": wall,
         "roofline": {
             "bound": "hbm",
-            "kernel": "score_kernel",
+            "kernel": dom_kernel,
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": counters_for("score.hip", args.workload),
+            "traffic": counters_for(dom_kernel, args.workload),
             "algorithmic_bytes": dom_bytes,
             "avg_launch_us": score_us,
         },
@@ -416,12 +461,12 @@ def run_prefill(args, torch, dsa, traffic, cfg):
         "wall_s": wall,
         "roofline": {
             "bound": "mfma",
-            "kernel": "score_kernel",
+            "kernel": f"score_kernel<{score_rpw(R, True)},true,false,false>",
             "achieved": tflops,
             "peak": FP8_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": tflops / FP8_PEAK_TFLOPS,
-            "traffic": counters_for("score.hip", args.workload),
+            "traffic": counters_for(f"score_kernel<{score_rpw(R, True)},true,false,false>", args.workload),
             "algorithmic_flops": flops,
             "avg_launch_us": score_us,
         },

@@ -249,8 +249,12 @@ int32_t dsa_sparse_mla_decode_noalloc(const dsa_batch* batch, const dsa_cache* c
  *   ws       workspace of dsa_workspace_size(DSA_WS_DECODE, rows, max_ctx, k, num_heads)
  *            (holds the fp32 scores, the selection and the attention partials).
  * Results are the same as dsa_index_score -> dsa_topk -> dsa_sparse_mla_decode
- * (the same selected set): the scorer stores every score, the top-k kernels
- * select, and attention reads the selection's cache rows directly.
+ * (the same selected set). Batches with max_ctx up to 40,960 store every
+ * score and select with the top-k kernels; longer ones run the filtered
+ * path (dsa_filter_threshold -> dsa_filter_score -> dsa_filter_select below):
+ * the scorer keeps only scores at or above a sampled per-row threshold, so
+ * the fp32 score rows never go to HBM and back. Either way attention reads
+ * the selection's cache rows directly.
  */
 int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
                    const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale, void* out,
@@ -281,6 +285,37 @@ int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, c
                                const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale,
                                const float* threshold, void* out, float* lse, int32_t* idx_out, void* ws,
                                size_t ws_bytes, void* stream);
+
+/*
+ * The filtered path's three stages, one call each, on one stream and one
+ * workspace (dsa_decode's: dsa_workspace_size(DSA_WS_DECODE, rows, max_ctx,
+ * k, 16)), which carries each stage's results to the next; call them in
+ * order with the same batch, cache, queries and k. Together they select
+ * exactly what dsa_topk selects over dsa_index_score's scores ("vLLM Day-0
+ * Support for Kimi K3.1 Pro", section "Fused low-latency decode for DSA
+ * layers": a scorer that keeps candidates for an exact top-k select).
+ *   dsa_filter_threshold  each row's visible length and candidate threshold:
+ *       the caller's (threshold, fp32 [rows] on the device, any value as in
+ *       dsa_decode_thresholded) or, with threshold NULL, sampled: 2,048 of
+ *       the row's scores (32 whole pages spread over its context) and a
+ *       value a little below the sampled rank that leaves about 1.25k scores
+ *       of the row above it; rows of at most 8,192 tokens keep every score.
+ *   dsa_filter_score      every score at or above its row's threshold, as
+ *       (score, position), into the workspace; nothing else is stored.
+ *   dsa_filter_select     idx int32 [rows][k]: the k largest candidates of
+ *       each row (the selection of dsa_topk, padding -1 included); a row its
+ *       candidates cannot decide is scored again in full and selected over
+ *       all of it.
+ * q_idx and w are dsa_index_score's bf16 query and head weights. Returns
+ * DSA_ERR_UNSUPPORTED if a request would need more than 1,024 scoring
+ * workgroups (contexts beyond about 128M tokens).
+ */
+int32_t dsa_filter_threshold(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                             int32_t k, const float* threshold, void* ws, size_t ws_bytes, void* stream);
+int32_t dsa_filter_score(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                         int32_t k, void* ws, size_t ws_bytes, void* stream);
+int32_t dsa_filter_select(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                          int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Decode context parallelism, simulated on one device. Under DCP, token p of

@@ -322,3 +322,35 @@ def dsa_decode(batch, cache, q_idx, w, q_mla, k, softmax_scale, out, lse=None, i
     else:
         _need(threshold, "threshold", _F32, rows)
         _check(lib.dsa_decode_thresholded(*head, _ptr(threshold), *tail), "dsa_decode_thresholded")
+
+
+def _filter_head(batch, cache, q_idx, w, k, ws):
+    rows = batch.rows
+    _need(q_idx, "q_idx", _BF16, rows * 32 * 128)
+    _need(w, "w", _BF16, rows * 32)
+    _need(ws, "ws", (torch.uint8,))
+    return (ctypes.byref(batch.c), ctypes.byref(cache.c), _ptr(q_idx), _ptr(w), int(k))
+
+
+def dsa_filter_threshold(batch, cache, q_idx, w, k, ws, threshold=None, stream=None):
+    """Filtered path, stage 1: each row's candidate threshold (sampled, or
+    `threshold`, fp32 [rows] on the device) into `ws` (dsa_decode's workspace)."""
+    head = _filter_head(batch, cache, q_idx, w, k, ws)
+    if threshold is not None:
+        _need(threshold, "threshold", _F32, batch.rows)
+    _check(load().dsa_filter_threshold(*head, _ptr(threshold), _ptr(ws), int(ws.numel()), _stream(stream)),
+           "dsa_filter_threshold")
+
+
+def dsa_filter_score(batch, cache, q_idx, w, k, ws, stream=None):
+    """Filtered path, stage 2: the scores at or above each row's threshold, kept in `ws`."""
+    head = _filter_head(batch, cache, q_idx, w, k, ws)
+    _check(load().dsa_filter_score(*head, _ptr(ws), int(ws.numel()), _stream(stream)), "dsa_filter_score")
+
+
+def dsa_filter_select(batch, cache, q_idx, w, k, idx, ws, stream=None):
+    """Filtered path, stage 3: the exact top-k of every row into idx (int32 [rows, k])."""
+    head = _filter_head(batch, cache, q_idx, w, k, ws)
+    _need(idx, "idx", _I32, batch.rows * int(k))
+    _check(load().dsa_filter_select(*head, _ptr(idx), _ptr(ws), int(ws.numel()), _stream(stream)),
+           "dsa_filter_select")

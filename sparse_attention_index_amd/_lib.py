@@ -31,6 +31,9 @@ EXPORTS = (
     "dsa_sparse_mla_decode_noalloc",
     "dsa_decode",
     "dsa_decode_thresholded",
+    "dsa_filter_threshold",
+    "dsa_filter_score",
+    "dsa_filter_select",
     "dsa_workspace_size",
     "dsa_dcp_topk",
     "dsa_dcp_mla_decode",
@@ -96,6 +99,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsa_sparse_mla_decode_noalloc": (I32, [BP, CP, P, I32, P, I32, F, P, P, P]),
         "dsa_decode": (I32, [BP, CP, P, P, P, I32, I32, F, P, P, P, P, SZ, P]),
         "dsa_decode_thresholded": (I32, [BP, CP, P, P, P, I32, I32, F, P, P, P, P, P, SZ, P]),
+        "dsa_filter_threshold": (I32, [BP, CP, P, P, I32, P, P, SZ, P]),
+        "dsa_filter_score": (I32, [BP, CP, P, P, I32, P, SZ, P]),
+        "dsa_filter_select": (I32, [BP, CP, P, P, I32, P, P, SZ, P]),
         "dsa_workspace_size": (SZ, [I32, I32, I64, I32, I32]),
         "dsa_dcp_topk": (I32, [P, I64, P, I32, I32, I32, I32, P, P, P, SZ, P]),
         "dsa_dcp_mla_decode": (I32, [BP, CP, P, I32, P, I32, I32, F, P, P, P, SZ, P]),

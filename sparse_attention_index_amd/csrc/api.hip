@@ -286,34 +286,15 @@ int32_t dsa_sparse_mla_prefill(const dsa_batch* batch, const dsa_cache* cache, c
 }
 
 // dsa_decode takes the filtered path (scores filtered into candidates
-// inside the scorer) for batches with max_ctx above this; 0 keeps every
-// batch on the stored-score path. The stored path is the faster one on
-// MI355X at every measured length, because the sampling pass costs more
-// than the score round trip it saves; dsa_decode_thresholded always filters.
+// inside the scorer) for batches with max_ctx above this; shorter batches
+// take the stored-score path, whose one-workgroup top-k of short rows needs
+// no sampling pass.
 static constexpr int kFilterMinCtx = 40960;
 
-// The decode step. thr_in (device, [rows]) set: the filtered path with the
-// caller's thresholds, whatever max_ctx is.
-static int32_t decode_impl(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                           const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale,
-                           const float* thr_in, void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
-                           void* stream) {
-  g_err[0] = 0;
-  int32_t r = check_batch(batch);
-  if (r) return r;
-  if ((r = check_cache(cache, true, true))) return r;
-  if (!q_idx || !w) return fail(DSA_ERR_INVALID_ARG, "q_idx or w is null");
-  if (!aligned(q_idx, 16)) return fail(DSA_ERR_INVALID_ARG, "q_idx must be 16-byte aligned");
-  if ((r = check_mla(num_heads, k, q_mla, idx_out, out, false))) return r;
-  const int32_t rows = batch->num_requests * batch->rows_per_request;
-  const size_t need = dsa_workspace_size(DSA_WS_DECODE, rows, batch->max_ctx, k, num_heads);
-  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "decode needs %zu workspace bytes", need);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  DecodeWs p;
-  decode_ws_parts(rows, batch->max_ctx, k, &p, ws);
-  const int64_t ld = decode_ld(batch->max_ctx);
-  int32_t* idx = idx_out ? idx_out : p.idx;
-  const int B = batch->num_requests;
+// The scorer's arguments for one batch (scores go to the workspace's score
+// rows: the stored path's and the filtered path's fallback).
+static ScoreArgs index_args(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                            const DecodeWs& p) {
   ScoreArgs a;
   a.q = q_idx;
   a.q_scale = nullptr;
@@ -324,36 +305,100 @@ static int32_t decode_impl(const dsa_batch* batch, const dsa_cache* cache, const
   a.max_blocks = batch->max_blocks;
   a.R = batch->rows_per_request;
   a.scores = p.scores;
-  a.ld = ld;
+  a.ld = decode_ld(batch->max_ctx);
+  return a;
+}
+
+// The filtered path's view of the same arguments, and its scorer grid.
+struct Filter {
+  ScoreArgs f;
+  int grid;  // scoring workgroups per row group (split over the requests)
+  bool fits; // no request has more than kMaxFilterWg of them
+};
+
+static Filter filter_of(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                        const DecodeWs& p) {
+  Filter F;
+  const int32_t rows = batch->num_requests * batch->rows_per_request;
+  F.f = index_args(batch, cache, q_idx, w, p);
+  F.f.thr = p.thr;
+  F.f.cand = p.fcand;
+  F.f.cand_count = p.fcount;
+  F.f.cap = filter_cap(rows);
+  const int B = batch->num_requests;
+  F.grid = filter_grid(B, batch->rows_per_request, batch->max_ctx, cache->key_format == DSA_KEY_MXFP4);
+  F.fits = F.grid - B + 1 <= kMaxFilterWg;
+  return F;
+}
+
+// The three stages of the filtered path.
+// 1. each row's visible length and threshold (sampled, or the caller's)
+static int32_t filter_threshold(const Filter& F, const DecodeWs& p, int32_t rows, int32_t k, const float* thr_in,
+                                hipStream_t st) {
+  return hip_status(launch_sample_threshold(F.f, rows, k, thr_in, p.thr, p.row_len, st), "filter threshold");
+}
+// 2. score, keeping only the candidates at or above the threshold
+static int32_t filter_score(const Filter& F, const dsa_batch* batch, hipStream_t st) {
+  return hip_status(launch_index_score(F.f, batch->num_requests, batch->max_ctx, false, st), "filter score");
+}
+// 3. exact selection from the candidates; a row they cannot decide is
+//    scored again in full (into the score rows) and selected over all of it
+static int32_t filter_select(const Filter& F, const dsa_batch* batch, const DecodeWs& p, int32_t rows, int32_t k,
+                             int32_t* idx, const SlotOut& so, hipStream_t st) {
+  return hip_status(launch_candidate_select(F.f, batch->num_requests, F.grid, p.thr, p.row_len, p.fcompact, rows, k,
+                                            idx, so, st),
+                    "filter select");
+}
+
+// Checks shared by the decode entry points: batch, cache, indexer query and
+// the workspace; the workspace carved into p.
+static int32_t decode_checks(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                             int32_t k, bool lat, void* ws, size_t ws_bytes, DecodeWs* p) {
+  int32_t r = check_batch(batch);
+  if (r) return r;
+  if ((r = check_cache(cache, true, lat))) return r;
+  if (!q_idx || !w) return fail(DSA_ERR_INVALID_ARG, "q_idx or w is null");
+  if (!aligned(q_idx, 16)) return fail(DSA_ERR_INVALID_ARG, "q_idx must be 16-byte aligned");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in [1, 2048]");
+  const int32_t rows = batch->num_requests * batch->rows_per_request;
+  const size_t need = dsa_workspace_size(DSA_WS_DECODE, rows, batch->max_ctx, k, DSA_MLA_HEADS);
+  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "decode needs %zu workspace bytes", need);
+  decode_ws_parts(rows, batch->max_ctx, k, p, ws);
+  return DSA_OK;
+}
+
+// The decode step. thr_in (device, [rows]) set: the filtered path with the
+// caller's thresholds, whatever max_ctx is.
+static int32_t decode_impl(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                           const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale,
+                           const float* thr_in, void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  g_err[0] = 0;
+  DecodeWs p;
+  int32_t r = check_mla(num_heads, k, q_mla, idx_out, out, false);
+  if (r) return r;
+  if ((r = decode_checks(batch, cache, q_idx, w, k, true, ws, ws_bytes, &p))) return r;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t rows = batch->num_requests * batch->rows_per_request;
+  int32_t* idx = idx_out ? idx_out : p.idx;
   SlotOut so;
   so.slots = p.slots;
   so.block_table = batch->block_table;
   so.max_blocks = batch->max_blocks;
-  const int grid = filter_grid(B, batch->rows_per_request, batch->max_ctx, cache->key_format == DSA_KEY_MXFP4);
-  const bool fits = grid - B + 1 <= kMaxFilterWg;  // no request past kMaxFilterWg scoring workgroups
-  if (thr_in && !fits)
+  const Filter F = filter_of(batch, cache, q_idx, w, p);
+  if (thr_in && !F.fits)
     return fail(DSA_ERR_UNSUPPORTED, "a request would need more than %d scoring workgroups", kMaxFilterWg);
-  const bool filtered = thr_in || (kFilterMinCtx > 0 && batch->max_ctx > kFilterMinCtx && fits);
-  if (filtered) {
-    ScoreArgs f = a;
-    f.thr = p.thr;
-    f.cand = p.fcand;
-    f.cand_count = p.fcount;
-    f.cap = filter_cap(rows);
-    // 1. each row's visible length and threshold (sampled, or the caller's)
-    if ((r = hip_status(launch_sample_threshold(f, rows, k, thr_in, p.thr, p.row_len, st), "decode threshold")))
-      return r;
-    // 2. score, keeping only the candidates at or above the threshold
-    if ((r = hip_status(launch_index_score(f, B, batch->max_ctx, false, st), "decode filtered score"))) return r;
-    // 3. exact selection from the candidates; a row they cannot decide is
-    //    scored again in full (into the score rows) and selected over all of it
-    if ((r = hip_status(launch_candidate_select(f, B, grid, p.thr, p.row_len, p.fcompact, rows, k, idx, so, st),
-                        "decode candidate select")))
-      return r;
+  if (thr_in || (batch->max_ctx > kFilterMinCtx && F.fits)) {
+    if ((r = filter_threshold(F, p, rows, k, thr_in, st))) return r;
+    if ((r = filter_score(F, batch, st))) return r;
+    if ((r = filter_select(F, batch, p, rows, k, idx, so, st))) return r;
   } else {
+    const ScoreArgs a = index_args(batch, cache, q_idx, w, p);
+    const int64_t ld = a.ld;
     const TopkWs tw = topk_ws_carve(p.topk, rows, ld);
     // 1. score
-    if ((r = hip_status(launch_index_score(a, B, batch->max_ctx, false, st), "decode score"))) return r;
+    if ((r = hip_status(launch_index_score(a, batch->num_requests, batch->max_ctx, false, st), "decode score")))
+      return r;
     // 2. select (the visible lengths are derived on the way), also writing the
     //    cache rows of the selection so that attention reads no block table
     if ((r = hip_status(launch_topk(p.scores, ld, p.row_len, rows, ld, k, idx, tw, st, batch->ctx_len,
@@ -361,8 +406,31 @@ static int32_t decode_impl(const dsa_batch* batch, const dsa_cache* cache, const
                         "decode topk")))
       return r;
   }
-  // attend
+  // 3. attend
   return run_mla(batch, cache, q_mla, idx, k, softmax_scale, out, lse, p.mla, true, st, p.slots);
+}
+
+// The filtered path's stages as entry points of their own (one workspace,
+// the decode step's, carries their state from one call to the next).
+static int32_t filter_stage(int stage, const dsa_batch* batch, const dsa_cache* cache, const void* q_idx,
+                            const void* w, int32_t k, const float* thr_in, int32_t* idx, void* ws, size_t ws_bytes,
+                            void* stream) {
+  g_err[0] = 0;
+  DecodeWs p;
+  int32_t r = decode_checks(batch, cache, q_idx, w, k, false, ws, ws_bytes, &p);
+  if (r) return r;
+  if (stage == 3 && !idx) return fail(DSA_ERR_INVALID_ARG, "idx is null");
+  const Filter F = filter_of(batch, cache, q_idx, w, p);
+  if (!F.fits) return fail(DSA_ERR_UNSUPPORTED, "a request would need more than %d scoring workgroups", kMaxFilterWg);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t rows = batch->num_requests * batch->rows_per_request;
+  if (stage == 1) return filter_threshold(F, p, rows, k, thr_in, st);
+  if (stage == 2) return filter_score(F, batch, st);
+  SlotOut so;  // no cache rows: the caller's attention resolves idx itself
+  so.slots = nullptr;
+  so.block_table = batch->block_table;
+  so.max_blocks = batch->max_blocks;
+  return filter_select(F, batch, p, rows, k, idx, so, st);
 }
 
 int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
@@ -382,6 +450,21 @@ int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, c
   }
   return decode_impl(batch, cache, q_idx, w, q_mla, num_heads, k, softmax_scale, threshold, out, lse, idx_out, ws,
                      ws_bytes, stream);
+}
+
+int32_t dsa_filter_threshold(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                             int32_t k, const float* threshold, void* ws, size_t ws_bytes, void* stream) {
+  return filter_stage(1, batch, cache, q_idx, w, k, threshold, nullptr, ws, ws_bytes, stream);
+}
+
+int32_t dsa_filter_score(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                         int32_t k, void* ws, size_t ws_bytes, void* stream) {
+  return filter_stage(2, batch, cache, q_idx, w, k, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int32_t dsa_filter_select(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
+                          int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return filter_stage(3, batch, cache, q_idx, w, k, nullptr, idx, ws, ws_bytes, stream);
 }
 
 size_t dsa_workspace_size(int32_t kind, int32_t rows, int64_t max_ctx, int32_t k, int32_t num_heads) {

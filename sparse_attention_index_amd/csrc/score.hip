@@ -69,7 +69,14 @@ static constexpr int kKeyBytes = kBlock * kIdxDim;  // one page of keys, 8 KB
 static constexpr int kF4KeyBytes = kBlock * kIdxDim / 2;  // one page of MXFP4 keys, 4 KB
 static constexpr int kF4Copies = kF4KeyBytes / 1024 + 1;  // 4 key copies + 1 scale copy
 static constexpr int kRing = 4;                     // LDS page slots per workgroup
-static constexpr int kMaxWgPages = 2048;            // pages one workgroup walks at most
+// Pages one workgroup walks at most (its page ids are staged in LDS): 4,096
+// for the 16-row prefill variant, whose registers already hold it to two
+// workgroups per CU, so that a 256K-token chunk still takes one round of
+// them; 2,048 for the others, where more would cost a resident workgroup.
+template <int RPW>
+constexpr int max_wg_pages() {
+  return RPW == 4 ? 4096 : 2048;
+}
 static constexpr int kThreads = 256;                // 4 waves
 static constexpr int kCopies = kKeyBytes / 1024 + 1;  // copy instructions per page (keys + scales)
 static constexpr int kCopiers = 3;                  // waves that issue copies
@@ -110,7 +117,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int PAGE = KF4 ? kF4KeyBytes : kKeyBytes;
   __shared__ __attribute__((aligned(16))) uint8_t key_s[kRing][PAGE];
   __shared__ __attribute__((aligned(16))) float ks_s[kRing][kBlock];  // fp32 scales, or 4 E8M0 per key
-  __shared__ int32_t tbl_s[kMaxWgPages];
+  __shared__ int32_t tbl_s[max_wg_pages<RPW>()];
   __shared__ __attribute__((aligned(16))) float w_s[ROWS][kIdxHeads];
   __shared__ float sc_s[LAG + 1][ROWS][kBlock];  // scores of the group's rows, by page
 
@@ -446,18 +453,23 @@ static int cu_count() {
 }
 
 // Workgroups per row group: one round of resident workgroups over the whole
-// grid, at least one per request, none past kMaxWgPages pages (each gets at
-// most about B * max_blk / (G - B) pages) and about two pages each at least.
+// grid, at least one per request, none past max_wg_pages pages and about two
+// pages each at least. A single request gets all G (max_blk / G pages each);
+// with several, request b gets 1 + floor(spare p_b / P) or more of them,
+// spare = G - B, P = the pages of all requests <= B max_blk, so each walks
+// fewer than P / spare + 1 pages.
 template <int RPW, bool QFP8, bool KF4, bool FILT>
 static long long grid_x(int B, int R, int max_ctx) {
+  constexpr long long kMax = max_wg_pages<RPW>();
   const int groups = (R + 4 * RPW - 1) / (4 * RPW);
   const long long max_blk = (max_ctx + kBlock - 1) / kBlock;
   const long long slots = (long long)resident_per_cu<RPW, QFP8, KF4, FILT>() * cu_count();
   long long G = slots / groups;
   const long long most = (long long)B * ((max_blk + 1) / 2);
   if (G > most) G = most;
-  const long long least = (long long)B + ((long long)B * max_blk + kMaxWgPages - 1) / kMaxWgPages;
+  const long long least = B == 1 ? (max_blk + kMax - 1) / kMax : (long long)B + ((long long)B * max_blk + kMax - 1) / kMax;
   if (G < least) G = least;
+  if (G < B) G = B;
   return G;
 }
 

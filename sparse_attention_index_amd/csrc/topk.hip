@@ -384,22 +384,29 @@ __global__ __launch_bounds__(kTF) void topk_final_kernel(const float* __restrict
   const uint32_t count = L.off[slices];
   const float* s = scores + (size_t)row * ld;
   if (count >= (uint32_t)k && count <= (uint32_t)kFinalLds) {
-    // regions that hold their slice's survivors: wave w copies slices w,
-    // w + 16, ..., four loads in flight per lane
+    // regions that hold their slice's survivors: groups of wps waves (one
+    // wave when there are 16 slices or more, all 16 for a single slice) copy
+    // slices g, g + groups, ..., four loads in flight per lane
     const uint2* regions = w.cand + (size_t)row * w.cap;
-    for (int r = wave; r < slices; r += kTF / 64) {
+    constexpr int kWaves = kTF / 64;
+    const int wps = slices >= kWaves ? 1 : kWaves / slices;  // waves per slice
+    const int groups = kWaves / wps;
+    const int gw = wave / wps;                       // this wave's group
+    const uint32_t gl = 64 * (wave % wps) + lane;    // its lane within the group
+    const uint32_t gsz = 64 * wps;
+    for (int r = gw; gw < groups && r < slices; r += groups) {
       const uint32_t o = L.off[r], cr = L.cnt[r];
-      if (cr > sub) continue;  // read again below (wave-uniform)
-      for (uint32_t j0 = 0; j0 < cr; j0 += 256) {
+      if (cr > sub) continue;  // read again below (uniform over the group)
+      for (uint32_t j0 = 0; j0 < cr; j0 += 4 * gsz) {
         uint2 v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint32_t j = j0 + 64 * u + lane;
+          const uint32_t j = j0 + gsz * u + gl;
           v[u] = j < cr ? regions[(size_t)r * sub + j] : make_uint2(0u, 0u);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint32_t j = j0 + 64 * u + lane;
+          const uint32_t j = j0 + gsz * u + gl;
           if (j < cr) L.elems[o + j] = v[u];
         }
       }

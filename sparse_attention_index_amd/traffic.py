@@ -36,6 +36,13 @@ def scorer_bytes(ctx_lens, R, key_format="fp8"):
     return sum(ctx_lens) * key_bytes(key_format) + SCORE_BYTES * sum(vis) + len(vis) * Q_IDX_BYTES
 
 
+def filter_scorer_bytes(ctx_lens, R, key_format="fp8"):
+    """The filtered scorer: keys once per request, the rows' queries and head
+    weights; the (score, position) candidates it keeps (a few thousand per
+    row, under 0.1% of the keys' bytes at 1M tokens) are not counted."""
+    return sum(ctx_lens) * key_bytes(key_format) + len(visible(ctx_lens, R)) * Q_IDX_BYTES
+
+
 def topk_bytes(ctx_lens, R, k):
     vis = visible(ctx_lens, R)
     return SCORE_BYTES * sum(vis) + 4 * k * len(vis)
@@ -46,10 +53,13 @@ def mla_bytes(ctx_lens, R, k):
     return sum(min(k, v) * (LAT_ROW_BYTES + 4) for v in vis) + len(vis) * (Q_MLA_BYTES + OUT_BYTES)
 
 
-def decode_step_bytes(ctx_lens, R, k, key_format="fp8"):
-    """Keys once per request + per row: selected latents and the score round trip."""
+def decode_step_bytes(ctx_lens, R, k, key_format="fp8", round_trip=True):
+    """Keys once per request + per row: selected latents and, with
+    round_trip, the fp32 score row written by the scorer and read by the
+    selection (the stored-score path; the filtered path keeps no score row)."""
     vis = visible(ctx_lens, R)
-    return sum(ctx_lens) * key_bytes(key_format) + sum(min(k, v) * LAT_ROW_BYTES + 2 * SCORE_BYTES * v for v in vis)
+    rt = 2 * SCORE_BYTES if round_trip else 0
+    return sum(ctx_lens) * key_bytes(key_format) + sum(min(k, v) * LAT_ROW_BYTES + rt * v for v in vis)
 
 
 def scorer_flops(ctx_lens, R, heads=32, dim=128):

@@ -22,19 +22,33 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert "one GPU" in r.stdout + r.stderr
 
 
+def _step_kernels(cfg, filtered):
+    R = cfg["R"]
+    fmt = str(cfg.get("key_format", "fp8") == "mxfp4").lower()
+    if filtered:
+        ks = [f"sample_threshold_kernel<{fmt}>", f"score_kernel<{bench.score_rpw(R)},false,{fmt},true>",
+              f"candidate_select_kernel<{fmt}>"]
+    else:
+        ks = [f"score_kernel<{bench.score_rpw(R)},false,{fmt},false>", "topk_short_kernel<true>"]
+    return ks + ["sparse_mla_kernel", "mla_combine_kernel"]
+
+
 @pytest.mark.parametrize("workload", ["decode_16x4_32k", "decode_4x4_1m_planted", "decode_4x4_1m_mxfp4"])
 def test_step_hbm_fields(workload):
     cfg = case_config(workload)
     kf = cfg.get("key_format", "fp8")
     lens, R, k = cfg["lengths"], cfg["R"], 2048
-    step = traffic.decode_step_bytes(lens, R, k, kf)
+    filtered = max(lens) > bench.FILTER_MIN_CTX
+    step = traffic.decode_step_bytes(lens, R, k, kf, round_trip=not filtered)
+    no_rt = traffic.decode_step_bytes(lens, R, k, kf, round_trip=False)
     sec = 1e-4
-    f = bench.step_hbm_fields(traffic, lens, R, k, kf, step, sec, workload)
+    f = bench.step_hbm_fields(traffic, lens, R, k, kf, sec, workload, _step_kernels(cfg, filtered), filtered)
     assert f["bytes"] == step
     assert f["frac"] == pytest.approx(step / sec / 1e9 / bench.HBM_PEAK_GBS)
-    # the score round trip is 8 bytes per visible (row, token)
+    # the score round trip is 8 bytes per visible (row, token), counted only on the stored path
     rt = 8 * sum(traffic.visible(lens, R))
-    assert f["frac_without_score_round_trip"] == pytest.approx((step - rt) / sec / 1e9 / bench.HBM_PEAK_GBS)
+    assert step - no_rt == (0 if filtered else rt)
+    assert f["frac_without_score_round_trip"] == pytest.approx(no_rt / sec / 1e9 / bench.HBM_PEAK_GBS)
     # with counters for the current sources, the counted bytes cover the algorithmic ones (within the
     # counters' granularity); once a kernel source changes they are None until taken again
     if f["measured_bytes"] is None:
@@ -44,11 +58,27 @@ def test_step_hbm_fields(workload):
         assert f["measured_frac"] == pytest.approx(f["measured_bytes"] / sec / 1e9 / bench.HBM_PEAK_GBS)
 
 
-def test_counters_need_the_current_source(monkeypatch):
-    assert bench.counters_for("score.hip", "no_such_workload") is None
-    assert bench.measured_step_bytes("no_such_workload") is None
-    # a changed kernel source invalidates its counter lines
-    real = bench.kernel_source_hash
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda names: "0" * 16 if names[0] == "score.hip" else real(names))
-    assert bench.counters_for("score.hip", "decode_16x4_32k") is None
-    assert bench.measured_step_bytes("decode_16x4_32k") is None
+def test_the_filtered_step_is_charged_no_score_round_trip():
+    lens, R, k = [1 << 20] * 4, 4, 2048
+    full = traffic.decode_step_bytes(lens, R, k)
+    filt = traffic.decode_step_bytes(lens, R, k, round_trip=False)
+    assert full - filt == 8 * sum(traffic.visible(lens, R))
+    assert traffic.filter_scorer_bytes(lens, R) == sum(lens) * 132 + 16 * traffic.Q_IDX_BYTES
+
+
+def test_counters_need_the_current_source(monkeypatch, tmp_path):
+    assert bench.counters_for("score_kernel<1,false,false,true>", "no_such_workload") is None
+    assert bench.measured_step_bytes("no_such_workload", ["sparse_mla_kernel"]) is None
+    # a table with one line for the current sources is read back; a changed source invalidates it
+    (tmp_path / "profiles").mkdir()
+    h = bench.kernel_source_hash("mla.hip")
+    (tmp_path / "profiles" / "hbm_counters.txt").write_text(
+        f"# header\nmla.hip wl sparse_mla_kernel {h} 1000 24\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda name: h)  # the sources as they were
+    assert bench.counters_for("sparse_mla_kernel", "wl") == 1024.0
+    assert bench.measured_step_bytes("wl", ["sparse_mla_kernel"]) == 1024.0
+    assert bench.measured_step_bytes("wl", ["sparse_mla_kernel", "mla_combine_kernel"]) is None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda name: "0" * 16)
+    assert bench.counters_for("sparse_mla_kernel", "wl") is None
+    assert bench.measured_step_bytes("wl", ["sparse_mla_kernel"]) is None

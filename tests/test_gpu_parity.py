@@ -383,6 +383,32 @@ def test_thresholded_decode_equals_the_staged_path_whatever_the_threshold(gpu, n
         check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"{name} {label}")
 
 
+@pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "2x4_ragged_perm", "40x4_many_rows"])
+def test_filter_stage_entry_points_select_the_stored_top_k(gpu, name):
+    """dsa_filter_threshold -> dsa_filter_score -> dsa_filter_select, called
+    one by one on a workspace that starts with stale bytes, select exactly
+    dsa_topk's set over dsa_index_score's scores: with sampled thresholds,
+    with each row's k-th score as the caller's threshold, and with +inf (every
+    row through the fallback). 2x4_ragged_perm is short enough that the fused
+    decode would not filter it; the stages filter whatever the length."""
+    case = _case(name)
+    k = case.topk
+    ref = gpu_topk(gpu_scores(case, sentinel=0.0), row_len_of(case), k).cpu().numpy()
+    b, c = dsa.Batch.of(case), dsa.Cache.of(case)
+    ws = dsa.workspace(dsa.dsa_workspace_size(dsa.DSA_WS_DECODE, case.rows, case.max_ctx, k))
+    kth = _kth_scores(case, k)
+    for label, thr in (("sampled", None), ("kth", kth), ("+inf", torch.full_like(kth, float("inf")))):
+        print(f"[filter stages] {name} {label}", flush=True)
+        ws.fill_(0xA5)
+        idx = torch.full((case.rows, k), -7, dtype=torch.int32, device="cuda")
+        dsa.dsa_filter_threshold(b, c, case.q_idx, case.w, k, ws, threshold=thr)
+        dsa.dsa_filter_score(b, c, case.q_idx, case.w, k, ws)
+        dsa.dsa_filter_select(b, c, case.q_idx, case.w, k, idx, ws)
+        got = idx.cpu().numpy()
+        for row in range(case.rows):
+            assert set(got[row].tolist()) == set(ref[row].tolist()), f"{name} {label} row {row}"
+
+
 def test_fused_decode_selection_is_deterministic(gpu):
     case = _case("2x4_ragged_perm")
     a = gpu_decode(case)
