@@ -13,8 +13,9 @@
 //     two tile buffers, so the next tile is in flight while one is computed.
 //     Completion is tracked with explicit vmcnt waits and raw s_barrier (a
 //     full __syncthreads would also wait for the copy in flight). Rows are
-//     stored unpadded with their 16-byte chunks rotated by the row index,
-//     which spreads both read patterns below over distinct LDS banks;
+//     stored unpadded with their 16-byte chunks rotated by row / 4
+//     (chunk_slot), which spreads both read patterns below over distinct
+//     LDS banks;
 //  2. QK: wave w computes the logits of 16 heads x 16 tokens [16w, 16w+16)
 //     with FP8 MFMAs on the raw E4M3 latent (no conversion): the bf16 query
 //     is split into two E4M3 terms (exact down to ~2^-10 of the head's
@@ -67,12 +68,25 @@ DSA_DEV i32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
 }
 
-// LDS byte offset of 16-byte chunk j of tile row r (chunks rotated by r).
-DSA_DEV int lat_off(int r, int j) {
-  int jp = j + (r % kChunks);
-  if (jp >= kChunks) jp -= kChunks;
-  return r * kLat + jp * 16;
+// Where chunk j of tile row r sits within the row: rotated by r / 4, the
+// 32 chunks of the 512 value dims among themselves and the 4 chunks of the
+// 64 RoPE dims among themselves. A row is 144 dwords, 16 banks on from the
+// one before, so 16 consecutive rows (an aligned block) reading the same
+// chunk land on 16 distinct groups of 4 banks: (4 (r mod 4) + r / 4 + j)
+// mod 16 differs for every r of the block. Both tile reads below take such
+// blocks (16 rows per 16-lane group of 16-byte reads, 16 rows per 32 lanes
+// of 8-byte transposed reads).
+DSA_DEV int chunk_slot(int r, int j) {
+  const int q = r >> 2;
+  return j < 32 ? (j + q) & 31 : 32 + ((j + q) & 3);
 }
+// The chunk held by slot s of row r (the inverse).
+DSA_DEV int slot_chunk(int r, int s) {
+  const int q = r >> 2;
+  return s < 32 ? (s - q) & 31 : 32 + ((s - 32 - q) & 3);
+}
+// LDS byte offset of 16-byte chunk j of tile row r.
+DSA_DEV int lat_off(int r, int j) { return r * kLat + chunk_slot(r, j) * 16; }
 
 // Max / sum over the 16 lanes of a DPP row (row_ror 1, 2, 4, 8).
 template <int CTRL>
@@ -154,9 +168,7 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
   for (int i = 0; i < kPer; ++i) {
     const int c = 64 * (kPer * wave + i) + lane;
     cr[i] = c / kChunks;
-    int j = c - cr[i] * kChunks - (cr[i] % kChunks);
-    if (j < 0) j += kChunks;
-    cj[i] = j;
+    cj[i] = slot_chunk(cr[i], c - cr[i] * kChunks);
   }
   // Copy tile t into ring slot t % 2 (skipped rows read row 0 and are zeroed
   // after arrival). Waves 0 and 1 also copy the tile's 128 scales.
@@ -202,14 +214,14 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
   // back in through the MFMA's A-operand block scale. (bf16 carries 8
   // significant bits, each E4M3 term 4; only elements ~2^10 below the head
   // maximum lose low bits, to E4M3's subnormal step.) The workgroup splits
-  // the query once, each thread 18 values, into [head][640] byte planes
+  // the query once, each thread 18 values, into [head][656] byte planes
   // staged in ring slot 1 (dims 576-639 zero), which tile 1's copies only
   // overwrite after the loop's first barrier; lane (g, n) then reads head
   // n, dims 128s + 32g + [0, 32) of step s.
   i32x8 qh[5], ql[5];
   int qscale;  // E8M0 exponent of 2^-e for this lane's head
   {
-    constexpr int kQRow = 640;
+    constexpr int kQRow = 656;  // 640 bytes per head plus 16: the 16 heads' rows start on distinct banks
     uint8_t* qhi = ring[1];
     uint8_t* qlo = ring[1] + kMlaHeads * kQRow;
     int* ex_s = reinterpret_cast<int*>(ring[1] + 2 * kMlaHeads * kQRow);
@@ -280,16 +292,12 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
       int tk = tok;
       asm volatile("" : "+v"(tk));  // offsets recomputed per tile rather than held in registers
       const uint8_t* kr = tile + tk * kLat;
-      const int rot = tk % kChunks;
 #pragma unroll
       for (int s = 0; s < 5; ++s) {
-        int c = 8 * s + 2 * g;
+        int c = 8 * s + 2 * g;  // even: c and c + 1 are both value or both RoPE chunks
         if (c >= kChunks) c -= 4;
-        int c0 = c + rot, c1 = c + 1 + rot;
-        if (c0 >= kChunks) c0 -= kChunks;
-        if (c1 >= kChunks) c1 -= kChunks;
-        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kr + 16 * c0);
-        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kr + 16 * c1);
+        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(kr + 16 * chunk_slot(tk, c));
+        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(kr + 16 * chunk_slot(tk, c + 1));
         const i32x8 bk = {(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
                           (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
         ah = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qh[s], bk, ah, 0, 0, 0, qscale, 0, 127);
