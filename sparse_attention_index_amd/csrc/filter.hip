@@ -36,17 +36,24 @@ struct RowQuery {
   float wv[16];
 };
 
+// The split of a loaded query row (lane n holds head n's values and
+// weight bits, both lane halves).
 template <bool KF4>
-DSA_DEV void row_query(const ScoreArgs& a, size_t row, RowQuery<KF4>& q) {
-  const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
-  QueryRaw<false, KF4> raw;
-  fetch_query<false, KF4>(a, row, n, g, raw);
-  const uint32_t wbits = a.w[row * kIdxHeads + n];
+DSA_DEV void finish_row_query(const QueryRaw<false, KF4>& raw, uint32_t wbits, RowQuery<KF4>& q) {
+  const int g = (threadIdx.x & 63) >> 5;
   const float head_scale = finish_query(raw, q.A);
   // head h's weight times its scale sits in lanes h and h + 32
   const float ws = __uint_as_float(wbits << 16) * head_scale;
 #pragma unroll
   for (int i = 0; i < 16; ++i) q.wv[i] = __shfl(ws, 8 * (i >> 2) + 4 * g + (i & 3));
+}
+
+template <bool KF4>
+DSA_DEV void row_query(const ScoreArgs& a, size_t row, RowQuery<KF4>& q) {
+  const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
+  QueryRaw<false, KF4> raw;
+  fetch_query<false, KF4>(a, row, n, g, raw);
+  finish_row_query<KF4>(raw, a.w[row * kIdxHeads + n], q);
 }
 
 // B operands of the 64 keys of one page (keys 32h + n for lane n of each
@@ -129,6 +136,11 @@ __global__ __launch_bounds__(kSampleThreads) void sample_threshold_kernel(ScoreA
   __shared__ ScanLds<NT> scan;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, n = lane & 31;
   const int row = blockIdx.x, R = a.R, b = row / R;
+  // the query row and head weights go out first: they depend on nothing,
+  // and their latency then overlaps the chain ctx_len -> page ids -> keys
+  QueryRaw<false, KF4> qraw;
+  fetch_query<false, KF4>(a, (size_t)row, n, g, qraw);
+  const uint32_t wbits = a.w[(size_t)row * kIdxHeads + n];
   const int vis = a.ctx_len[b] - R + row % R + 1;
   const int64_t nvis = vis > 0 ? vis : 0;
   if (t == 0) row_len[row] = (int32_t)nvis;
@@ -151,8 +163,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_threshold_kernel(ScoreA
   PageKeys<KF4> pk[PPW];
 #pragma unroll
   for (int i = 0; i < PPW; ++i) load_page<KF4>(a, pid[i], pk[i]);
+  hold_query(qraw);
   RowQuery<KF4> q;
-  row_query<KF4>(a, row, q);
+  finish_row_query<KF4>(qraw, wbits, q);
 #pragma unroll
   for (int i = 0; i < PPW; ++i) {
     float v[2];
