@@ -412,6 +412,36 @@ def test_filter_stage_entry_points_select_the_stored_top_k(gpu, name):
             assert set(got[row].tolist()) == set(ref[row].tolist()), f"{name} {label} row {row}"
 
 
+def test_filter_stages_refuse_requests_past_the_selection_capacity(gpu):
+    """One row at 140M tokens would spread its request over more than 1,024
+    scoring workgroups (each stages at most 2,048 page ids, and the
+    selection has one thread per workgroup): the filtered stages and the
+    thresholded decode refuse it on the host, before any kernel runs (the
+    cache holds one zero page that every table entry points to)."""
+    L = 140 << 20
+    dev = "cuda"
+    b = dsa.Batch(1, torch.tensor([L], dtype=torch.int32, device=dev),
+                  torch.zeros((1, (L + 63) // 64), dtype=torch.int32, device=dev), L)
+    c = dsa.Cache(torch.zeros((1, 64, 128), dtype=torch.uint8, device=dev), torch.ones(64, device=dev),
+                  torch.zeros((1, 64, 576), dtype=torch.uint8, device=dev), torch.ones(64, device=dev))
+    q = torch.zeros((1, 32, 128), dtype=torch.bfloat16, device=dev)
+    w = torch.zeros((1, 32), dtype=torch.bfloat16, device=dev)
+    ws = dsa.workspace(dsa.dsa_workspace_size(dsa.DSA_WS_DECODE, 1, L, 2048))
+    for call in (lambda: dsa.dsa_filter_threshold(b, c, q, w, 2048, ws),
+                 lambda: dsa.dsa_filter_score(b, c, q, w, 2048, ws),
+                 lambda: dsa.dsa_filter_select(b, c, q, w, 2048, torch.empty((1, 2048), dtype=torch.int32,
+                                                                             device=dev), ws)):
+        with pytest.raises(dsa.DsaError) as err:
+            call()
+        assert err.value.status == dsa.DSA_ERR_UNSUPPORTED and "1024 scoring workgroups" in str(err.value)
+    out = torch.empty((1, 16, 512), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(dsa.DsaError) as err:
+        dsa.dsa_decode(b, c, q, w, torch.zeros((1, 16, 576), dtype=torch.bfloat16, device=dev), 2048, 0.04, out,
+                       ws=ws, threshold=torch.zeros(1, device=dev))
+    assert err.value.status == dsa.DSA_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+
+
 def test_fused_decode_selection_is_deterministic(gpu):
     case = _case("2x4_ragged_perm")
     a = gpu_decode(case)
