@@ -14,9 +14,13 @@
  *    hipStream_t passed as void* (NULL = the default stream). All work is
  *    enqueued asynchronously on that stream; nothing synchronises the host.
  *  - The caller owns every buffer, workspace included. The library never
- *    allocates or frees memory and keeps no pointer after a call returns. It
- *    holds no state between calls; calls on different streams with disjoint
- *    outputs and workspaces may run concurrently.
+ *    allocates or frees memory and keeps no pointer after a call returns.
+ *    Between calls it holds only read-only facts about the device (scorer
+ *    occupancy, compute-unit count), the message of the last error (per
+ *    thread), and the device array of dsa_sparse_mla_decode_noalloc;
+ *    calls on different streams with disjoint outputs and workspaces may
+ *    run concurrently (dsa_sparse_mla_decode_noalloc calls on one device
+ *    excepted).
  *  - Errors are returned as dsa_status codes, never thrown. Arguments are
  *    checked on the host before anything is enqueued; on any error nothing is
  *    enqueued. DSA_ERR_HIP reports a failed launch (see dsa_last_error()).

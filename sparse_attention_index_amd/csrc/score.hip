@@ -11,7 +11,10 @@
 // rows ("TokenSpeed Kimi K3.1", section "Reducing indexer overhead on AMD
 // MI350X": each key is loaded once for all of a request's verification
 // rows). The workgroup's page ids are read from the block table once, up
-// front, into LDS.
+// front, into LDS. Requests get workgroups in proportion to their pages
+// (wg_range, computed in the kernel from ctx_len), so ragged requests
+// finish together ("vLLM Day-0 Support for Kimi K3.1 Pro", section "Fused
+// low-latency decode for DSA layers": a key-balanced scorer).
 //
 // Streaming. The page copies go from HBM straight into a ring of kRing LDS
 // slots (global_load_lds, no VGPR staging) and kRing - 1 pages stay in
