@@ -31,6 +31,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -67,13 +68,21 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text):
+    """Source text without comments and whitespace (string literals kept), so
+    that only a change to the code itself changes the hash."""
+    text = re.sub(r'"(?:\\.|[^"\\])*"|/\*.*?\*/|//[^\n]*',
+                  lambda m: m.group(0) if m.group(0).startswith('"') else " ", text, flags=re.S)
+    return re.sub(r"\s+", "", text)
+
+
 def kernel_source_hash(name):
-    """Hash of a kernel's source file and every header beside it (what it may include)."""
+    """Hash of the code of a kernel's source file and of every header beside it (what it may include)."""
     csrc = os.path.join(ROOT, "sparse_attention_index_amd", "csrc")
     h = hashlib.sha256()
     for n in [name] + sorted(f for f in os.listdir(csrc) if f.endswith(".h")):
-        with open(os.path.join(csrc, n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(csrc, n), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -82,3 +82,11 @@ def test_counters_need_the_current_source(monkeypatch, tmp_path):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda name: "0" * 16)
     assert bench.counters_for("sparse_mla_kernel", "wl") is None
     assert bench.measured_step_bytes("wl", ["sparse_mla_kernel"]) is None
+
+
+def test_counter_hash_follows_code_not_comments():
+    a = "int f(int x) { return x + 1; }  // one\n/* note */\n"
+    b = "int f(int x)\n{\n  return x + 1;  // other words\n}\n"
+    c = "int f(int x) { return x + 2; }\n"
+    assert bench._code_only(a) == bench._code_only(b) != bench._code_only(c)
+    assert bench._code_only('const char* s = "// kept";') == 'constchar*s="//kept";'
