@@ -86,9 +86,9 @@ int64_t decode_ld(int32_t max_ctx) { return ((int64_t)max_ctx + 63) / 64 * 64; }
 
 // Candidate slots per row of the filtered decode, split into one region per
 // scoring workgroup of the row's request: the sampled threshold leaves about
-// 3k to 10k of a row's scores (the selection holds up to 16,384 in LDS and
-// selects from larger runs where they are); a workgroup that passes its
-// region sends the row to the exact fallback.
+// 3k to 8k of a row's scores at long contexts (the selection holds up to
+// 16,384 in LDS and selects from larger runs where they are); a workgroup
+// that passes its region sends the row to the exact fallback.
 int32_t filter_cap(int32_t rows) { return rows <= 128 ? 65536 : 32768; }
 
 struct DecodeWs {
@@ -99,6 +99,7 @@ struct DecodeWs {
   void* topk;
   void* mla;
   float* thr;       // filtered path: per-row score threshold
+  float* samp;      // filtered path: [rows][kSampleBufKeys] sampled scores
   uint32_t* fcount; // filtered path: [rows][kMaxFilterWg] candidates per scoring workgroup
   uint2* fcand;     // filtered path: [rows][filter_cap] candidates, one region per scoring workgroup
   uint2* fcompact;  // filtered path: [rows][filter_cap] a row's candidates in one run (past LDS capacity)
@@ -114,13 +115,15 @@ size_t decode_ws_parts(int32_t rows, int64_t max_ctx, int32_t k, DecodeWs* out, 
       align256(topk_ws_bytes(rows, ld)),                              // topk
       align256(mla_ws_bytes(rows, k, true)),                          // mla
       align256((size_t)rows * sizeof(float)),                         // thr
+      align256((size_t)rows * kSampleBufKeys * sizeof(float)),        // samp
       align256((size_t)rows * kMaxFilterWg * sizeof(uint32_t)),       // fcount
       align256((size_t)rows * filter_cap(rows) * sizeof(uint2)),      // fcand
       align256((size_t)rows * filter_cap(rows) * sizeof(uint2)),      // fcompact
   };
   size_t total = 0;
-  char* part[10];
-  for (int i = 0; i < 10; ++i) {
+  constexpr int kParts = sizeof(sizes) / sizeof(sizes[0]);
+  char* part[kParts];
+  for (int i = 0; i < kParts; ++i) {
     part[i] = static_cast<char*>(base) + total;
     total += sizes[i];
   }
@@ -132,9 +135,10 @@ size_t decode_ws_parts(int32_t rows, int64_t max_ctx, int32_t k, DecodeWs* out, 
     out->topk = part[4];
     out->mla = sizes[5] ? part[5] : nullptr;
     out->thr = reinterpret_cast<float*>(part[6]);
-    out->fcount = reinterpret_cast<uint32_t*>(part[7]);
-    out->fcand = reinterpret_cast<uint2*>(part[8]);
-    out->fcompact = reinterpret_cast<uint2*>(part[9]);
+    out->samp = reinterpret_cast<float*>(part[7]);
+    out->fcount = reinterpret_cast<uint32_t*>(part[8]);
+    out->fcand = reinterpret_cast<uint2*>(part[9]);
+    out->fcompact = reinterpret_cast<uint2*>(part[10]);
   }
   return total;
 }
@@ -335,7 +339,7 @@ static Filter filter_of(const dsa_batch* batch, const dsa_cache* cache, const vo
 // 1. each row's visible length and threshold (sampled, or the caller's)
 static int32_t filter_threshold(const Filter& F, const DecodeWs& p, int32_t rows, int32_t k, const float* thr_in,
                                 hipStream_t st) {
-  return hip_status(launch_sample_threshold(F.f, rows, k, thr_in, p.thr, p.row_len, st), "filter threshold");
+  return hip_status(launch_sample_threshold(F.f, rows, k, thr_in, p.samp, p.thr, p.row_len, st), "filter threshold");
 }
 // 2. score, keeping only the candidates at or above the threshold
 static int32_t filter_score(const Filter& F, const dsa_batch* batch, hipStream_t st) {

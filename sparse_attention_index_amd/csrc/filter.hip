@@ -21,10 +21,14 @@
 
 namespace dsa {
 
-static constexpr int kSamplePages = 32;              // pages sampled per row (2,048 keys)
+static constexpr int kSamplePages = 128;             // pages sampled per row (8,192 keys)
 static constexpr int kSampleKeys = kSamplePages * kBlock;
-static constexpr int kSampleThreads = 512;           // 8 waves, 4 sampled pages each
-static constexpr int kCandLds = 16384;               // candidates a selecting workgroup holds in LDS
+static_assert(kSampleKeys == kSampleBufKeys, "the workspace holds a row's samples");
+static constexpr int kSampleThreads = 512;           // most waves (one per row) scoring sampled pages
+static constexpr int kSelectThreads = 1024;          // threshold of a row from its samples
+static constexpr int kCandLds = 16384;               // candidates a selecting workgroup holds in LDS ...
+static constexpr int kCandLdsTbl = 8192;             // ... or this many, beside its request's page table
+static constexpr int kTblLds = 16384;                // pages of that table (1,048,576 tokens)
 
 // ------------------------------------------------------------------ one page, straight from HBM
 
@@ -120,28 +124,83 @@ DSA_DEV void score_page(const RowQuery<KF4>& q, const PageKeys<KF4>& p, float (&
 
 // ------------------------------------------------------------------ sampling pass
 
-// One workgroup per query row. The row's visible length n goes to row_len.
-// A row of more than kTakeAll tokens scores 2,048 sampled keys -- 32 whole
-// pages evenly spaced over the pages it sees in full -- and takes the
-// top-k's sampled threshold over them (sample_select: a little below the
-// sampled rank that leaves about 1.25k scores of the row above it), written
-// as the float a kept score must reach. Shorter rows keep every score
-// (-inf). With thr_in set the caller's thresholds are copied instead.
-template <bool KF4>
-__global__ __launch_bounds__(kSampleThreads) void sample_threshold_kernel(ScoreArgs a, int k, const float* thr_in,
-                                                                         float* thr, int32_t* row_len) {
-  constexpr int NT = kSampleThreads, NW = NT / 64, PPW = kSamplePages / NW;
-  __shared__ float samp[kSampleKeys];
+// Two kernels. The first scores the sampled pages of every row of more than
+// kTakeAll tokens: NSP whole pages (128, or 64 past 32 rows) evenly spaced
+// over the `full` pages that every such row of the request sees in full (at
+// least 128, so the sampled pages are distinct), sampled page j being page
+// floor(j * full / NSP). A workgroup takes PPW sampled pages of one request
+// for all its rows, one wave per row (rows w, w + 8, ... past 8 rows): the
+// waves load the same pages, so all but the first copy come from the CU's
+// cache, and the pages' latency is spread over B * NSP / PPW workgroups
+// (each wave splits its row's query once per workgroup). The second takes
+// each row's threshold from its samples (sample_select: a little below the
+// sampled rank that leaves about 1.25k of the row's scores above it).
+template <bool KF4, int NSP, int PPW, bool MULTI>
+__global__ __launch_bounds__(kSampleThreads) void sample_score_kernel(ScoreArgs a, float* __restrict__ samp) {
+  static_assert(NSP <= kSamplePages, "the workspace holds 128 sampled pages per row");
+  constexpr int WPQ = NSP / PPW;  // workgroups per request
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, n = lane & 31;
+  const int R = a.R, b = blockIdx.x / WPQ, j0 = (blockIdx.x % WPQ) * PPW;
+  const int64_t L = a.ctx_len[b];
+  if (L <= kTakeAll) return;  // no row of the request sees more (its last row sees L tokens)
+  // the query row and head weights of the wave's first row go out first:
+  // they depend on nothing, and their latency then overlaps the chain
+  // ctx_len -> page ids -> keys
+  QueryRaw<false, KF4> qraw;
+  fetch_query<false, KF4>(a, (size_t)b * R + wave, n, g, qraw);
+  uint32_t wbits = a.w[((size_t)b * R + wave) * kIdxHeads + n];
+  // pages every sampled row of the request sees in full: those of its first
+  // row, and at least 128 (a row with more than kTakeAll tokens sees them)
+  const int64_t first = (L - R + 1) / kBlock;
+  const uint32_t full = (uint32_t)(first > kSamplePages ? first : kSamplePages);
+  const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
+  int32_t pid[PPW];
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) pid[i] = table[(uint32_t)((uint64_t)(j0 + i) * full / NSP)];
+  PageKeys<KF4> pk[PPW];
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) load_page<KF4>(a, pid[i], pk[i]);
+  auto score_row = [&](int r) {
+    const size_t row = (size_t)b * R + r;
+    if (L - R + r + 1 <= kTakeAll) return;  // this row keeps every score
+    hold_query(qraw);
+    RowQuery<KF4> q;
+    finish_row_query<KF4>(qraw, wbits, q);
+    float* out = samp + row * kSampleKeys;
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      float v[2];
+      score_page<KF4>(q, pk[i], v);
+      if (g == 0) {
+        out[(j0 + i) * kBlock + n] = v[0];
+        out[(j0 + i) * kBlock + 32 + n] = v[1];
+      }
+    }
+  };
+  score_row(wave);
+  if constexpr (MULTI) {  // more than 8 rows: wave w also takes rows w + 8, w + 16, ...
+    for (int r = wave + kSampleThreads / 64; r < R; r += kSampleThreads / 64) {
+      const size_t row = (size_t)b * R + r;
+      fetch_query<false, KF4>(a, row, n, g, qraw);
+      wbits = a.w[row * kIdxHeads + n];
+      score_row(r);
+    }
+  }
+}
+
+// One workgroup per row: the row's visible length goes to row_len, and its
+// threshold to thr: -inf for rows of at most kTakeAll tokens (every score is
+// kept), the caller's with thr_in set, else the sampled one, written as the
+// float a kept score must reach.
+__global__ __launch_bounds__(kSelectThreads) void sample_select_kernel(const int32_t* __restrict__ ctx_len, int R,
+                                                                        const float* __restrict__ samp, int ns, int k,
+                                                                        const float* thr_in, float* thr,
+                                                                        int32_t* row_len) {
+  constexpr int NT = kSelectThreads;
   __shared__ uint32_t hist[kHistBins];
   __shared__ ScanLds<NT> scan;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, n = lane & 31;
-  const int row = blockIdx.x, R = a.R, b = row / R;
-  // the query row and head weights go out first: they depend on nothing,
-  // and their latency then overlaps the chain ctx_len -> page ids -> keys
-  QueryRaw<false, KF4> qraw;
-  fetch_query<false, KF4>(a, (size_t)row, n, g, qraw);
-  const uint32_t wbits = a.w[(size_t)row * kIdxHeads + n];
-  const int vis = a.ctx_len[b] - R + row % R + 1;
+  const int t = threadIdx.x, row = blockIdx.x;
+  const int64_t vis = (int64_t)ctx_len[row / R] - R + row % R + 1;
   const int64_t nvis = vis > 0 ? vis : 0;
   if (t == 0) row_len[row] = (int32_t)nvis;
   if (thr_in) {
@@ -152,34 +211,12 @@ __global__ __launch_bounds__(kSampleThreads) void sample_threshold_kernel(ScoreA
     if (t == 0) thr[row] = -INFINITY;
     return;
   }
-  const uint32_t full = (uint32_t)(nvis / kBlock);  // pages the row sees in full (> 128)
-  const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
-  // sampled page j (< 32) is full page floor(j * full / 32). The page ids,
-  // then every key load of the wave's four pages, are issued before the
-  // query is split, so the split overlaps their latency.
-  int32_t pid[PPW];
+  // ns samples: thread t holds samples t + NT i (i < ns / NT)
+  const float* s = samp + (size_t)row * kSampleKeys;
+  uint32_t raw[kSampleKeys / NT];
 #pragma unroll
-  for (int i = 0; i < PPW; ++i) pid[i] = table[((uint32_t)(wave * PPW + i) * full) / kSamplePages];
-  PageKeys<KF4> pk[PPW];
-#pragma unroll
-  for (int i = 0; i < PPW; ++i) load_page<KF4>(a, pid[i], pk[i]);
-  hold_query(qraw);
-  RowQuery<KF4> q;
-  finish_row_query<KF4>(qraw, wbits, q);
-#pragma unroll
-  for (int i = 0; i < PPW; ++i) {
-    float v[2];
-    score_page<KF4>(q, pk[i], v);
-    if (g == 0) {
-      samp[(wave * PPW + i) * kBlock + n] = v[0];
-      samp[(wave * PPW + i) * kBlock + 32 + n] = v[1];
-    }
-  }
-  __syncthreads();
-  uint32_t raw[kSample / NT];
-#pragma unroll
-  for (int i = 0; i < kSample / NT; ++i) raw[i] = t + NT * i < kSampleKeys ? __float_as_uint(samp[t + NT * i]) : 0u;
-  const uint32_t T = sample_select<NT>(raw, nvis, k, hist, scan, kSampleKeys);
+  for (int i = 0; i < kSampleKeys / NT; ++i) raw[i] = t + NT * i < ns ? __float_as_uint(s[t + NT * i]) : 0u;
+  const uint32_t T = sample_select<NT, kSampleKeys>(raw, nvis, k, hist, scan, ns);
   if (t == 0) thr[row] = key_threshold_float(T);
 }
 
@@ -192,8 +229,15 @@ struct CandLds {
   uint32_t off[kMaxFilterWg + 1];  // each workgroup region's first candidate in the row's run; the total last
   uint32_t wsum[kTF / 64];
   uint32_t wmax[kTF / 64];
-  uint2 elems[kCandLds];
+  union {
+    uint2 elems[kCandLds];
+    struct {
+      uint2 elems[kCandLdsTbl];  // the same storage as elems above
+      int32_t page[kTblLds];     // the request's page table: positions become cache rows as they are emitted
+    } tbl;
+  } u;
 };
+static_assert(sizeof(CandLds) <= 160 * 1024, "one selecting workgroup per CU");
 
 // One workgroup per row. a: the scorer's arguments (the fallback writes the
 // row's scores to a.scores); G: the scorer's workgroups per row group, split
@@ -217,6 +261,18 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
     emit_all_positions(row, R, n, k, out, so);
     return;
   }
+  const int npages = (int)((n + kBlock - 1) / kBlock);
+  // with cache rows asked for, the request's page table is loaded now (its
+  // latency overlaps the gather) and staged in LDS if the candidates leave
+  // room for it; else the rows are looked up after the selection
+  constexpr int kTblPer = kTblLds / kTF;
+  const bool tbl_fits = so.slots && npages <= kTblLds && npages <= so.max_blocks;
+  int32_t tpage[kTblPer];
+  if (tbl_fits) {
+    const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
+#pragma unroll
+    for (int i = 0; i < kTblPer; ++i) tpage[i] = table[t + kTF * i < npages ? t + kTF * i : 0];
+  }
   // the scoring workgroups of this row's request, as the scorer split them
   const WgRange wr = wg_range(a.ctx_len, B, G, 0, row / R);
   const int nw = wr.count;  // <= kMaxFilterWg (checked by the host)
@@ -235,47 +291,61 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
   if (t < nw) L.off[t] = before + incl - c;
   if (t == 0) L.off[nw] = total;
   __syncthreads();
-  const Emit emit{out, nullptr, nullptr};
   const uint2* regions = a.cand + (size_t)row * a.cap;
+  bool slots_done = false;
   if (!bad && total >= (uint32_t)k) {
-    // gather: wave w copies the regions w, w + 16, ..., four regions' loads
-    // in flight per lane, into LDS when they fit, else into the row's
-    // compact run; and finds the largest key
+    // gather: wave w copies the regions w, w + 16, ..., sixteen at a time
+    // (the first 64 candidates of each, one load per lane: a single round
+    // trip for up to 256 regions), into LDS when they fit, else into the
+    // row's compact run; and finds the largest key
     const bool in_lds = total <= (uint32_t)kCandLds;
-    uint2* dst = in_lds ? L.elems : compact + (size_t)row * a.cap;
+    const bool with_tbl = tbl_fits && total <= (uint32_t)kCandLdsTbl;
+    uint2* const run = compact + (size_t)row * a.cap;
+    constexpr int kBatch = 16;
     uint32_t kmax = 0;
-    for (int r0 = wave; r0 < nw; r0 += 4 * (kTF / 64)) {
-      uint2 v[4][2];
+    // dst: LDS or the compact run (the branch on in_lds is uniform, so each
+    // copy loop stores to one kind of memory only)
+    auto gather = [&](uint2* dst) {
+      for (int r0 = wave; r0 < nw; r0 += kBatch * (kTF / 64)) {
+        // Every lane loads (no branch around the loads, so that all sixteen
+        // are in flight at once): lanes past a region's count re-read its
+        // slot 0, regions past the last re-read region 0's (in bounds: a
+        // region's count is at most sub here).
+        uint2 v[kBatch];
+        uint32_t o[kBatch], cr[kBatch];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = r0 + u * (kTF / 64);
-        const uint32_t cr = r < nw ? L.off[r + 1] - L.off[r] : 0u;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t j = lane + 64 * e;
-          v[u][e] = j < cr ? regions[(size_t)r * sub + j] : make_uint2(0u, 0u);
+        for (int u = 0; u < kBatch; ++u) {
+          const int r = r0 + u * (kTF / 64);
+          o[u] = r < nw ? L.off[r] : 0u;
+          cr[u] = r < nw ? L.off[r + 1] - o[u] : 0u;
+          const uint32_t j = (uint32_t)lane < cr[u] ? (uint32_t)lane : 0u;
+          v[u] = regions[(size_t)(r < nw ? r : 0) * sub + j];
         }
-      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = r0 + u * (kTF / 64);
-        const uint32_t o = r < nw ? L.off[r] : 0u;
-        const uint32_t cr = r < nw ? L.off[r + 1] - o : 0u;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t j = lane + 64 * e;
-          if (j < cr) {
-            dst[o + j] = v[u][e];
-            kmax = max(kmax, v[u][e].x);
+        for (int u = 0; u < kBatch; ++u) {
+          if ((uint32_t)lane < cr[u]) {
+            dst[o[u] + lane] = v[u];
+            kmax = max(kmax, v[u].x);
           }
         }
-        // regions of more than 128 candidates: the rest, one pass per 64
-        for (uint32_t j = 128 + lane; j < cr; j += 64) {
-          const uint2 x = regions[(size_t)r * sub + j];
-          dst[o + j] = x;
-          kmax = max(kmax, x.x);
+        // regions of more than 64 candidates: the rest, one pass per 64
+        // (unrolled: o and cr stay in registers)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int r = r0 + u * (kTF / 64);
+          for (uint32_t j = 64 + lane; j < cr[u]; j += 64) {
+            const uint2 x = regions[(size_t)r * sub + j];
+            dst[o[u] + j] = x;
+            kmax = max(kmax, x.x);
+          }
         }
       }
+    };
+    if (in_lds) gather(L.u.elems);
+    else gather(run);
+    if (with_tbl) {  // after the gather's loads: waiting for the table then costs nothing
+#pragma unroll
+      for (int i = 0; i < kTblPer; ++i) L.u.tbl.page[t + kTF * i] = tpage[i];
     }
     const uint32_t wm = wave_max32(kmax);
     if (lane == 0) L.wmax[wave] = wm;
@@ -283,10 +353,13 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
     __syncthreads();
     kmax = wave_max32(lane < kTF / 64 ? L.wmax[lane] : 0u);
     const uint64_t lo = (uint64_t)T << 32, hi = ((uint64_t)kmax << 32) | 0xffffffffull;
+    const Emit emit{out, with_tbl ? so.slots + (size_t)row * k : nullptr, L.u.tbl.page};
+    slots_done = with_tbl;
     if (in_lds)
-      select_top(L.s, total, k, emit, [&](int64_t i) { return composite(L.elems[i].x, L.elems[i].y); }, true, lo, hi);
+      select_top(L.s, total, k, emit, [&](int64_t i) { return composite(L.u.elems[i].x, L.u.elems[i].y); }, true, lo,
+                 hi);
     else
-      select_top(L.s, total, k, emit, [&](int64_t i) { const uint2 e = dst[i]; return composite(e.x, e.y); }, true, lo,
+      select_top(L.s, total, k, emit, [&](int64_t i) { const uint2 e = run[i]; return composite(e.x, e.y); }, true, lo,
                  hi);
   } else {
     // the candidates cannot decide this row: score it in full (waves take
@@ -295,7 +368,6 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
     const int32_t* table = a.block_table + (size_t)(row / R) * a.max_blocks;
     RowQuery<KF4> q;
     row_query<KF4>(a, (size_t)row, q);
-    const int npages = (int)((n + kBlock - 1) / kBlock);
     const int nl = lane & 31;
     for (int p = wave; p < npages; p += kTF / 64) {
       PageKeys<KF4> pk;
@@ -312,9 +384,10 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
     }
     __threadfence();  // the row is read back by the whole workgroup
     __syncthreads();
+    const Emit emit{out, nullptr, nullptr};
     select_top(L.s, n, k, emit, [&](int64_t i) { return composite(ordered_key(srow[i]), (uint32_t)i); });
   }
-  if (so.slots) {
+  if (so.slots && !slots_done) {  // uniform
     __syncthreads();  // the selection is written (workgroup-visible)
     emit_slots(row, R, k, out, so);
   }
@@ -322,14 +395,38 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_sample_threshold(const ScoreArgs& a, int rows, int k, const float* thr_in, float* thr,
+// Pages sampled per row: 128 (8,192 keys) for up to 32 rows, 64 beyond,
+// where the sampling pass would otherwise cost more than the tighter
+// threshold saves the selection.
+static int sampled_pages(int rows) { return rows > 32 ? 64 : kSamplePages; }
+
+template <bool KF4, int NSP, int PPW, bool MULTI>
+static void launch_sample_score(const ScoreArgs& a, int rows, float* samp, hipStream_t st) {
+  const int B = rows / a.R, waves = MULTI ? kSampleThreads / 64 : a.R;
+  hipLaunchKernelGGL((sample_score_kernel<KF4, NSP, PPW, MULTI>), dim3(B * (NSP / PPW)), dim3(64 * waves), 0, st, a,
+                     samp);
+}
+
+template <bool KF4>
+static void launch_sample_score(const ScoreArgs& a, int rows, float* samp, hipStream_t st) {
+  const bool multi = a.R > kSampleThreads / 64;
+  if (sampled_pages(rows) == kSamplePages) {
+    if (multi) launch_sample_score<KF4, kSamplePages, 2, true>(a, rows, samp, st);
+    else launch_sample_score<KF4, kSamplePages, 2, false>(a, rows, samp, st);
+  } else {
+    if (multi) launch_sample_score<KF4, 64, 2, true>(a, rows, samp, st);
+    else launch_sample_score<KF4, 64, 2, false>(a, rows, samp, st);
+  }
+}
+
+hipError_t launch_sample_threshold(const ScoreArgs& a, int rows, int k, const float* thr_in, float* samp, float* thr,
                                    int32_t* row_len, hipStream_t st) {
-  if (a.key_fp4)
-    hipLaunchKernelGGL(sample_threshold_kernel<true>, dim3(rows), dim3(kSampleThreads), 0, st, a, k, thr_in, thr,
-                       row_len);
-  else
-    hipLaunchKernelGGL(sample_threshold_kernel<false>, dim3(rows), dim3(kSampleThreads), 0, st, a, k, thr_in, thr,
-                       row_len);
+  if (!thr_in) {
+    if (a.key_fp4) launch_sample_score<true>(a, rows, samp, st);
+    else launch_sample_score<false>(a, rows, samp, st);
+  }
+  hipLaunchKernelGGL(sample_select_kernel, dim3(rows), dim3(kSelectThreads), 0, st, a.ctx_len, a.R, samp,
+                     sampled_pages(rows) * kBlock, k, thr_in, thr, row_len);
   return hipGetLastError();
 }
 

@@ -45,13 +45,14 @@ constexpr int kMaxFilterWg = 1024;
 // gets at most grid - B + 1 of them.
 int filter_grid(int B, int R, int max_ctx, bool mxfp4);
 
-// Sampling pass of the filtered decode, one workgroup per row: the row's
-// visible length goes to row_len and its score threshold to thr (-inf for
-// rows of at most 8,192 tokens: everything is kept). A row of more tokens
-// scores 2,048 sampled keys (32 whole pages evenly spaced over its full
-// pages) and takes the top-k's sampled threshold over them. With thr_in set,
-// thr[row] = thr_in[row] and nothing is sampled.
-hipError_t launch_sample_threshold(const ScoreArgs& a, int rows, int k, const float* thr_in, float* thr,
+// Sampling pass of the filtered decode: each row's visible length goes to
+// row_len and its score threshold to thr (-inf for rows of at most 8,192
+// tokens: everything is kept). A row of more tokens scores 8,192 sampled
+// keys (128 whole pages evenly spaced over its full pages; 4,096 past 32
+// rows) into samp[row] and takes the top-k's sampled threshold over them.
+// With thr_in set, thr[row] = thr_in[row] and nothing is sampled.
+constexpr int kSampleBufKeys = 8192;  // samp row stride
+hipError_t launch_sample_threshold(const ScoreArgs& a, int rows, int k, const float* thr_in, float* samp, float* thr,
                                    int32_t* row_len, hipStream_t st);
 
 struct TopkWs {

@@ -250,18 +250,19 @@ DSA_DEV void sample_load(const float* __restrict__ s, int64_t n, uint32_t (&raw)
 }
 
 // sample_select: the ordered-key threshold T from the samples; every element
-// is kept (T = 0) for rows of at most kTakeAll elements.
-template <int NT>
-DSA_DEV uint32_t sample_select(const uint32_t (&raw)[kSample / NT], int64_t n, int k, uint32_t* hist,
+// is kept (T = 0) for rows of at most kTakeAll elements. Thread t holds
+// samples t + NT i (i < NS / NT; NS bounds the sample count).
+template <int NT, int NS = kSample>
+DSA_DEV uint32_t sample_select(const uint32_t (&raw)[NS / NT], int64_t n, int k, uint32_t* hist,
                                ScanLds<NT>& scan, int ns_given = 0) {
   const int t = threadIdx.x;
   if (n <= kTakeAll) return 0u;
   // ns_given: the number of samples when the caller drew its own
   const int ns = ns_given > 0 ? ns_given : (n > (1 << 18) ? 4096 : 2048);
   const int per = ns / NT;
-  uint32_t key[kSample / NT];
+  uint32_t key[NS / NT];
 #pragma unroll
-  for (int i = 0; i < kSample / NT; ++i) key[i] = ordered_key(__uint_as_float(raw[i]));
+  for (int i = 0; i < NS / NT; ++i) key[i] = ordered_key(__uint_as_float(raw[i]));
   // Rank m of the threshold among the samples: the samples expected above
   // the k-th score of the row (e = k ns / n) times 1.25, plus 3 standard
   // deviations of that count (sqrt e) and 8, so that a threshold above the
@@ -276,7 +277,7 @@ DSA_DEV uint32_t sample_select(const uint32_t (&raw)[kSample / NT], int64_t n, i
   const int lane = t & 63, wave = t >> 6;
   uint32_t lo = ~0u, hi = 0u;
 #pragma unroll
-  for (int i = 0; i < kSample / NT; ++i)
+  for (int i = 0; i < NS / NT; ++i)
     if (i < per) {
       lo = min(lo, key[i]);
       hi = max(hi, key[i]);
@@ -300,7 +301,7 @@ DSA_DEV uint32_t sample_select(const uint32_t (&raw)[kSample / NT], int64_t n, i
     for (int i = t; i < kHistBins; i += NT) hist[i] = 0;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kSample / NT; ++i)
+    for (int i = 0; i < NS / NT; ++i)
       if (i < per && (shift == 32 || (key[i] >> shift) == prefix))
         atomicAdd(&hist[(key[i] >> lo_bit) & ((1u << width) - 1)], 1u);
     __syncthreads();
@@ -348,7 +349,8 @@ struct SelectLds {
 //  2. One 11-bit step finds the bin b holding the k-th largest; a second
 //     pass emits everything above b and gathers b's elements into LDS.
 //  3. Further 11-bit steps over the gathered elements resolve the rest
-//     (without the gather, when b holds more than kBinLds elements).
+//     (without the gather, when b holds more than kBinLds elements); a bin
+//     of at most 64 elements is ranked by one wave instead.
 // Where the i-th selected position goes: out[i], and with a page table also
 // its physical cache slot (page id * 64 + offset) to slots[i].
 struct Emit {
@@ -450,6 +452,23 @@ DSA_DEV void select_top(SelectLds& L, int64_t count, int k, const Emit& out, Com
         const uint32_t slot = wave_append(&L.emitted, take);
         if (take && emitted0 + slot < (uint32_t)k) out(emitted0 + slot, ~(uint32_t)c);
       }
+    }
+    return;
+  }
+  // a bin of at most 64 gathered elements: the first wave ranks them (each
+  // lane counts the larger composites of the bin; they are distinct) and
+  // emits the `need` largest, with no more barriers
+  if (gather && th.at <= 64) {
+    if (t < 64) {
+      const uint32_t nbin = th.at;
+      const uint64_t c = (uint32_t)t < nbin ? L.bin[t] : 0ull;
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < nbin; ++j) {  // uniform trip count
+        const uint64_t cj = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(c >> 32), j) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((uint32_t)c, j);
+        rank += cj > c ? 1u : 0u;
+      }
+      if ((uint32_t)t < nbin && rank < need) out(emitted0 + rank, ~(uint32_t)c);
     }
     return;
   }

@@ -44,6 +44,8 @@ FUSED_ONLY = {
     "40x4_many_rows": dict(B=40, R=4, lengths=[45000 + 97 * b for b in range(40)], seed=114, device="cuda"),
     # filtered decode with seven verification rows per request (two rows per wave)
     "2x7_filtered": dict(B=2, R=7, lengths=[45000, 70001], seed=115, permute_blocks=True),
+    # ten rows per request: the sampling pass's waves take a second row each
+    "1x10_filtered": dict(B=1, R=10, lengths=[52000], seed=116, permute_blocks=True),
 }
 
 
@@ -284,7 +286,7 @@ def test_sparse_mla_skips_invalid_entries(gpu):
 
 
 @pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "3x3_short_perm", "1x8", "2x2_long_perm",
-                                  "5x3_filtered_ragged", "2x7_filtered"])
+                                  "5x3_filtered_ragged", "2x7_filtered", "1x10_filtered"])
 def test_fused_decode_matches_oracle_and_stages(gpu, name):
     case = _case(name)
     out, lse, idx = gpu_decode(case)
@@ -347,7 +349,8 @@ def _kth_scores(case, k):
     return torch.topk(s, min(k, n), dim=1).values[:, -1].contiguous()
 
 
-@pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "1x1_8k", "40x4_many_rows", "2x7_filtered"])
+@pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "1x1_8k", "40x4_many_rows", "2x7_filtered",
+                                  "1x10_filtered"])
 def test_thresholded_decode_equals_the_staged_path_whatever_the_threshold(gpu, name):
     """The filtered decode with caller-given thresholds against the stored
     path (dsa_index_score -> dsa_topk -> dsa_sparse_mla_decode). Too high a
@@ -386,7 +389,7 @@ def test_thresholded_decode_equals_the_staged_path_whatever_the_threshold(gpu, n
 
 
 @pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "2x4_ragged_perm", "40x4_many_rows",
-                                  "2x7_filtered"])
+                                  "2x7_filtered", "1x10_filtered"])
 def test_filter_stage_entry_points_select_the_stored_top_k(gpu, name):
     """dsa_filter_threshold -> dsa_filter_score -> dsa_filter_select, called
     one by one on a workspace that starts with stale bytes, select exactly
