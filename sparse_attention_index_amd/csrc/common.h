@@ -67,6 +67,16 @@ DSA_DEV void copy4_to_lds(const void* src, void* lds_base) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(base) : "memory");
 }
+// The same copies from a wave-uniform base plus a per-lane 32-bit byte
+// offset (the base lives in scalar registers: no 64-bit address per lane).
+DSA_DEV void copy16_to_lds_at(const void* sbase, uint32_t off, void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sbase), "s"(m0) : "memory");
+}
+DSA_DEV void copy4_to_lds_at(const void* sbase, uint32_t off, void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(sbase), "s"(m0) : "memory");
+}
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>

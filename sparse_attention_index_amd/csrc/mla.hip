@@ -474,7 +474,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaPart part, uint16_t
 
 static int splits_for(int rows, int k) {
   int s = (256 + rows - 1) / rows;  // aim at one workgroup per CU
-  const int max_s = (k + 2 * TK - 1) / (2 * TK);  // at least two tiles per split
+  const int max_s = (k + TK - 1) / TK;  // at least one tile per split
   if (s > max_s) s = max_s;
   if (s > 64) s = 64;
   if (s < 1) s = 1;

@@ -164,9 +164,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // MXFP4 pages: 4 copies of 1 KB (16-byte chunks of 64-byte key rows,
   // chunk c of key r at position c ^ ((r >> 2) & 3)) and one of the 64 keys'
   // E8M0 words; waves 0 and 1 issue two key copies each, wave 2 the scales.
+  // Page bases are wave-uniform (scalar registers); lanes add 32-bit offsets.
   auto issue = [&](int i) {
     const int slot = i % kRing;
-    const size_t page = (size_t)tbl_s[i];
+    const size_t page = (uint32_t)__builtin_amdgcn_readfirstlane(tbl_s[i]);
     if constexpr (KF4) {
       const uint8_t* pg = a.key_fp4 + page * kF4KeyBytes;
 #pragma unroll
@@ -175,9 +176,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if (j < kF4Copies - 1) {
           const int c = 64 * j + lane;
           const int key = c >> 2;
-          copy16_to_lds(pg + key * (kIdxDim / 2) + (((c & 3) ^ ((key >> 2) & 3)) << 4), key_s[slot] + 1024 * j);
+          copy16_to_lds_at(pg, (uint32_t)(key * (kIdxDim / 2) + (((c & 3) ^ ((key >> 2) & 3)) << 4)),
+                           key_s[slot] + 1024 * j);
         } else if (j == kF4Copies - 1) {
-          copy4_to_lds(a.key_e8m0 + (page * kBlock + lane) * 4, ks_s[slot]);
+          copy4_to_lds_at(a.key_e8m0 + page * kBlock * 4, (uint32_t)lane * 4, ks_s[slot]);
         }
       }
       return;
@@ -189,9 +191,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       if (j < kCopies - 1) {
         const int c = 64 * j + lane;
         const int key = c >> 3;
-        copy16_to_lds(pg + key * kIdxDim + (((c & 7) ^ ((key >> 1) & 7)) << 4), key_s[slot] + 1024 * j);
+        copy16_to_lds_at(pg, (uint32_t)(key * kIdxDim + (((c & 7) ^ ((key >> 1) & 7)) << 4)), key_s[slot] + 1024 * j);
       } else {
-        copy4_to_lds(a.key_scale + page * kBlock + lane, ks_s[slot]);
+        copy4_to_lds_at(a.key_scale + page * kBlock, (uint32_t)lane * 4, ks_s[slot]);
       }
     }
   };
