@@ -75,10 +75,18 @@ static constexpr int kRing = 4;                     // LDS page slots per workgr
 // Pages one workgroup walks at most (its page ids are staged in LDS): 4,096
 // for the 16-row prefill variant, whose registers already hold it to two
 // workgroups per CU, so that a 256K-token chunk still takes one round of
-// them; 2,048 for the others, where more would cost a resident workgroup.
+// them; 1,024 for one row per wave, so that four workgroups fit a CU's LDS;
+// 2,048 for the others, where more would cost a resident workgroup.
 template <int RPW>
 constexpr int max_wg_pages() {
-  return RPW == 4 ? 4096 : 2048;
+  return RPW == 4 ? 4096 : (RPW == 1 ? 1024 : 2048);
+}
+// Waves per SIMD the register allocation aims at: four for the filtered
+// decode with one bf16 row per wave and FP8 keys (128 registers: four
+// workgroups per CU, measured 3-4% faster than three), two otherwise.
+template <int RPW, bool QFP8, bool KF4, bool FILT>
+constexpr int score_waves_per_eu() {
+  return FILT && RPW == 1 && !QFP8 && !KF4 ? 4 : 2;
 }
 static constexpr int kThreads = 256;                // 4 waves
 static constexpr int kCopies = kKeyBytes / 1024 + 1;  // copy instructions per page (keys + scales)
@@ -112,8 +120,9 @@ static constexpr uint32_t kPastEnd = 0x80000000u;
 enum WaveRole { kCopier, kFlusher };
 
 template <int RPW, bool QFP8, bool KF4, bool FILT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void score_kernel(ScoreArgs a,
-                                                                                                 int B) {
+__global__ __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(score_waves_per_eu<RPW, QFP8, KF4, FILT>()))) void score_kernel(ScoreArgs a,
+                                                                                                       int B) {
   constexpr int ROWS = 4 * RPW;
   constexpr int NT = QFP8 ? 1 : 2;  // E4M3 terms per query value
   constexpr int LAG = 2;             // a page's scores are complete two barriers later
