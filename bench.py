@@ -48,6 +48,13 @@ FILTER_MIN_CTX = 40960
 SHORT_TOPK_MAX = 40960
 
 
+def sample_kernels(rows, R, mxfp4):
+    """The sampling pass's two kernels as profiles name them: 128 sampled pages per row up to 32
+    rows, 64 beyond; waves take several rows past 8 rows per request (filter.hip)."""
+    nsp = 128 if rows <= 32 else 64
+    return [f"sample_score_kernel<{str(mxfp4).lower()},{nsp},2,{str(R > 8).lower()}>", "sample_select_kernel"]
+
+
 def score_rpw(R, q_fp8=False):
     """Query rows per wave of the scorer variant a row group of R rows takes (csrc/score.hip)."""
     if q_fp8:
@@ -344,8 +351,8 @@ def run_decode(args, torch, dsa, traffic, cfg):
         score_us = stage_us["score"]
         dom_bytes = traffic.filter_scorer_bytes(lens, R, kfmt)
         dom_kernel = f"score_kernel<{score_rpw(R)},false,{str(kfmt == 'mxfp4').lower()},true>"
-        step_kernels = ["sample_threshold_kernel<%s>" % str(kfmt == "mxfp4").lower(), dom_kernel,
-                        "candidate_select_kernel<%s>" % str(kfmt == "mxfp4").lower()]
+        step_kernels = sample_kernels(len(lens) * R, R, kfmt == "mxfp4") + [
+            dom_kernel, "candidate_select_kernel<%s>" % str(kfmt == "mxfp4").lower()]
     else:
         stage_us = stored
         # ---- dominant kernel: the indexer scorer (its share of the step grows with context),

@@ -283,7 +283,7 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
  *              so idx, out and lse are those of dsa_decode whatever it is.
  * Other arguments and the workspace are dsa_decode's. Returns
  * DSA_ERR_UNSUPPORTED if a request would need more than 1,024 scoring
- * workgroups (contexts beyond about 128M tokens).
+ * workgroups (contexts beyond about 64M tokens).
  */
 int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
                                const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale,
@@ -300,10 +300,11 @@ int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, c
  * layers": a scorer that keeps candidates for an exact top-k select).
  *   dsa_filter_threshold  each row's visible length and candidate threshold:
  *       the caller's (threshold, fp32 [rows] on the device, any value as in
- *       dsa_decode_thresholded) or, with threshold NULL, sampled: 2,048 of
- *       the row's scores (32 whole pages spread over its context) and a
- *       value a little below the sampled rank that leaves about 1.25k scores
- *       of the row above it; rows of at most 8,192 tokens keep every score.
+ *       dsa_decode_thresholded) or, with threshold NULL, sampled: 8,192 of
+ *       the row's scores (128 whole pages spread over its context; 4,096
+ *       scores from 64 pages past 32 rows) and a value a little below the
+ *       sampled rank that leaves about 1.25k scores of the row above it;
+ *       rows of at most 8,192 tokens keep every score.
  *   dsa_filter_score      every score at or above its row's threshold, as
  *       (score, position), into the workspace; nothing else is stored.
  *   dsa_filter_select     idx int32 [rows][k]: the k largest candidates of
@@ -312,7 +313,7 @@ int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, c
  *       all of it.
  * q_idx and w are dsa_index_score's bf16 query and head weights. Returns
  * DSA_ERR_UNSUPPORTED if a request would need more than 1,024 scoring
- * workgroups (contexts beyond about 128M tokens).
+ * workgroups (contexts beyond about 64M tokens).
  */
 int32_t dsa_filter_threshold(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
                              int32_t k, const float* threshold, void* ws, size_t ws_bytes, void* stream);

@@ -430,18 +430,21 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaPart part, uint16_t
   const int d = 64 * blockIdx.x + 4 * j;
   const float* po = part.o + (size_t)row * S * kMlaHeads * kV + h * kV + d;
   constexpr size_t kSplitStride = (size_t)kMlaHeads * kV;
-  f32x4 v[8];
+  // The first 16 splits' partial outputs are loaded before the weights are
+  // known, all at once: every load is issued (splits past the last re-read
+  // it; those values are never used), no branch waits on one of them.
+  constexpr int kFirst = 16;
+  f32x4 v[kFirst];
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    v[u] = u < S ? *reinterpret_cast<const f32x4*>(po + u * kSplitStride) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < kFirst; ++u) v[u] = *reinterpret_cast<const f32x4*>(po + (u < S ? u : S - 1) * kSplitStride);
   const float2* ml = reinterpret_cast<const float2*>(part.ml) + (size_t)row * S * kMlaHeads;
   float m[4], l[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int s = j + 16 * u;
-    const float2 x = s < S ? ml[s * kMlaHeads + h] : make_float2(-INFINITY, 0.f);
-    m[u] = x.x;
-    l[u] = x.y;
+    const float2 x = ml[(s < S ? s : S - 1) * kMlaHeads + h];
+    m[u] = s < S ? x.x : -INFINITY;
+    l[u] = s < S ? x.y : 0.f;
   }
   const float M = row_max16(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])));
   float L = 0.f;
@@ -457,9 +460,9 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaPart part, uint16_t
   __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
+  for (int u = 0; u < kFirst; ++u)
     if (u < S) acc += v[u] * wgt_s[u][h];
-  for (int s0 = 8; s0 < S; s0 += 8) {
+  for (int s0 = kFirst; s0 < S; s0 += 8) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       v[u] = s0 + u < S ? *reinterpret_cast<const f32x4*>(po + (s0 + u) * kSplitStride) : f32x4{0.f, 0.f, 0.f, 0.f};

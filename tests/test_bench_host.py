@@ -26,8 +26,8 @@ def _step_kernels(cfg, filtered):
     R = cfg["R"]
     fmt = str(cfg.get("key_format", "fp8") == "mxfp4").lower()
     if filtered:
-        ks = [f"sample_threshold_kernel<{fmt}>", f"score_kernel<{bench.score_rpw(R)},false,{fmt},true>",
-              f"candidate_select_kernel<{fmt}>"]
+        ks = bench.sample_kernels(len(cfg["lengths"]) * R, R, fmt == "true") + [
+            f"score_kernel<{bench.score_rpw(R)},false,{fmt},true>", f"candidate_select_kernel<{fmt}>"]
     else:
         ks = [f"score_kernel<{bench.score_rpw(R)},false,{fmt},false>", "topk_short_kernel<true>"]
     return ks + ["sparse_mla_kernel", "mla_combine_kernel"]
@@ -82,6 +82,12 @@ def test_counters_need_the_current_source(monkeypatch, tmp_path):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda name: "0" * 16)
     assert bench.counters_for("sparse_mla_kernel", "wl") is None
     assert bench.measured_step_bytes("wl", ["sparse_mla_kernel"]) is None
+
+
+def test_sample_kernel_names_follow_the_row_count():
+    assert bench.sample_kernels(16, 4, False) == ["sample_score_kernel<false,128,2,false>", "sample_select_kernel"]
+    assert bench.sample_kernels(64, 4, True) == ["sample_score_kernel<true,64,2,false>", "sample_select_kernel"]
+    assert bench.sample_kernels(10, 10, False)[0] == "sample_score_kernel<false,128,2,true>"
 
 
 def test_counter_hash_follows_code_not_comments():
