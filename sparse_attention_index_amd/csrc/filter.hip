@@ -262,17 +262,12 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
     return;
   }
   const int npages = (int)((n + kBlock - 1) / kBlock);
-  // with cache rows asked for, the request's page table is loaded now (its
-  // latency overlaps the gather) and staged in LDS if the candidates leave
-  // room for it; else the rows are looked up after the selection
+  // with cache rows asked for, the request's page table is staged in LDS
+  // if the candidates leave room for it (copied straight into LDS beside the
+  // gather, so its latency overlaps the gather's); else the rows are looked
+  // up after the selection
   constexpr int kTblPer = kTblLds / kTF;
   const bool tbl_fits = so.slots && npages <= kTblLds && npages <= so.max_blocks;
-  int32_t tpage[kTblPer];
-  if (tbl_fits) {
-    const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
-#pragma unroll
-    for (int i = 0; i < kTblPer; ++i) tpage[i] = table[t + kTF * i < npages ? t + kTF * i : 0];
-  }
   // the scoring workgroups of this row's request, as the scorer split them
   const WgRange wr = wg_range(a.ctx_len, B, G, 0, row / R);
   const int nw = wr.count;  // <= kMaxFilterWg (checked by the host)
@@ -341,12 +336,20 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
         }
       }
     };
+    if (with_tbl) {
+      // entry (16 i + w) 64 + lane of the table for lane `lane` of wave w,
+      // copy i (entries past the request's pages re-read entry 0); issued
+      // just before the gather's loads, so waiting for those waits for these
+      const int32_t* table = so.block_table + (size_t)(row / R) * so.max_blocks;
+#pragma unroll
+      for (int i = 0; i < kTblPer; ++i) {
+        const int base = (kTF / 64 * i + wave) * 64;
+        copy4_to_lds(table + (base + lane < npages ? base + lane : 0), &L.u.tbl.page[base]);
+      }
+    }
     if (in_lds) gather(L.u.elems);
     else gather(run);
-    if (with_tbl) {  // after the gather's loads: waiting for the table then costs nothing
-#pragma unroll
-      for (int i = 0; i < kTblPer; ++i) L.u.tbl.page[t + kTF * i] = tpage[i];
-    }
+    if (with_tbl) wait_vmcnt<0>();  // the table copies have landed (the barrier below publishes them)
     const uint32_t wm = wave_max32(kmax);
     if (lane == 0) L.wmax[wave] = wm;
     if (!in_lds) __threadfence();  // the compact run is read back by the whole workgroup
@@ -355,12 +358,16 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
     const uint64_t lo = (uint64_t)T << 32, hi = ((uint64_t)kmax << 32) | 0xffffffffull;
     const Emit emit{out, with_tbl ? so.slots + (size_t)row * k : nullptr, L.u.tbl.page};
     slots_done = with_tbl;
+    // a row that keeps every score (threshold -inf) has no useful lower
+    // bound: select_top then finds the extremes itself (a bound at -inf would
+    // put every candidate in the first radix step's top bin)
+    const bool bounded = T > ordered_key(-INFINITY);
     if (in_lds)
-      select_top(L.s, total, k, emit, [&](int64_t i) { return composite(L.u.elems[i].x, L.u.elems[i].y); }, true, lo,
-                 hi);
+      select_top(L.s, total, k, emit, [&](int64_t i) { return composite(L.u.elems[i].x, L.u.elems[i].y); },
+                 bounded, lo, hi);
     else
-      select_top(L.s, total, k, emit, [&](int64_t i) { const uint2 e = run[i]; return composite(e.x, e.y); }, true, lo,
-                 hi);
+      select_top(L.s, total, k, emit, [&](int64_t i) { const uint2 e = run[i]; return composite(e.x, e.y); },
+                 bounded, lo, hi);
   } else {
     // the candidates cannot decide this row: score it in full (waves take
     // pages w, w + 16, ...) and select over the whole row

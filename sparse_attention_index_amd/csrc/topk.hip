@@ -97,6 +97,7 @@ struct ShortLds {
   SelectLds f;
   uint32_t cnt;
   uint32_t wmax[kTF / 64];
+  uint32_t wmin[kTF / 64];
   int32_t tbl[kShortMax / kBlock];  // page ids of the row's request (when slots are emitted)
   uint2 elems[kFinalLds + 1];       // survivors, plus one spare entry taking overflow writes
 };
@@ -177,42 +178,53 @@ __global__ __launch_bounds__(kTF) void topk_short_kernel(const float* __restrict
       }
     }
   }
-  // survivors -> LDS as (score bits, position), in batches of 8 scores: one
-  // reservation per wave and batch; slots past the buffer all land on its
-  // spare last entry. The row maximum bounds the survivors from above.
-  float mx = -INFINITY;
+  // survivors -> LDS as (score bits, position): one reservation per wave;
+  // slots past the buffer all land on its spare last entry. The row's
+  // largest score bounds the survivors from above, and the larger of T and
+  // its smallest from below (rows that keep everything have T = 0: a bound
+  // at 0 would put all of them in the first radix step's top bin).
+  float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
-  for (int j = 0; j < kShortPer; ++j) mx = fmaxf(mx, x[j]);  // NaN operands are ignored
+  for (int j = 0; j < kShortPer; ++j) {  // NaN operands are ignored
+    mx = fmaxf(mx, x[j]);
+    mn = fminf(mn, x[j]);
+  }
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j) mine += (uint32_t)(x[j] >= Tf);
+  uint32_t total;
+  const uint32_t pre = wave_prefix_small<6>(mine, total);
+  uint32_t slot = wave_reserve(&L.cnt, total) + pre;
   uint32_t pbase = (uint32_t)(4 * t);
-  asm volatile("" : "+v"(pbase));  // keeps the compiler from precomputing every position
+  float tf = Tf;
+  // keeps the compiler from precomputing every position, and makes the
+  // comparisons again here rather than holding forty masks from the count
+  // above in scalar registers (which spill)
+  asm volatile("" : "+v"(pbase), "+v"(tf));
 #pragma unroll
-  for (int b = 0; b < kShortPer; b += 8) {
-    uint32_t mine = 0;
-#pragma unroll
-    for (int j = b; j < b + 8; ++j) mine += (uint32_t)(x[j] >= Tf);
-    uint32_t total;
-    const uint32_t pre = wave_prefix_small<4>(mine, total);
-    uint32_t slot = wave_reserve(&L.cnt, total) + pre;
-#pragma unroll
-    for (int j = b; j < b + 8; ++j) {
-      const bool kp = x[j] >= Tf;
-      if (kp)
-        L.elems[slot < (uint32_t)kFinalLds ? slot : (uint32_t)kFinalLds] =
-            make_uint2(__float_as_uint(x[j]), pbase + (uint32_t)(4096 * (j >> 2) + (j & 3)));
-      slot += kp;
-    }
+  for (int j = 0; j < kShortPer; ++j) {
+    const bool kp = x[j] >= tf;
+    if (kp)
+      L.elems[slot < (uint32_t)kFinalLds ? slot : (uint32_t)kFinalLds] =
+          make_uint2(__float_as_uint(x[j]), pbase + (uint32_t)(4096 * (j >> 2) + (j & 3)));
+    slot += kp;
   }
   const uint32_t wm = wave_max32(ordered_key(mx));
-  if (lane == 0) L.wmax[wave] = wm;
+  const uint32_t wn = ~wave_max32(~ordered_key(mn));
+  if (lane == 0) {
+    L.wmax[wave] = wm;
+    L.wmin[wave] = wn;
+  }
   __syncthreads();
   const uint32_t count = L.cnt;
   const uint32_t kmax = wave_max32(lane < kTF / 64 ? L.wmax[lane] : 0u);
+  const uint32_t kmin = ~wave_max32(lane < kTF / 64 ? ~L.wmin[lane] : 0u);
   const Emit emit{out, slots, L.tbl};
   if (count >= (uint32_t)k && count <= (uint32_t)kFinalLds)
     select_top(
         L.f, count, k, emit,
         [&](int64_t i) { return composite(ordered_key(__uint_as_float(L.elems[i].x)), L.elems[i].y); }, true,
-        (uint64_t)T << 32, ((uint64_t)kmax << 32) | 0xffffffffull);
+        (uint64_t)(T > kmin ? T : kmin) << 32, ((uint64_t)kmax << 32) | 0xffffffffull);
   else  // the sample missed: select over the whole row
     select_top(L.f, n, k, emit, [&](int64_t i) { return composite(ordered_key(s[i]), (uint32_t)i); });
 }
