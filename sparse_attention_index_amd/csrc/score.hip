@@ -262,6 +262,34 @@ __global__ __launch_bounds__(kThreads)
     // with the group's first row, lanes >= 32 with its second.
     constexpr int G = RPW < 2 ? RPW : 2;
     constexpr int NG = RPW / G;
+    // One row per wave: each half page leaves a partial head sum per lane
+    // (16 heads); the two halves are completed together by one lane-half
+    // swap, after which lane l holds the score of key l of the page. The
+    // additions are the same, in the same order, as for a half at a time.
+    auto head_sum = [&](const f32x16& acc) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) sum = __builtin_fmaf(wv[i2], relu(acc[i2]), sum);
+      return sum;
+    };
+    auto finish_page = [&](float p0, float p1, float ksl, int i) {
+      if (i < 0) return;
+      const float v = halves_sum_pair(p0, p1) * ksl;
+      if constexpr (FILT) {
+        const int pos = (jx + i * stride) * kBlock + lane;
+        const bool keep = wr0 < nr && pos <= pos0 + wr0 && v >= thr_w[0];
+        const uint64_t m = __ballot(keep);
+        if (m) {
+          const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          const uint32_t slot = fcnt[0] + rank;
+          if (keep && slot < fsub)
+            a.cand[(row0 + wr0) * (size_t)a.cap + (size_t)jx * fsub + slot] = make_uint2(ordered_key(v), (uint32_t)pos);
+          fcnt[0] += (uint32_t)__popcll(m);
+        }
+      } else {
+        sc_s[i % (LAG + 1)][wr0][lane] = v;
+      }
+    };
     // head-weighted ReLU sum of one unit (keys 32h .. 32h+31 of the i-th
     // page, rows gi*G ..) into the LDS score buffer
     auto epilogue = [&](const f32x16(&acc)[G], float ks, int i, int h, int gi) {
@@ -392,6 +420,7 @@ __global__ __launch_bounds__(kThreads)
 #pragma unroll
     for (int r = 0; r < G; ++r) acc[1][r] = f32x16{};
     float ks_prev = 0.f;
+    float p_half0 = 0.f;  // one row per wave: the current page's first-half partial sums
     for (int i = 0; i < n_my; ++i) {
       if ((i & 7) == 0) set_progress_priority(i, n_my);
       wait_page(i);
@@ -412,6 +441,7 @@ __global__ __launch_bounds__(kThreads)
       if constexpr (NG == 1) load_b(kbuf, ksb, 1, B[NG == 1 ? 1 : 0], SB[NG == 1 ? 1 : 0]);
       // MXFP4 keys carry their scales inside the dot products (E8M0 per block)
       const float ks[2] = {KF4 ? 1.f : ksb[n], KF4 ? 1.f : ksb[32 + n]};
+      const float ksl = KF4 ? 1.f : ksb[lane];  // one row per wave: the scale of key `lane`
 #pragma unroll
       for (int u = 0; u < 2 * NG; ++u) {  // unit u: half u / NG, group u % NG
         const int h = u / NG, gi = u % NG;
@@ -419,12 +449,18 @@ __global__ __launch_bounds__(kThreads)
           if (u == NG) load_b(kbuf, ksb, 1, B[0], SB[0]);
         }
         mfma_unit(acc[u & 1], B[NG == 1 ? h : 0], SB[NG == 1 ? h : 0], gi);
-        if (u == 0) epilogue(acc[1], ks_prev, i - 1, 1, NG - 1);  // last unit of the previous page
-        else epilogue(acc[(u - 1) & 1], ks[(u - 1) / NG], i, (u - 1) / NG, (u - 1) % NG);
+        if constexpr (G == 1) {
+          if (u == 0) finish_page(p_half0, head_sum(acc[1][0]), ks_prev, i - 1);  // the previous page
+          else p_half0 = head_sum(acc[0][0]);
+        } else {
+          if (u == 0) epilogue(acc[1], ks_prev, i - 1, 1, NG - 1);  // last unit of the previous page
+          else epilogue(acc[(u - 1) & 1], ks[(u - 1) / NG], i, (u - 1) / NG, (u - 1) % NG);
+        }
       }
-      ks_prev = ks[1];
+      ks_prev = G == 1 ? ksl : ks[1];
     }
-    epilogue(acc[1], ks_prev, n_my - 1, 1, NG - 1);
+    if constexpr (G == 1) finish_page(p_half0, head_sum(acc[1][0]), ks_prev, n_my - 1);
+    else epilogue(acc[1], ks_prev, n_my - 1, 1, NG - 1);
     __syncthreads();  // the last scores are in LDS
     if constexpr (role == kFlusher) {
       for (int i = max(0, n_my - LAG); i < n_my; ++i) flush(i);
