@@ -314,19 +314,25 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
     const float sc = scl[tok];
     const float f = a.sm_scale * sc;
     float x[4], p[4];
-    bool over = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = valid ? sacc[i] * f : -INFINITY;
-      over |= x[i] > m_run[i] + kSlack;
-      p[i] = (x[i] == -INFINITY) ? 0.f : __expf(x[i] - m_run[i]);
-      p_s[(4 * g + i) * PP + tok] = (__bf16)(p[i] * sc);
+    for (int i = 0; i < 4; ++i) x[i] = valid ? sacc[i] * f : -INFINITY;
+    // The first tile always sets the reference (it starts at -inf), so it
+    // goes straight to the exchange of tile maxima.
+    bool exchange = true;
+    if (t > 0) {
+      bool over = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        over |= x[i] > m_run[i] + kSlack;
+        p[i] = (x[i] == -INFINITY) ? 0.f : __expf(x[i] - m_run[i]);
+        p_s[(4 * g + i) * PP + tok] = (__bf16)(p[i] * sc);
+      }
+      const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;  // all lanes take part
+      if (lane == 0) flag_s[wave] = wave_over ? 1 : 0;
+      lds_barrier();
+      exchange = *reinterpret_cast<const uint64_t*>(flag_s) != 0;
     }
-    const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;  // all lanes take part
-    if (lane == 0) flag_s[wave] = wave_over ? 1 : 0;
-    lds_barrier();
-    const uint64_t flags = *reinterpret_cast<const uint64_t*>(flag_s);
-    if (flags != 0) {  // every wave reads the same flags: a uniform branch
+    if (exchange) {  // every wave reads the same flags: a uniform branch
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float mx = row_max16(x[i]);
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
   // Row sums: every lane holds the part of its own tokens.
 #pragma unroll
   for (int i = 0; i < 4; ++i) l_run[i] = row_sum16(l_run[i]);
-  __syncthreads();
+  // mx_s is free: its last reads in the loop were followed by a barrier
   if (n == 0)
 #pragma unroll
     for (int i = 0; i < 4; ++i) mx_s[wave][4 * g + i] = l_run[i];
@@ -401,16 +407,17 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
         a.lse[(size_t)row * kMlaHeads + h] = l_run[i] > 0.f ? m_run[i] + __logf(l_run[i]) : -INFINITY;
     }
   } else {
+    // partials are read once, by the merge: streamed stores (nontemporal)
     const size_t base = (size_t)row * part.splits + split;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * g + i;
       float* orow = part.o + (base * kMlaHeads + h) * kV;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) orow[64 * wave + 16 * j + n] = o[j][i];
+      for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(o[j][i], &orow[64 * wave + 16 * j + n]);
       if (wave == 0 && n == 0) {
-        part.ml[(base * kMlaHeads + h) * 2 + 0] = m_run[i];
-        part.ml[(base * kMlaHeads + h) * 2 + 1] = l_run[i];
+        __builtin_nontemporal_store(m_run[i], &part.ml[(base * kMlaHeads + h) * 2 + 0]);
+        __builtin_nontemporal_store(l_run[i], &part.ml[(base * kMlaHeads + h) * 2 + 1]);
       }
     }
   }
