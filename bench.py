@@ -48,11 +48,15 @@ FILTER_MIN_CTX = 40960
 SHORT_TOPK_MAX = 40960
 
 
-def sample_kernels(rows, R, mxfp4):
+def _b(x):
+    return str(bool(x)).lower()
+
+
+def sample_kernels(rows, R, mxfp4, q_fp8=False):
     """The sampling pass's two kernels as profiles name them: 128 sampled pages per row up to 32
     rows, 64 beyond; waves take several rows past 8 rows per request (filter.hip)."""
     nsp = 128 if rows <= 32 else 64
-    return [f"sample_score_kernel<{str(mxfp4).lower()},{nsp},2,{str(R > 8).lower()}>", "sample_select_kernel"]
+    return [f"sample_score_kernel<{_b(mxfp4)},{nsp},2,{_b(R > 8)},{_b(q_fp8)}>", "sample_select_kernel"]
 
 
 def score_rpw(R, q_fp8=False):
@@ -250,6 +254,7 @@ def run_decode(args, torch, dsa, traffic, cfg):
     k = 2048
     rows = B * R
     kfmt = cfg.get("key_format", "fp8")
+    q_fp8 = bool(cfg.get("fp8_query", False))  # E4M3 index queries with row scales
     step_bytes = traffic.decode_step_bytes(lens, R, k, kfmt)
     filtered = max(lens) > FILTER_MIN_CTX
     set_bytes = sum(lens) * (traffic.key_bytes(kfmt) + traffic.LAT_ROW_BYTES)
@@ -269,7 +274,8 @@ def run_decode(args, torch, dsa, traffic, cfg):
 
     def step(i):
         c = cases[i]
-        dsa.dsa_decode(batches[i], caches[i], c.q_idx, c.w, c.q_mla, k, c.sm_scale, out, lse, idx, ws)
+        dsa.dsa_decode(batches[i], caches[i], c.q_idx, c.w, c.q_mla, k, c.sm_scale, out, lse, idx, ws,
+                       q_scale=c.q_idx_scale)
 
     for i in range(args.warmup):
         step(i % nsets)
@@ -316,7 +322,7 @@ def run_decode(args, torch, dsa, traffic, cfg):
 
     def score(i):
         j = i % nsets
-        dsa.dsa_index_score(batches[j], caches[j], cases[j].q_idx, cases[j].w, scores)
+        dsa.dsa_index_score(batches[j], caches[j], cases[j].q_idx, cases[j].w, scores, q_scale=cases[j].q_idx_scale)
 
     def topk(i):
         dsa.dsa_topk(scores, row_len[i % nsets], k, idx, tk_ws)
@@ -333,15 +339,18 @@ def run_decode(args, torch, dsa, traffic, cfg):
 
         def f_thr(i):
             j = i % nsets
-            dsa.dsa_filter_threshold(batches[j], caches[j], cases[j].q_idx, cases[j].w, k, wss[j])
+            dsa.dsa_filter_threshold(batches[j], caches[j], cases[j].q_idx, cases[j].w, k, wss[j],
+                                     q_scale=cases[j].q_idx_scale)
 
         def f_score(i):
             j = i % nsets
-            dsa.dsa_filter_score(batches[j], caches[j], cases[j].q_idx, cases[j].w, k, wss[j])
+            dsa.dsa_filter_score(batches[j], caches[j], cases[j].q_idx, cases[j].w, k, wss[j],
+                                 q_scale=cases[j].q_idx_scale)
 
         def f_select(i):
             j = i % nsets
-            dsa.dsa_filter_select(batches[j], caches[j], cases[j].q_idx, cases[j].w, k, idx, wss[j])
+            dsa.dsa_filter_select(batches[j], caches[j], cases[j].q_idx, cases[j].w, k, idx, wss[j],
+                                  q_scale=cases[j].q_idx_scale)
 
         stage_us = stage_times(torch, [("threshold", f_thr), ("score", f_score), ("select", f_select),
                                        ("attend", attend)], n_stage)
@@ -349,17 +358,17 @@ def run_decode(args, torch, dsa, traffic, cfg):
         # ---- dominant kernel: the filtered scorer, one kernel per dsa_filter_score call,
         # timed inside the stage sequence above
         score_us = stage_us["score"]
-        dom_bytes = traffic.filter_scorer_bytes(lens, R, kfmt)
-        dom_kernel = f"score_kernel<{score_rpw(R)},false,{str(kfmt == 'mxfp4').lower()},true>"
-        step_kernels = sample_kernels(len(lens) * R, R, kfmt == "mxfp4") + [
-            dom_kernel, "candidate_select_kernel<%s>" % str(kfmt == "mxfp4").lower()]
+        dom_bytes = traffic.filter_scorer_bytes(lens, R, kfmt, q_fp8)
+        dom_kernel = f"score_kernel<{score_rpw(R)},{_b(q_fp8)},{_b(kfmt == 'mxfp4')},true>"
+        step_kernels = sample_kernels(len(lens) * R, R, kfmt == "mxfp4", q_fp8) + [
+            dom_kernel, f"candidate_select_kernel<{_b(kfmt == 'mxfp4')},{_b(q_fp8)}>"]
     else:
         stage_us = stored
         # ---- dominant kernel: the indexer scorer (its share of the step grows with context),
         # one kernel per dsa_index_score call, timed inside the stage sequence above
         score_us = stage_us["score"]
-        dom_bytes = traffic.scorer_bytes(lens, R, kfmt)
-        dom_kernel = f"score_kernel<{score_rpw(R)},false,{str(kfmt == 'mxfp4').lower()},false>"
+        dom_bytes = traffic.scorer_bytes(lens, R, kfmt, q_fp8)
+        dom_kernel = f"score_kernel<{score_rpw(R, q_fp8)},{_b(q_fp8)},{_b(kfmt == 'mxfp4')},false>"
         step_kernels = [dom_kernel, "topk_short_kernel<true>" if max_ctx <= SHORT_TOPK_MAX else "topk_slice_kernel<true>"]
         if max_ctx > SHORT_TOPK_MAX:
             step_kernels.append("topk_final_kernel<true>")
@@ -379,7 +388,7 @@ def run_decode(args, torch, dsa, traffic, cfg):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if q_fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": args.workload,
@@ -388,7 +397,8 @@ def run_decode(args, torch, dsa, traffic, cfg):
             "context": lens[0] if len(set(lens)) == 1 else [min(lens), max(lens)],
             "topk": k,
             "indexer": ("32h x 128d, MXFP4 keys (E2M1 + E8M0 per 32 dims, 68 B)" if kfmt == "mxfp4"
-                        else "32h x 128d, E4M3 keys + fp32 scale"),
+                        else "32h x 128d, E4M3 keys + fp32 scale")
+            + (", E4M3 queries + fp32 row scale" if q_fp8 else ", bf16 queries"),
             "mla": "16h x 576 latent (E4M3 + fp32 scale) -> 512",
             "input_sets_rotated": nsets,
             "launch": "eager" if graph is None else "hip graph",
@@ -599,7 +609,7 @@ def run_dcp(args, torch, dsa, traffic):
 
     def score(i):
         j = i % nsets
-        dsa.dsa_index_score(batches[j], caches[j], cases[j].q_idx, cases[j].w, scores)
+        dsa.dsa_index_score(batches[j], caches[j], cases[j].q_idx, cases[j].w, scores, q_scale=cases[j].q_idx_scale)
 
     def merge(i):
         dsa.dsa_dcp_topk(scores, row_len[i % nsets], k, W, C, idx, resend, tws)

@@ -241,12 +241,17 @@ int32_t dsa_sparse_mla_decode_noalloc(const dsa_batch* batch, const dsa_cache* c
                                       void* out, float* lse, void* stream);
 
 /*
- * The whole decode step: Score (bf16 queries) -> Select (top-k) -> Attend, as
- * one call on one stream. The pages' problem statement: for every query row
- * the indexer scores one FP8 key per earlier token, the top k are kept, and
- * MLA runs over only those rows ("TokenSpeed Kimi K3.1", section
- * "Integrating sparse attention with the K3 stack", steps 2-4).
- *   q_idx    bf16 [rows][32][128], w bf16 [rows][32]  (as dsa_index_score)
+ * The whole decode step: Score -> Select (top-k) -> Attend, as one call on
+ * one stream. The pages' problem statement: for every query row the indexer
+ * scores one FP8 key per earlier token, the top k are kept, and MLA runs
+ * over only those rows ("TokenSpeed Kimi K3.1", section "Integrating sparse
+ * attention with the K3 stack", steps 2-4).
+ *   q_idx, q_dtype, q_scale, w: the indexer query and head weights, as
+ *            dsa_index_score takes them: bf16 [rows][32][128] (q_scale
+ *            NULL), or E4M3 codes with a row scale each (DSA_Q_FP8: the
+ *            FP8 index queries of "TokenSpeed Kimi K3.1", section "Reducing
+ *            indexer overhead on AMD MI350X"; one MFMA term per product
+ *            instead of the bf16 split's two); w bf16 [rows][32]
  *   q_mla    bf16 [rows][num_heads][576]              (as dsa_sparse_mla_decode)
  *   out      bf16 [rows][num_heads][512]; lse fp32 [rows][num_heads] or NULL
  *   idx_out  int32 [rows][k] or NULL: receives the selection.
@@ -260,9 +265,10 @@ int32_t dsa_sparse_mla_decode_noalloc(const dsa_batch* batch, const dsa_cache* c
  * the fp32 score rows never go to HBM and back. Either way attention reads
  * the selection's cache rows directly.
  */
-int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                   const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale, void* out,
-                   float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                   const float* q_scale, const void* w, const void* q_mla, int32_t num_heads, int32_t k,
+                   float softmax_scale, void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                   void* stream);
 
 /*
  * dsa_decode with scores filtered inside the scorer against a per-row
@@ -285,10 +291,10 @@ int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q
  * DSA_ERR_UNSUPPORTED if a request would need more than 1,024 scoring
  * workgroups (contexts beyond about 64M tokens).
  */
-int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                               const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale,
-                               const float* threshold, void* out, float* lse, int32_t* idx_out, void* ws,
-                               size_t ws_bytes, void* stream);
+int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                               const float* q_scale, const void* w, const void* q_mla, int32_t num_heads, int32_t k,
+                               float softmax_scale, const float* threshold, void* out, float* lse, int32_t* idx_out,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /*
  * The filtered path's three stages, one call each, on one stream and one
@@ -311,16 +317,18 @@ int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, c
  *       each row (the selection of dsa_topk, padding -1 included); a row its
  *       candidates cannot decide is scored again in full and selected over
  *       all of it.
- * q_idx and w are dsa_index_score's bf16 query and head weights. Returns
+ * q_idx, q_dtype, q_scale and w are dsa_decode's (bf16 or E4M3 queries). Returns
  * DSA_ERR_UNSUPPORTED if a request would need more than 1,024 scoring
  * workgroups (contexts beyond about 64M tokens).
  */
-int32_t dsa_filter_threshold(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                             int32_t k, const float* threshold, void* ws, size_t ws_bytes, void* stream);
-int32_t dsa_filter_score(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                         int32_t k, void* ws, size_t ws_bytes, void* stream);
-int32_t dsa_filter_select(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                          int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+int32_t dsa_filter_threshold(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                             const float* q_scale, const void* w, int32_t k, const float* threshold, void* ws,
+                             size_t ws_bytes, void* stream);
+int32_t dsa_filter_score(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                         const float* q_scale, const void* w, int32_t k, void* ws, size_t ws_bytes, void* stream);
+int32_t dsa_filter_select(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                          const float* q_scale, const void* w, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /*
  * Decode context parallelism, simulated on one device. Under DCP, token p of

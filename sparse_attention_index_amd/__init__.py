@@ -194,16 +194,21 @@ def dsa_index_key_write(batch: Batch, k, ln_weight, ln_bias, key_fp8, key_scale,
     _check(st, "dsa_index_key_write")
 
 
-def dsa_index_score(batch: Batch, cache: Cache, q, w, scores, q_scale=None, stream=None):
-    """scores[row, s] for every visible token s (fp32 [rows, ld])."""
-    q_dtype = DSA_Q_FP8 if q_scale is not None else DSA_Q_BF16
-    rows = batch.rows
+def _index_query(q, q_scale, w, rows, name="q"):
+    """The indexer query's format: bf16, or E4M3 codes with fp32 row scales."""
     if q_scale is None:
-        _need(q, "q", _BF16, rows * 32 * 128)
+        _need(q, name, _BF16, rows * 32 * 128)
     else:
-        _need(q, "q", _CODES, rows * 32 * 128)
+        _need(q, name, _CODES, rows * 32 * 128)
         _need(q_scale, "q_scale", _F32, rows)
     _need(w, "w", _BF16, rows * 32)
+    return DSA_Q_FP8 if q_scale is not None else DSA_Q_BF16
+
+
+def dsa_index_score(batch: Batch, cache: Cache, q, w, scores, q_scale=None, stream=None):
+    """scores[row, s] for every visible token s (fp32 [rows, ld])."""
+    rows = batch.rows
+    q_dtype = _index_query(q, q_scale, w, rows)
     _check_scores(scores, rows, batch.max_ctx)
     st = load().dsa_index_score(
         ctypes.byref(batch.c), ctypes.byref(cache.c), _ptr(q), q_dtype, _ptr(q_scale), _ptr(w),
@@ -296,13 +301,13 @@ def dsa_sparse_mla_prefill(batch, cache, q, idx, softmax_scale, out, lse=None, w
 
 
 def dsa_decode(batch, cache, q_idx, w, q_mla, k, softmax_scale, out, lse=None, idx_out=None, ws=None,
-               stream=None, threshold=None):
+               stream=None, threshold=None, q_scale=None):
     """The whole decode step (score -> select -> attend). With `threshold`
     (fp32 [rows] on the device) the rows' candidate thresholds are the
-    caller's (dsa_decode_thresholded) instead of sampled; results are the same."""
+    caller's (dsa_decode_thresholded) instead of sampled; results are the same.
+    With `q_scale` (fp32 [rows]) q_idx holds E4M3 codes, else bf16 values."""
     rows = batch.rows
-    _need(q_idx, "q_idx", _BF16, rows * 32 * 128)
-    _need(w, "w", _BF16, rows * 32)
+    q_dtype = _index_query(q_idx, q_scale, w, rows, "q_idx")
     _need(q_mla, "q_mla", _BF16)
     if q_mla.dim() != 3 or q_mla.shape[0] != rows or q_mla.shape[2] != 576:
         raise ValueError(f"q_mla must be bf16 [{rows}, heads, 576]")
@@ -314,8 +319,8 @@ def dsa_decode(batch, cache, q_idx, w, q_mla, k, softmax_scale, out, lse=None, i
     if ws is not None:
         _need(ws, "ws", (torch.uint8,))
     lib = load()
-    head = (ctypes.byref(batch.c), ctypes.byref(cache.c), _ptr(q_idx), _ptr(w), _ptr(q_mla), int(q_mla.shape[1]),
-            int(k), float(softmax_scale))
+    head = (ctypes.byref(batch.c), ctypes.byref(cache.c), _ptr(q_idx), q_dtype, _ptr(q_scale), _ptr(w), _ptr(q_mla),
+            int(q_mla.shape[1]), int(k), float(softmax_scale))
     tail = (_ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), int(ws.numel()) if ws is not None else 0, _stream(stream))
     if threshold is None:
         _check(lib.dsa_decode(*head, *tail), "dsa_decode")
@@ -324,33 +329,31 @@ def dsa_decode(batch, cache, q_idx, w, q_mla, k, softmax_scale, out, lse=None, i
         _check(lib.dsa_decode_thresholded(*head, _ptr(threshold), *tail), "dsa_decode_thresholded")
 
 
-def _filter_head(batch, cache, q_idx, w, k, ws):
-    rows = batch.rows
-    _need(q_idx, "q_idx", _BF16, rows * 32 * 128)
-    _need(w, "w", _BF16, rows * 32)
+def _filter_head(batch, cache, q_idx, w, k, ws, q_scale):
+    q_dtype = _index_query(q_idx, q_scale, w, batch.rows, "q_idx")
     _need(ws, "ws", (torch.uint8,))
-    return (ctypes.byref(batch.c), ctypes.byref(cache.c), _ptr(q_idx), _ptr(w), int(k))
+    return (ctypes.byref(batch.c), ctypes.byref(cache.c), _ptr(q_idx), q_dtype, _ptr(q_scale), _ptr(w), int(k))
 
 
-def dsa_filter_threshold(batch, cache, q_idx, w, k, ws, threshold=None, stream=None):
+def dsa_filter_threshold(batch, cache, q_idx, w, k, ws, threshold=None, stream=None, q_scale=None):
     """Filtered path, stage 1: each row's candidate threshold (sampled, or
     `threshold`, fp32 [rows] on the device) into `ws` (dsa_decode's workspace)."""
-    head = _filter_head(batch, cache, q_idx, w, k, ws)
+    head = _filter_head(batch, cache, q_idx, w, k, ws, q_scale)
     if threshold is not None:
         _need(threshold, "threshold", _F32, batch.rows)
     _check(load().dsa_filter_threshold(*head, _ptr(threshold), _ptr(ws), int(ws.numel()), _stream(stream)),
            "dsa_filter_threshold")
 
 
-def dsa_filter_score(batch, cache, q_idx, w, k, ws, stream=None):
+def dsa_filter_score(batch, cache, q_idx, w, k, ws, stream=None, q_scale=None):
     """Filtered path, stage 2: the scores at or above each row's threshold, kept in `ws`."""
-    head = _filter_head(batch, cache, q_idx, w, k, ws)
+    head = _filter_head(batch, cache, q_idx, w, k, ws, q_scale)
     _check(load().dsa_filter_score(*head, _ptr(ws), int(ws.numel()), _stream(stream)), "dsa_filter_score")
 
 
-def dsa_filter_select(batch, cache, q_idx, w, k, idx, ws, stream=None):
+def dsa_filter_select(batch, cache, q_idx, w, k, idx, ws, stream=None, q_scale=None):
     """Filtered path, stage 3: the exact top-k of every row into idx (int32 [rows, k])."""
-    head = _filter_head(batch, cache, q_idx, w, k, ws)
+    head = _filter_head(batch, cache, q_idx, w, k, ws, q_scale)
     _need(idx, "idx", _I32, batch.rows * int(k))
     _check(load().dsa_filter_select(*head, _ptr(idx), _ptr(ws), int(ws.numel()), _stream(stream)),
            "dsa_filter_select")

@@ -97,11 +97,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsa_sparse_mla_decode": (I32, [BP, CP, P, I32, P, I32, F, P, P, P, SZ, P]),
         "dsa_sparse_mla_prefill": (I32, [BP, CP, P, I32, P, I32, F, P, P, P, SZ, P]),
         "dsa_sparse_mla_decode_noalloc": (I32, [BP, CP, P, I32, P, I32, F, P, P, P]),
-        "dsa_decode": (I32, [BP, CP, P, P, P, I32, I32, F, P, P, P, P, SZ, P]),
-        "dsa_decode_thresholded": (I32, [BP, CP, P, P, P, I32, I32, F, P, P, P, P, P, SZ, P]),
-        "dsa_filter_threshold": (I32, [BP, CP, P, P, I32, P, P, SZ, P]),
-        "dsa_filter_score": (I32, [BP, CP, P, P, I32, P, SZ, P]),
-        "dsa_filter_select": (I32, [BP, CP, P, P, I32, P, P, SZ, P]),
+        "dsa_decode": (I32, [BP, CP, P, I32, P, P, P, I32, I32, F, P, P, P, P, SZ, P]),
+        "dsa_decode_thresholded": (I32, [BP, CP, P, I32, P, P, P, I32, I32, F, P, P, P, P, P, SZ, P]),
+        "dsa_filter_threshold": (I32, [BP, CP, P, I32, P, P, I32, P, P, SZ, P]),
+        "dsa_filter_score": (I32, [BP, CP, P, I32, P, P, I32, P, SZ, P]),
+        "dsa_filter_select": (I32, [BP, CP, P, I32, P, P, I32, P, P, SZ, P]),
         "dsa_workspace_size": (SZ, [I32, I32, I64, I32, I32]),
         "dsa_dcp_topk": (I32, [P, I64, P, I32, I32, I32, I32, P, P, P, SZ, P]),
         "dsa_dcp_mla_decode": (I32, [BP, CP, P, I32, P, I32, I32, F, P, P, P, SZ, P]),

@@ -173,13 +173,8 @@ int32_t run_mla(const dsa_batch* batch, const dsa_cache* cache, const void* q, c
 
 extern "C" {
 
-int32_t dsa_index_score(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t q_dtype,
-                        const float* q_scale, const void* w, float* scores, int64_t ld, void* stream) {
-  g_err[0] = 0;
-  int32_t r = check_batch(batch);
-  if (r) return r;
-  if ((r = check_cache(cache, true, false))) return r;
-  if (!q || !w || !scores) return fail(DSA_ERR_INVALID_ARG, "q, w or scores is null");
+// The indexer query's format: bf16 without row scales, or E4M3 codes with them.
+static int32_t check_q_format(int32_t q_dtype, const float* q_scale) {
   if (q_dtype == DSA_Q_BF16) {
     if (q_scale) return fail(DSA_ERR_INVALID_ARG, "q_scale must be null for bf16 queries");
   } else if (q_dtype == DSA_Q_FP8) {
@@ -187,6 +182,17 @@ int32_t dsa_index_score(const dsa_batch* batch, const dsa_cache* cache, const vo
   } else {
     return fail(DSA_ERR_UNSUPPORTED, "q_dtype must be DSA_Q_BF16 or DSA_Q_FP8");
   }
+  return DSA_OK;
+}
+
+int32_t dsa_index_score(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t q_dtype,
+                        const float* q_scale, const void* w, float* scores, int64_t ld, void* stream) {
+  g_err[0] = 0;
+  int32_t r = check_batch(batch);
+  if (r) return r;
+  if ((r = check_cache(cache, true, false))) return r;
+  if (!q || !w || !scores) return fail(DSA_ERR_INVALID_ARG, "q, w or scores is null");
+  if ((r = check_q_format(q_dtype, q_scale))) return r;
   if (ld < batch->max_ctx) return fail(DSA_ERR_INVALID_ARG, "ld < max_ctx");
   if (!aligned(q, 16)) return fail(DSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
   ScoreArgs a;
@@ -297,11 +303,11 @@ static constexpr int kFilterMinCtx = 40960;
 
 // The scorer's arguments for one batch (scores go to the workspace's score
 // rows: the stored path's and the filtered path's fallback).
-static ScoreArgs index_args(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                            const DecodeWs& p) {
+static ScoreArgs index_args(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const float* q_scale,
+                            const void* w, const DecodeWs& p) {
   ScoreArgs a;
   a.q = q_idx;
-  a.q_scale = nullptr;
+  a.q_scale = q_scale;  // set for E4M3 queries
   a.w = static_cast<const uint16_t*>(w);
   set_keys(a, cache);
   a.ctx_len = batch->ctx_len;
@@ -320,17 +326,18 @@ struct Filter {
   bool fits; // no request has more than kMaxFilterWg of them
 };
 
-static Filter filter_of(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                        const DecodeWs& p) {
+static Filter filter_of(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const float* q_scale,
+                        const void* w, const DecodeWs& p) {
   Filter F;
   const int32_t rows = batch->num_requests * batch->rows_per_request;
-  F.f = index_args(batch, cache, q_idx, w, p);
+  F.f = index_args(batch, cache, q_idx, q_scale, w, p);
   F.f.thr = p.thr;
   F.f.cand = p.fcand;
   F.f.cand_count = p.fcount;
   F.f.cap = filter_cap(rows);
   const int B = batch->num_requests;
-  F.grid = filter_grid(B, batch->rows_per_request, batch->max_ctx, cache->key_format == DSA_KEY_MXFP4);
+  F.grid = filter_grid(B, batch->rows_per_request, batch->max_ctx, cache->key_format == DSA_KEY_MXFP4,
+                       q_scale != nullptr);
   F.fits = F.grid - B + 1 <= kMaxFilterWg;
   return F;
 }
@@ -343,7 +350,8 @@ static int32_t filter_threshold(const Filter& F, const DecodeWs& p, int32_t rows
 }
 // 2. score, keeping only the candidates at or above the threshold
 static int32_t filter_score(const Filter& F, const dsa_batch* batch, hipStream_t st) {
-  return hip_status(launch_index_score(F.f, batch->num_requests, batch->max_ctx, false, st), "filter score");
+  return hip_status(launch_index_score(F.f, batch->num_requests, batch->max_ctx, F.f.q_scale != nullptr, st),
+                    "filter score");
 }
 // 3. exact selection from the candidates; a row they cannot decide is
 //    scored again in full (into the score rows) and selected over all of it
@@ -356,12 +364,14 @@ static int32_t filter_select(const Filter& F, const dsa_batch* batch, const Deco
 
 // Checks shared by the decode entry points: batch, cache, indexer query and
 // the workspace; the workspace carved into p.
-static int32_t decode_checks(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                             int32_t k, bool lat, void* ws, size_t ws_bytes, DecodeWs* p) {
+static int32_t decode_checks(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                             const float* q_scale, const void* w, int32_t k, bool lat, void* ws, size_t ws_bytes,
+                             DecodeWs* p) {
   int32_t r = check_batch(batch);
   if (r) return r;
   if ((r = check_cache(cache, true, lat))) return r;
   if (!q_idx || !w) return fail(DSA_ERR_INVALID_ARG, "q_idx or w is null");
+  if ((r = check_q_format(q_dtype, q_scale))) return r;
   if (!aligned(q_idx, 16)) return fail(DSA_ERR_INVALID_ARG, "q_idx must be 16-byte aligned");
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in [1, 2048]");
   const int32_t rows = batch->num_requests * batch->rows_per_request;
@@ -373,15 +383,16 @@ static int32_t decode_checks(const dsa_batch* batch, const dsa_cache* cache, con
 
 // The decode step. thr_in (device, [rows]) set: the filtered path with the
 // caller's thresholds, whatever max_ctx is.
-static int32_t decode_impl(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                           const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale,
+static int32_t decode_impl(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                           const float* q_scale, const void* w, const void* q_mla, int32_t num_heads, int32_t k,
+                           float softmax_scale,
                            const float* thr_in, void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
                            void* stream) {
   g_err[0] = 0;
   DecodeWs p;
   int32_t r = check_mla(num_heads, k, q_mla, idx_out, out, false);
   if (r) return r;
-  if ((r = decode_checks(batch, cache, q_idx, w, k, true, ws, ws_bytes, &p))) return r;
+  if ((r = decode_checks(batch, cache, q_idx, q_dtype, q_scale, w, k, true, ws, ws_bytes, &p))) return r;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t rows = batch->num_requests * batch->rows_per_request;
   int32_t* idx = idx_out ? idx_out : p.idx;
@@ -389,7 +400,7 @@ static int32_t decode_impl(const dsa_batch* batch, const dsa_cache* cache, const
   so.slots = p.slots;
   so.block_table = batch->block_table;
   so.max_blocks = batch->max_blocks;
-  const Filter F = filter_of(batch, cache, q_idx, w, p);
+  const Filter F = filter_of(batch, cache, q_idx, q_scale, w, p);
   if (thr_in && !F.fits)
     return fail(DSA_ERR_UNSUPPORTED, "a request would need more than %d scoring workgroups", kMaxFilterWg);
   if (thr_in || (batch->max_ctx > kFilterMinCtx && F.fits)) {
@@ -397,11 +408,12 @@ static int32_t decode_impl(const dsa_batch* batch, const dsa_cache* cache, const
     if ((r = filter_score(F, batch, st))) return r;
     if ((r = filter_select(F, batch, p, rows, k, idx, so, st))) return r;
   } else {
-    const ScoreArgs a = index_args(batch, cache, q_idx, w, p);
+    const ScoreArgs a = index_args(batch, cache, q_idx, q_scale, w, p);
     const int64_t ld = a.ld;
     const TopkWs tw = topk_ws_carve(p.topk, rows, ld);
     // 1. score
-    if ((r = hip_status(launch_index_score(a, batch->num_requests, batch->max_ctx, false, st), "decode score")))
+    if ((r = hip_status(launch_index_score(a, batch->num_requests, batch->max_ctx, q_dtype == DSA_Q_FP8, st),
+                        "decode score")))
       return r;
     // 2. select (the visible lengths are derived on the way), also writing the
     //    cache rows of the selection so that attention reads no block table
@@ -417,14 +429,14 @@ static int32_t decode_impl(const dsa_batch* batch, const dsa_cache* cache, const
 // The filtered path's stages as entry points of their own (one workspace,
 // the decode step's, carries their state from one call to the next).
 static int32_t filter_stage(int stage, const dsa_batch* batch, const dsa_cache* cache, const void* q_idx,
-                            const void* w, int32_t k, const float* thr_in, int32_t* idx, void* ws, size_t ws_bytes,
-                            void* stream) {
+                            int32_t q_dtype, const float* q_scale, const void* w, int32_t k, const float* thr_in,
+                            int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   DecodeWs p;
-  int32_t r = decode_checks(batch, cache, q_idx, w, k, false, ws, ws_bytes, &p);
+  int32_t r = decode_checks(batch, cache, q_idx, q_dtype, q_scale, w, k, false, ws, ws_bytes, &p);
   if (r) return r;
   if (stage == 3 && !idx) return fail(DSA_ERR_INVALID_ARG, "idx is null");
-  const Filter F = filter_of(batch, cache, q_idx, w, p);
+  const Filter F = filter_of(batch, cache, q_idx, q_scale, w, p);
   if (!F.fits) return fail(DSA_ERR_UNSUPPORTED, "a request would need more than %d scoring workgroups", kMaxFilterWg);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t rows = batch->num_requests * batch->rows_per_request;
@@ -437,38 +449,41 @@ static int32_t filter_stage(int stage, const dsa_batch* batch, const dsa_cache* 
   return filter_select(F, batch, p, rows, k, idx, so, st);
 }
 
-int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                   const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale, void* out, float* lse,
-                   int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
-  return decode_impl(batch, cache, q_idx, w, q_mla, num_heads, k, softmax_scale, nullptr, out, lse, idx_out, ws,
-                     ws_bytes, stream);
+int32_t dsa_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                   const float* q_scale, const void* w, const void* q_mla, int32_t num_heads, int32_t k,
+                   float softmax_scale, void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                   void* stream) {
+  return decode_impl(batch, cache, q_idx, q_dtype, q_scale, w, q_mla, num_heads, k, softmax_scale, nullptr, out, lse,
+                     idx_out, ws, ws_bytes, stream);
 }
 
-int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                               const void* q_mla, int32_t num_heads, int32_t k, float softmax_scale,
-                               const float* threshold, void* out, float* lse, int32_t* idx_out, void* ws,
-                               size_t ws_bytes, void* stream) {
+int32_t dsa_decode_thresholded(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                               const float* q_scale, const void* w, const void* q_mla, int32_t num_heads, int32_t k,
+                               float softmax_scale, const float* threshold, void* out, float* lse, int32_t* idx_out,
+                               void* ws, size_t ws_bytes, void* stream) {
   if (!threshold) {
     g_err[0] = 0;
     return fail(DSA_ERR_INVALID_ARG, "threshold is null");
   }
-  return decode_impl(batch, cache, q_idx, w, q_mla, num_heads, k, softmax_scale, threshold, out, lse, idx_out, ws,
-                     ws_bytes, stream);
+  return decode_impl(batch, cache, q_idx, q_dtype, q_scale, w, q_mla, num_heads, k, softmax_scale, threshold, out,
+                     lse, idx_out, ws, ws_bytes, stream);
 }
 
-int32_t dsa_filter_threshold(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                             int32_t k, const float* threshold, void* ws, size_t ws_bytes, void* stream) {
-  return filter_stage(1, batch, cache, q_idx, w, k, threshold, nullptr, ws, ws_bytes, stream);
+int32_t dsa_filter_threshold(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                             const float* q_scale, const void* w, int32_t k, const float* threshold, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return filter_stage(1, batch, cache, q_idx, q_dtype, q_scale, w, k, threshold, nullptr, ws, ws_bytes, stream);
 }
 
-int32_t dsa_filter_score(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                         int32_t k, void* ws, size_t ws_bytes, void* stream) {
-  return filter_stage(2, batch, cache, q_idx, w, k, nullptr, nullptr, ws, ws_bytes, stream);
+int32_t dsa_filter_score(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                         const float* q_scale, const void* w, int32_t k, void* ws, size_t ws_bytes, void* stream) {
+  return filter_stage(2, batch, cache, q_idx, q_dtype, q_scale, w, k, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
-int32_t dsa_filter_select(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, const void* w,
-                          int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  return filter_stage(3, batch, cache, q_idx, w, k, nullptr, idx, ws, ws_bytes, stream);
+int32_t dsa_filter_select(const dsa_batch* batch, const dsa_cache* cache, const void* q_idx, int32_t q_dtype,
+                          const float* q_scale, const void* w, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return filter_stage(3, batch, cache, q_idx, q_dtype, q_scale, w, k, nullptr, idx, ws, ws_bytes, stream);
 }
 
 size_t dsa_workspace_size(int32_t kind, int32_t rows, int64_t max_ctx, int32_t k, int32_t num_heads) {

@@ -32,18 +32,20 @@ static constexpr int kTblLds = 16384;                // pages of that table (1,0
 
 // ------------------------------------------------------------------ one page, straight from HBM
 
-// A row's query split (the scorer's), and the scaled weights of the 16 heads
+// A row's query operands (the scorer's: a bf16 row split into two E4M3
+// terms, or E4M3 codes as they are), and the scaled weights of the 16 heads
 // each lane reduces, for one wave.
-template <bool KF4>
+template <bool QFP8, bool KF4>
 struct RowQuery {
-  i32x8 A[2][2];
+  i32x8 A[QFP8 ? 1 : 2][2];
   float wv[16];
 };
 
-// The split of a loaded query row (lane n holds head n's values and
-// weight bits, both lane halves).
-template <bool KF4>
-DSA_DEV void finish_row_query(const QueryRaw<false, KF4>& raw, uint32_t wbits, RowQuery<KF4>& q) {
+// The operands of a loaded query row (lane n holds head n's values and
+// weight bits, both lane halves); the head's scale (the power of two of the
+// split, or the row scale of E4M3 codes) goes into its weight.
+template <bool QFP8, bool KF4>
+DSA_DEV void finish_row_query(const QueryRaw<QFP8, KF4>& raw, uint32_t wbits, RowQuery<QFP8, KF4>& q) {
   const int g = (threadIdx.x & 63) >> 5;
   const float head_scale = finish_query(raw, q.A);
   // head h's weight times its scale sits in lanes h and h + 32
@@ -52,12 +54,12 @@ DSA_DEV void finish_row_query(const QueryRaw<false, KF4>& raw, uint32_t wbits, R
   for (int i = 0; i < 16; ++i) q.wv[i] = __shfl(ws, 8 * (i >> 2) + 4 * g + (i & 3));
 }
 
-template <bool KF4>
-DSA_DEV void row_query(const ScoreArgs& a, size_t row, RowQuery<KF4>& q) {
+template <bool QFP8, bool KF4>
+DSA_DEV void row_query(const ScoreArgs& a, size_t row, RowQuery<QFP8, KF4>& q) {
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
-  QueryRaw<false, KF4> raw;
-  fetch_query<false, KF4>(a, row, n, g, raw);
-  finish_row_query<KF4>(raw, a.w[row * kIdxHeads + n], q);
+  QueryRaw<QFP8, KF4> raw;
+  fetch_query<QFP8, KF4>(a, row, n, g, raw);
+  finish_row_query<QFP8, KF4>(raw, a.w[row * kIdxHeads + n], q);
 }
 
 // B operands of the 64 keys of one page (keys 32h + n for lane n of each
@@ -103,13 +105,13 @@ DSA_DEV void load_page(const ScoreArgs& a, int32_t pid, PageKeys<KF4>& p) {
 
 // Scores of keys 32h + n (v[h], in both lane halves): the scorer's MFMAs and
 // head-weighted ReLU reduction.
-template <bool KF4>
-DSA_DEV void score_page(const RowQuery<KF4>& q, const PageKeys<KF4>& p, float (&v)[2]) {
+template <bool QFP8, bool KF4>
+DSA_DEV void score_page(const RowQuery<QFP8, KF4>& q, const PageKeys<KF4>& p, float (&v)[2]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     f32x16 acc = f32x16{};
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < (QFP8 ? 1 : 2); ++t)
 #pragma unroll
       for (int st = 0; st < 2; ++st)
         acc = KF4 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q.A[t][st], p.b[h][st], acc, 0, 4, 0, 127, 0,
@@ -135,7 +137,7 @@ DSA_DEV void score_page(const RowQuery<KF4>& q, const PageKeys<KF4>& p, float (&
 // (each wave splits its row's query once per workgroup). The second takes
 // each row's threshold from its samples (sample_select: a little below the
 // sampled rank that leaves about 1.25k of the row's scores above it).
-template <bool KF4, int NSP, int PPW, bool MULTI>
+template <bool KF4, int NSP, int PPW, bool MULTI, bool QFP8>
 __global__ __launch_bounds__(kSampleThreads) void sample_score_kernel(ScoreArgs a, float* __restrict__ samp) {
   static_assert(NSP <= kSamplePages, "the workspace holds 128 sampled pages per row");
   constexpr int WPQ = NSP / PPW;  // workgroups per request
@@ -146,8 +148,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_score_kernel(ScoreArgs 
   // the query row and head weights of the wave's first row go out first:
   // they depend on nothing, and their latency then overlaps the chain
   // ctx_len -> page ids -> keys
-  QueryRaw<false, KF4> qraw;
-  fetch_query<false, KF4>(a, (size_t)b * R + wave, n, g, qraw);
+  QueryRaw<QFP8, KF4> qraw;
+  fetch_query<QFP8, KF4>(a, (size_t)b * R + wave, n, g, qraw);
   uint32_t wbits = a.w[((size_t)b * R + wave) * kIdxHeads + n];
   // pages every sampled row of the request sees in full: those of its first
   // row, and at least 128 (a row with more than kTakeAll tokens sees them)
@@ -164,13 +166,13 @@ __global__ __launch_bounds__(kSampleThreads) void sample_score_kernel(ScoreArgs 
     const size_t row = (size_t)b * R + r;
     if (L - R + r + 1 <= kTakeAll) return;  // this row keeps every score
     hold_query(qraw);
-    RowQuery<KF4> q;
-    finish_row_query<KF4>(qraw, wbits, q);
+    RowQuery<QFP8, KF4> q;
+    finish_row_query<QFP8, KF4>(qraw, wbits, q);
     float* out = samp + row * kSampleKeys;
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
       float v[2];
-      score_page<KF4>(q, pk[i], v);
+      score_page<QFP8, KF4>(q, pk[i], v);
       if (g == 0) {
         out[(j0 + i) * kBlock + n] = v[0];
         out[(j0 + i) * kBlock + 32 + n] = v[1];
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_score_kernel(ScoreArgs 
   if constexpr (MULTI) {  // more than 8 rows: wave w also takes rows w + 8, w + 16, ...
     for (int r = wave + kSampleThreads / 64; r < R; r += kSampleThreads / 64) {
       const size_t row = (size_t)b * R + r;
-      fetch_query<false, KF4>(a, row, n, g, qraw);
+      fetch_query<QFP8, KF4>(a, row, n, g, qraw);
       wbits = a.w[row * kIdxHeads + n];
       score_row(r);
     }
@@ -243,7 +245,7 @@ static_assert(sizeof(CandLds) <= 160 * 1024, "one selecting workgroup per CU");
 // row's scores to a.scores); G: the scorer's workgroups per row group, split
 // over the B requests as the scorer split them; compact: [rows][a.cap] room
 // for a row's candidates past what LDS holds.
-template <bool KF4>
+template <bool KF4, bool QFP8>
 __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int B, int G, const float* thr,
                                                                const int32_t* __restrict__ row_len, uint2* compact,
                                                                int k, int32_t* __restrict__ idx, SlotOut so) {
@@ -373,14 +375,14 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
     // pages w, w + 16, ...) and select over the whole row
     float* srow = a.scores + (size_t)row * a.ld;
     const int32_t* table = a.block_table + (size_t)(row / R) * a.max_blocks;
-    RowQuery<KF4> q;
-    row_query<KF4>(a, (size_t)row, q);
+    RowQuery<QFP8, KF4> q;
+    row_query<QFP8, KF4>(a, (size_t)row, q);
     const int nl = lane & 31;
     for (int p = wave; p < npages; p += kTF / 64) {
       PageKeys<KF4> pk;
       load_page<KF4>(a, table[p], pk);
       float v[2];
-      score_page<KF4>(q, pk, v);
+      score_page<QFP8, KF4>(q, pk, v);
       if (lane < 32) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -407,44 +409,61 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
 // threshold saves the selection.
 static int sampled_pages(int rows) { return rows > 32 ? 64 : kSamplePages; }
 
-template <bool KF4, int NSP, int PPW, bool MULTI>
+template <bool KF4, int NSP, int PPW, bool MULTI, bool QFP8>
 static void launch_sample_score(const ScoreArgs& a, int rows, float* samp, hipStream_t st) {
   const int B = rows / a.R, waves = MULTI ? kSampleThreads / 64 : a.R;
-  hipLaunchKernelGGL((sample_score_kernel<KF4, NSP, PPW, MULTI>), dim3(B * (NSP / PPW)), dim3(64 * waves), 0, st, a,
-                     samp);
+  hipLaunchKernelGGL((sample_score_kernel<KF4, NSP, PPW, MULTI, QFP8>), dim3(B * (NSP / PPW)), dim3(64 * waves), 0,
+                     st, a, samp);
 }
 
-template <bool KF4>
+template <bool KF4, bool QFP8>
 static void launch_sample_score(const ScoreArgs& a, int rows, float* samp, hipStream_t st) {
   const bool multi = a.R > kSampleThreads / 64;
   if (sampled_pages(rows) == kSamplePages) {
-    if (multi) launch_sample_score<KF4, kSamplePages, 2, true>(a, rows, samp, st);
-    else launch_sample_score<KF4, kSamplePages, 2, false>(a, rows, samp, st);
+    if (multi) launch_sample_score<KF4, kSamplePages, 2, true, QFP8>(a, rows, samp, st);
+    else launch_sample_score<KF4, kSamplePages, 2, false, QFP8>(a, rows, samp, st);
   } else {
-    if (multi) launch_sample_score<KF4, 64, 2, true>(a, rows, samp, st);
-    else launch_sample_score<KF4, 64, 2, false>(a, rows, samp, st);
+    if (multi) launch_sample_score<KF4, 64, 2, true, QFP8>(a, rows, samp, st);
+    else launch_sample_score<KF4, 64, 2, false, QFP8>(a, rows, samp, st);
   }
 }
 
+// E4M3 query codes arrive with their row scales (a.q_scale set); bf16
+// queries without.
 hipError_t launch_sample_threshold(const ScoreArgs& a, int rows, int k, const float* thr_in, float* samp, float* thr,
                                    int32_t* row_len, hipStream_t st) {
   if (!thr_in) {
-    if (a.key_fp4) launch_sample_score<true>(a, rows, samp, st);
-    else launch_sample_score<false>(a, rows, samp, st);
+    const bool q8 = a.q_scale != nullptr;
+    if (a.key_fp4) {
+      if (q8) launch_sample_score<true, true>(a, rows, samp, st);
+      else launch_sample_score<true, false>(a, rows, samp, st);
+    } else {
+      if (q8) launch_sample_score<false, true>(a, rows, samp, st);
+      else launch_sample_score<false, false>(a, rows, samp, st);
+    }
   }
   hipLaunchKernelGGL(sample_select_kernel, dim3(rows), dim3(kSelectThreads), 0, st, a.ctx_len, a.R, samp,
                      sampled_pages(rows) * kBlock, k, thr_in, thr, row_len);
   return hipGetLastError();
 }
 
+template <bool KF4, bool QFP8>
+static void launch_candidate_select(const ScoreArgs& a, int B, int G, const float* thr, const int32_t* row_len,
+                                    uint2* compact, int rows, int k, int32_t* idx, const SlotOut& so, hipStream_t st) {
+  hipLaunchKernelGGL((candidate_select_kernel<KF4, QFP8>), dim3(rows), dim3(kTF), 0, st, a, B, G, thr, row_len,
+                     compact, k, idx, so);
+}
+
 hipError_t launch_candidate_select(const ScoreArgs& a, int B, int G, const float* thr, const int32_t* row_len,
                                    uint2* compact, int rows, int k, int32_t* idx, const SlotOut& so, hipStream_t st) {
-  if (a.key_fp4)
-    hipLaunchKernelGGL(candidate_select_kernel<true>, dim3(rows), dim3(kTF), 0, st, a, B, G, thr, row_len, compact, k,
-                       idx, so);
-  else
-    hipLaunchKernelGGL(candidate_select_kernel<false>, dim3(rows), dim3(kTF), 0, st, a, B, G, thr, row_len, compact,
-                       k, idx, so);
+  const bool q8 = a.q_scale != nullptr;
+  if (a.key_fp4) {
+    if (q8) launch_candidate_select<true, true>(a, B, G, thr, row_len, compact, rows, k, idx, so, st);
+    else launch_candidate_select<true, false>(a, B, G, thr, row_len, compact, rows, k, idx, so, st);
+  } else {
+    if (q8) launch_candidate_select<false, true>(a, B, G, thr, row_len, compact, rows, k, idx, so, st);
+    else launch_candidate_select<false, false>(a, B, G, thr, row_len, compact, rows, k, idx, so, st);
+  }
   return hipGetLastError();
 }
 

@@ -35,15 +35,15 @@ struct ScoreArgs {
 };
 
 // Scores every (row, visible token). B requests, max_ctx bounds ctx_len.
-// With a.cand set (bf16 queries only) the scores are filtered into
-// candidates instead of stored.
+// With a.cand set the scores are filtered into candidates instead of
+// stored. q_fp8: E4M3 query codes with row scales (a.q_scale), else bf16.
 hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st);
 // Most scoring workgroups a request gets in the filtered decode.
 constexpr int kMaxFilterWg = 1024;
 // Workgroups per row group the scorer launches in the filtered decode for B
-// requests of R rows (bf16 queries) of at most max_ctx tokens; a request
-// gets at most grid - B + 1 of them.
-int filter_grid(int B, int R, int max_ctx, bool mxfp4);
+// requests of R rows of at most max_ctx tokens (bf16 or E4M3 queries); a
+// request gets at most grid - B + 1 of them.
+int filter_grid(int B, int R, int max_ctx, bool mxfp4, bool q_fp8);
 
 // Sampling pass of the filtered decode: each row's visible length goes to
 // row_len and its score threshold to thr (-inf for rows of at most 8,192

@@ -82,11 +82,11 @@ constexpr int max_wg_pages() {
   return RPW == 4 ? 4096 : (RPW == 1 ? 1024 : 2048);
 }
 // Waves per SIMD the register allocation aims at: four for the filtered
-// decode with one bf16 row per wave and FP8 keys (128 registers: four
+// decode with one row per wave and FP8 keys (128 registers: four
 // workgroups per CU, measured 3-4% faster than three), two otherwise.
 template <int RPW, bool QFP8, bool KF4, bool FILT>
 constexpr int score_waves_per_eu() {
-  return FILT && RPW == 1 && !QFP8 && !KF4 ? 4 : 2;
+  return FILT && RPW == 1 && !KF4 ? 4 : 2;
 }
 static constexpr int kThreads = 256;                // 4 waves
 static constexpr int kCopies = kKeyBytes / 1024 + 1;  // copy instructions per page (keys + scales)
@@ -535,13 +535,18 @@ template <bool KF4>
 static void launch_format(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hipStream_t st) {
   // Rows per wave: one for decode-sized requests; more when a request brings
   // many FP8 query rows (prefill chunks), so that more rows share each page.
-  if (q_fp8) {
+  if (a.cand) {  // filtered decode
+    if (q_fp8) {
+      if (a.R > 4) launch_variant<2, true, KF4, true>(a, B, max_ctx, st);
+      else launch_variant<1, true, KF4, true>(a, B, max_ctx, st);
+    } else {
+      if (a.R > 4) launch_variant<2, false, KF4, true>(a, B, max_ctx, st);
+      else launch_variant<1, false, KF4, true>(a, B, max_ctx, st);
+    }
+  } else if (q_fp8) {
     if (a.R > 16) launch_variant<4, true, KF4, false>(a, B, max_ctx, st);
     else if (a.R > 4) launch_variant<2, true, KF4, false>(a, B, max_ctx, st);
     else launch_variant<1, true, KF4, false>(a, B, max_ctx, st);
-  } else if (a.cand) {  // filtered decode
-    if (a.R > 4) launch_variant<2, false, KF4, true>(a, B, max_ctx, st);
-    else launch_variant<1, false, KF4, true>(a, B, max_ctx, st);
   } else {
     // up to 8 verification rows read each page once
     if (a.R > 4) launch_variant<2, false, KF4, false>(a, B, max_ctx, st);
@@ -556,13 +561,14 @@ hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8
 }
 
 
-template <bool KF4>
+template <bool KF4, bool QFP8>
 static int filter_grid_fmt(int B, int R, int max_ctx) {
-  return (int)(R > 4 ? grid_x<2, false, KF4, true>(B, R, max_ctx) : grid_x<1, false, KF4, true>(B, R, max_ctx));
+  return (int)(R > 4 ? grid_x<2, QFP8, KF4, true>(B, R, max_ctx) : grid_x<1, QFP8, KF4, true>(B, R, max_ctx));
 }
 
-int filter_grid(int B, int R, int max_ctx, bool mxfp4) {
-  return mxfp4 ? filter_grid_fmt<true>(B, R, max_ctx) : filter_grid_fmt<false>(B, R, max_ctx);
+int filter_grid(int B, int R, int max_ctx, bool mxfp4, bool q_fp8) {
+  if (q_fp8) return mxfp4 ? filter_grid_fmt<true, true>(B, R, max_ctx) : filter_grid_fmt<false, true>(B, R, max_ctx);
+  return mxfp4 ? filter_grid_fmt<true, false>(B, R, max_ctx) : filter_grid_fmt<false, false>(B, R, max_ctx);
 }
 
 }  // namespace dsa

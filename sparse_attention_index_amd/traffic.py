@@ -18,6 +18,7 @@ KEY_BYTES_MXFP4 = 68
 LAT_ROW_BYTES = 580
 SCORE_BYTES = 4
 Q_IDX_BYTES = 32 * 128 * 2 + 32 * 2  # bf16 indexer query + bf16 head weights per row
+Q_IDX_BYTES_FP8 = 32 * 128 + 4 + 32 * 2  # E4M3 indexer query + fp32 row scale + bf16 head weights
 Q_MLA_BYTES = 16 * 576 * 2
 OUT_BYTES = 16 * 512 * 2 + 16 * 4
 
@@ -31,16 +32,20 @@ def key_bytes(key_format="fp8"):
     return KEY_BYTES_MXFP4 if key_format == "mxfp4" else KEY_BYTES
 
 
-def scorer_bytes(ctx_lens, R, key_format="fp8"):
+def q_idx_bytes(q_fp8=False):
+    return Q_IDX_BYTES_FP8 if q_fp8 else Q_IDX_BYTES
+
+
+def scorer_bytes(ctx_lens, R, key_format="fp8", q_fp8=False):
     vis = visible(ctx_lens, R)
-    return sum(ctx_lens) * key_bytes(key_format) + SCORE_BYTES * sum(vis) + len(vis) * Q_IDX_BYTES
+    return sum(ctx_lens) * key_bytes(key_format) + SCORE_BYTES * sum(vis) + len(vis) * q_idx_bytes(q_fp8)
 
 
-def filter_scorer_bytes(ctx_lens, R, key_format="fp8"):
+def filter_scorer_bytes(ctx_lens, R, key_format="fp8", q_fp8=False):
     """The filtered scorer: keys once per request, the rows' queries and head
     weights; the (score, position) candidates it keeps (a few thousand per
     row, under 0.1% of the keys' bytes at 1M tokens) are not counted."""
-    return sum(ctx_lens) * key_bytes(key_format) + len(visible(ctx_lens, R)) * Q_IDX_BYTES
+    return sum(ctx_lens) * key_bytes(key_format) + len(visible(ctx_lens, R)) * q_idx_bytes(q_fp8)
 
 
 def topk_bytes(ctx_lens, R, k):

@@ -60,5 +60,5 @@ def gpu_decode(case, k=None, threshold=None):
     lse = torch.full((rows, 16), float("nan"), dtype=torch.float32, device="cuda")
     idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
     dsa.dsa_decode(dsa.Batch.of(case), dsa.Cache.of(case), case.q_idx, case.w, case.q_mla, k, case.sm_scale,
-                   out, lse, idx, ws, threshold=threshold)
+                   out, lse, idx, ws, threshold=threshold, q_scale=case.q_idx_scale)
     return out, lse, idx

@@ -107,10 +107,20 @@ def test_argument_errors_are_reported_before_any_launch(lib):
     assert kw(ctypes.byref(b), P, P, P, 1e-6, P, P, 0, None) == _lib.DSA_ERR_INVALID_ARG
     assert kw(ctypes.byref(b), P + 2, P, P, 1e-6, P, P, 1, None) == _lib.DSA_ERR_INVALID_ARG
     # fused decode
-    assert lib.dsa_decode(ctypes.byref(b), ctypes.byref(c), P, P, P, 16, 2048, 0.1, P, None, None, P, 16, None) == \
-        _lib.DSA_ERR_WORKSPACE
-    assert lib.dsa_decode(ctypes.byref(b), ctypes.byref(_cache(lat_fp8=0)), P, P, P, 16, 2048, 0.1, P, None, None, P,
+    BF, F8 = _lib.DSA_Q_BF16, _lib.DSA_Q_FP8
+    assert lib.dsa_decode(ctypes.byref(b), ctypes.byref(c), P, BF, None, P, P, 16, 2048, 0.1, P, None, None, P, 16,
+                          None) == _lib.DSA_ERR_WORKSPACE
+    assert lib.dsa_decode(ctypes.byref(b), ctypes.byref(_cache(lat_fp8=0)), P, BF, None, P, P, 16, 2048, 0.1, P, None,
+                          None, P, 1 << 30, None) == _lib.DSA_ERR_INVALID_ARG
+    # the indexer query's format: FP8 codes need their row scales, bf16 takes none
+    assert lib.dsa_decode(ctypes.byref(b), ctypes.byref(c), P, F8, None, P, P, 16, 2048, 0.1, P, None, None, P,
                           1 << 30, None) == _lib.DSA_ERR_INVALID_ARG
+    assert lib.dsa_decode(ctypes.byref(b), ctypes.byref(c), P, BF, P, P, P, 16, 2048, 0.1, P, None, None, P,
+                          1 << 30, None) == _lib.DSA_ERR_INVALID_ARG
+    assert lib.dsa_decode(ctypes.byref(b), ctypes.byref(c), P, 7, None, P, P, 16, 2048, 0.1, P, None, None, P,
+                          1 << 30, None) == _lib.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_filter_score(ctypes.byref(b), ctypes.byref(c), P, F8, None, P, 2048, P, 1 << 30, None) == \
+        _lib.DSA_ERR_INVALID_ARG
 
 
 def test_binding_refuses_host_tensors():

@@ -25,15 +25,18 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 def _step_kernels(cfg, filtered):
     R = cfg["R"]
     fmt = str(cfg.get("key_format", "fp8") == "mxfp4").lower()
+    q8 = bool(cfg.get("fp8_query", False))
+    qf = str(q8).lower()
     if filtered:
-        ks = bench.sample_kernels(len(cfg["lengths"]) * R, R, fmt == "true") + [
-            f"score_kernel<{bench.score_rpw(R)},false,{fmt},true>", f"candidate_select_kernel<{fmt}>"]
+        ks = bench.sample_kernels(len(cfg["lengths"]) * R, R, fmt == "true", q8) + [
+            f"score_kernel<{bench.score_rpw(R)},{qf},{fmt},true>", f"candidate_select_kernel<{fmt},{qf}>"]
     else:
-        ks = [f"score_kernel<{bench.score_rpw(R)},false,{fmt},false>", "topk_short_kernel<true>"]
+        ks = [f"score_kernel<{bench.score_rpw(R, q8)},{qf},{fmt},false>", "topk_short_kernel<true>"]
     return ks + ["sparse_mla_kernel", "mla_combine_kernel"]
 
 
-@pytest.mark.parametrize("workload", ["decode_16x4_32k", "decode_4x4_1m_planted", "decode_4x4_1m_mxfp4"])
+@pytest.mark.parametrize("workload", ["decode_16x4_32k", "decode_4x4_1m_planted", "decode_4x4_1m_mxfp4",
+                                      "decode_4x4_1m_fp8q"])
 def test_step_hbm_fields(workload):
     cfg = case_config(workload)
     kf = cfg.get("key_format", "fp8")
@@ -64,6 +67,8 @@ def test_the_filtered_step_is_charged_no_score_round_trip():
     filt = traffic.decode_step_bytes(lens, R, k, round_trip=False)
     assert full - filt == 8 * sum(traffic.visible(lens, R))
     assert traffic.filter_scorer_bytes(lens, R) == sum(lens) * 132 + 16 * traffic.Q_IDX_BYTES
+    # E4M3 queries: 4 KB of codes and a 4-byte row scale per row instead of 8 KB of bf16
+    assert traffic.filter_scorer_bytes(lens, R, q_fp8=True) == sum(lens) * 132 + 16 * (4096 + 4 + 64)
 
 
 def test_counters_need_the_current_source(monkeypatch, tmp_path):
@@ -85,9 +90,11 @@ def test_counters_need_the_current_source(monkeypatch, tmp_path):
 
 
 def test_sample_kernel_names_follow_the_row_count():
-    assert bench.sample_kernels(16, 4, False) == ["sample_score_kernel<false,128,2,false>", "sample_select_kernel"]
-    assert bench.sample_kernels(64, 4, True) == ["sample_score_kernel<true,64,2,false>", "sample_select_kernel"]
-    assert bench.sample_kernels(10, 10, False)[0] == "sample_score_kernel<false,128,2,true>"
+    assert bench.sample_kernels(16, 4, False) == ["sample_score_kernel<false,128,2,false,false>",
+                                                  "sample_select_kernel"]
+    assert bench.sample_kernels(64, 4, True) == ["sample_score_kernel<true,64,2,false,false>", "sample_select_kernel"]
+    assert bench.sample_kernels(10, 10, False)[0] == "sample_score_kernel<false,128,2,true,false>"
+    assert bench.sample_kernels(16, 4, False, True)[0] == "sample_score_kernel<false,128,2,false,true>"
 
 
 def test_counter_hash_follows_code_not_comments():

@@ -27,7 +27,8 @@ from workloads import case_config, make_case, structure_kwargs
 pytestmark = pytest.mark.gpu
 
 DECODE = ["decode_1x1_8k", "decode_16x4_32k", "decode_16x8_32k", "decode_16x4_ragged_128k_256k",
-          "decode_4x4_1m_planted", "decode_4x4_1m_mxfp4", "decode_4x4_1m_recent", "decode_16x4_256k_1m"]
+          "decode_4x4_1m_planted", "decode_4x4_1m_mxfp4", "decode_4x4_1m_recent", "decode_16x4_256k_1m",
+          "decode_4x4_1m_fp8q"]
 
 
 def _make(name):

@@ -29,7 +29,8 @@ CASES = [
 
 
 def _run(case, batch, cache, ws, out, lse, idx):
-    dsa.dsa_decode(batch, cache, case.q_idx, case.w, case.q_mla, case.topk, case.sm_scale, out, lse, idx, ws)
+    dsa.dsa_decode(batch, cache, case.q_idx, case.w, case.q_mla, case.topk, case.sm_scale, out, lse, idx, ws,
+                   q_scale=case.q_idx_scale)
 
 
 def _check(tag, got, ref):

@@ -46,6 +46,14 @@ FUSED_ONLY = {
     "2x7_filtered": dict(B=2, R=7, lengths=[45000, 70001], seed=115, permute_blocks=True),
     # ten rows per request: the sampling pass's waves take a second row each
     "1x10_filtered": dict(B=1, R=10, lengths=[52000], seed=116, permute_blocks=True),
+    # E4M3 index queries with row scales through the filtered decode: one row
+    # per wave (with a request shorter than k), two rows per wave, two row
+    # groups, and MXFP4 keys
+    "fp8q_3x4_filtered": dict(B=3, R=4, lengths=[45000, 70000, 1900], seed=117, permute_blocks=True,
+                              fp8_query=True),
+    "fp8q_2x6_filtered": dict(B=2, R=6, lengths=[50000, 43000], seed=118, fp8_query=True),
+    "fp8q_1x10_filtered": dict(B=1, R=10, lengths=[52000], seed=119, permute_blocks=True, fp8_query=True),
+    "fp8q_mx_2x4_filtered": dict(B=2, R=4, lengths=[50000, 41500], seed=120, fp8_query=True, key_format="mxfp4"),
 }
 
 
@@ -286,7 +294,9 @@ def test_sparse_mla_skips_invalid_entries(gpu):
 
 
 @pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "3x3_short_perm", "1x8", "2x2_long_perm",
-                                  "5x3_filtered_ragged", "2x7_filtered", "1x10_filtered"])
+                                  "5x3_filtered_ragged", "2x7_filtered", "1x10_filtered", "fp8q_2x7",
+                                  "fp8q_3x4_filtered", "fp8q_2x6_filtered", "fp8q_1x10_filtered",
+                                  "fp8q_mx_2x4_filtered"])
 def test_fused_decode_matches_oracle_and_stages(gpu, name):
     case = _case(name)
     out, lse, idx = gpu_decode(case)
@@ -350,7 +360,7 @@ def _kth_scores(case, k):
 
 
 @pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "1x1_8k", "40x4_many_rows", "2x7_filtered",
-                                  "1x10_filtered"])
+                                  "1x10_filtered", "fp8q_3x4_filtered", "fp8q_2x6_filtered"])
 def test_thresholded_decode_equals_the_staged_path_whatever_the_threshold(gpu, name):
     """The filtered decode with caller-given thresholds against the stored
     path (dsa_index_score -> dsa_topk -> dsa_sparse_mla_decode). Too high a
@@ -389,7 +399,8 @@ def test_thresholded_decode_equals_the_staged_path_whatever_the_threshold(gpu, n
 
 
 @pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "2x4_ragged_perm", "40x4_many_rows",
-                                  "2x7_filtered", "1x10_filtered"])
+                                  "2x7_filtered", "1x10_filtered", "fp8q_3x4_filtered", "fp8q_1x10_filtered",
+                                  "fp8q_mx_2x4_filtered"])
 def test_filter_stage_entry_points_select_the_stored_top_k(gpu, name):
     """dsa_filter_threshold -> dsa_filter_score -> dsa_filter_select, called
     one by one on a workspace that starts with stale bytes, select exactly
@@ -407,9 +418,10 @@ def test_filter_stage_entry_points_select_the_stored_top_k(gpu, name):
         print(f"[filter stages] {name} {label}", flush=True)
         ws.fill_(0xA5)
         idx = torch.full((case.rows, k), -7, dtype=torch.int32, device="cuda")
-        dsa.dsa_filter_threshold(b, c, case.q_idx, case.w, k, ws, threshold=thr)
-        dsa.dsa_filter_score(b, c, case.q_idx, case.w, k, ws)
-        dsa.dsa_filter_select(b, c, case.q_idx, case.w, k, idx, ws)
+        qs = case.q_idx_scale
+        dsa.dsa_filter_threshold(b, c, case.q_idx, case.w, k, ws, threshold=thr, q_scale=qs)
+        dsa.dsa_filter_score(b, c, case.q_idx, case.w, k, ws, q_scale=qs)
+        dsa.dsa_filter_select(b, c, case.q_idx, case.w, k, idx, ws, q_scale=qs)
         got = idx.cpu().numpy()
         for row in range(case.rows):
             assert set(got[row].tolist()) == set(ref[row].tolist()), f"{name} {label} row {row}"
@@ -457,8 +469,9 @@ def test_fused_decode_selection_is_deterministic(gpu):
 
 
 def test_binding_rejects_mismatched_tensors_before_launch(gpu):
-    """The fused decode takes bf16 indexer queries: E4M3 query codes (half the
-    bytes) must be refused by the binding before any kernel reads them."""
+    """Without row scales the fused decode takes bf16 indexer queries: E4M3
+    query codes (half the bytes) passed without q_scale must be refused by
+    the binding before any kernel reads them."""
     case = _case("fp8q_2x7")
     rows, k = case.rows, case.topk
     ws = torch.empty(1, dtype=torch.uint8, device="cuda")

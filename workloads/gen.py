@@ -267,6 +267,11 @@ WORKLOADS = {
     "decode_16x4_256k_1m": dict(B=16, R=4, lengths=None, seed=20260009, permute_blocks=True,
                                 length_range=(262144, 1048576)),
     "prefill_4096_on_128k": dict(B=1, R=4096, lengths=[131072 + 4096], seed=20260005, fp8_query=True),
+    # the 1M workload with E4M3 index queries (row scales), as the pages' decode indexer takes them
+    "decode_4x4_1m_fp8q": dict(B=4, R=4, lengths=[1 << 20] * 4, seed=20260010, plant_frac=0.01, fp8_query=True),
+    # the target shape with E4M3 index queries
+    "decode_16x4_256k_1m_fp8q": dict(B=16, R=4, lengths=None, seed=20260011, permute_blocks=True,
+                                     length_range=(262144, 1048576), fp8_query=True),
 }
 
 
