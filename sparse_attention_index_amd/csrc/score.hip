@@ -276,10 +276,15 @@ __global__ __launch_bounds__(kThreads)
       if (i < 0) return;
       const float v = halves_sum_pair(p0, p1) * ksl;
       if constexpr (FILT) {
-        const int pos = (jx + i * stride) * kBlock + lane;
-        const bool keep = wr0 < nr && pos <= pos0 + wr0 && v >= thr_w[0];
-        const uint64_t m = __ballot(keep);
+        if (wr0 >= nr) return;  // the wave's row is past the group's last (uniform)
+        const int page_pos = (jx + i * stride) * kBlock;
+        const int pos = page_pos + lane;
+        // the keys of the page the row sees: lanes below nv (all but on its last page)
+        const int nv = pos0 + wr0 - page_pos + 1;
+        const uint64_t vis = nv >= 64 ? ~0ull : (nv <= 0 ? 0ull : (1ull << nv) - 1);
+        const uint64_t m = __ballot(v >= thr_w[0]) & vis;
         if (m) {
+          const bool keep = v >= thr_w[0] && lane < nv;  // this lane's bit of m
           const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
           const uint32_t slot = fcnt[0] + rank;
           if (keep && slot < fsub)
