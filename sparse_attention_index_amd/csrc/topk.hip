@@ -290,16 +290,21 @@ __global__ __launch_bounds__(kT) void topk_slice_kernel(const float* __restrict_
   uint32_t skey[kSample / kT];
   sample_load<kT>(s, n, skey);
   wait_vmcnt<0>();
-  float cur[16], nxt[16];
-  if (s0 < s1) load_step(s0, cur);
-  if (s0 + 4096 < s1) load_step(s0 + 4096, nxt);
+  // Two step buffers in turn, loaded unconditionally (past the slice the
+  // descriptor returns zeros that no test reads): with no branch around a
+  // load, the compiler's wait before a step is for that step's loads only,
+  // and the other buffer's stay in flight behind it (a register copy from a
+  // `next` buffer would wait for every load).
+  float bufa[16], bufb[16];
+  load_step(s0, bufa);
+  load_step(s0 + 4096, bufb);
   if (t == 0) L.cnt = 0;
   lds_barrier();  // the counter is cleared before any wave reserves (the loads stay in flight)
   const uint32_t T = sample_select<kT>(skey, n, k, L.hist, L.scan);
   const float Tf = key_threshold_float(T);
 
   float mx = -INFINITY;
-  for (int64_t base = s0; base < s1; base += 4096) {
+  auto step = [&](int64_t base, float (&cur)[16]) {
     const bool whole = base + 4096 <= s1;  // uniform: no position test needed
     const int64_t wbase = base + 1024 * wave + 4 * lane;
     if (VEC && !whole && (s1 & 3)) {
@@ -334,9 +339,12 @@ __global__ __launch_bounds__(kT) void topk_slice_kernel(const float* __restrict_
         ++slot;
       }
     }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
-    if (base + 8192 < s1) load_step(base + 8192, nxt);
+  };
+  for (int64_t base = s0; base < s1; base += 8192) {
+    step(base, bufa);
+    load_step(base + 8192, bufa);
+    if (base + 4096 < s1) step(base + 4096, bufb);  // uniform
+    load_step(base + 12288, bufb);
   }
   const uint32_t wm = wave_max32(ordered_key(mx));
   if (lane == 0) L.wmax[wave] = wm;
