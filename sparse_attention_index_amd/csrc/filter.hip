@@ -131,10 +131,11 @@ DSA_DEV void score_page(const RowQuery<QFP8, KF4>& q, const PageKeys<KF4>& p, fl
 // over the `full` pages that every such row of the request sees in full (at
 // least 128, so the sampled pages are distinct), sampled page j being page
 // floor(j * full / NSP). A workgroup takes PPW sampled pages of one request
-// for all its rows, one wave per row (rows w, w + 8, ... past 8 rows): the
-// waves load the same pages, so all but the first copy come from the CU's
-// cache, and the pages' latency is spread over B * NSP / PPW workgroups
-// (each wave splits its row's query once per workgroup). The second takes
+// for its rows, one wave per row (past 8 rows, workgroup row y of the grid
+// takes rows 8y .. 8y + 7): the waves load the same pages, so all but the
+// first copy come from the CU's cache, and the pages' latency is spread
+// over the workgroups (each wave splits its row's query once per
+// workgroup). The second takes
 // each row's threshold from its samples (sample_select: a little below the
 // sampled rank that leaves about 1.25k of the row's scores above it).
 template <bool KF4, int NSP, int PPW, bool MULTI, bool QFP8>
@@ -143,14 +144,15 @@ __global__ __launch_bounds__(kSampleThreads) void sample_score_kernel(ScoreArgs 
   constexpr int WPQ = NSP / PPW;  // workgroups per request
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, n = lane & 31;
   const int R = a.R, b = blockIdx.x / WPQ, j0 = (blockIdx.x % WPQ) * PPW;
+  const int r = MULTI ? (int)blockIdx.y * (kSampleThreads / 64) + wave : wave;  // this wave's row
+  if (r >= R) return;  // a spare wave of the last row group (the kernel has no barrier)
   const int64_t L = a.ctx_len[b];
   if (L <= kTakeAll) return;  // no row of the request sees more (its last row sees L tokens)
-  // the query row and head weights of the wave's first row go out first:
-  // they depend on nothing, and their latency then overlaps the chain
-  // ctx_len -> page ids -> keys
+  // the query row and head weights go out first: they depend on nothing, and
+  // their latency then overlaps the chain ctx_len -> page ids -> keys
   QueryRaw<QFP8, KF4> qraw;
-  fetch_query<QFP8, KF4>(a, (size_t)b * R + wave, n, g, qraw);
-  uint32_t wbits = a.w[((size_t)b * R + wave) * kIdxHeads + n];
+  fetch_query<QFP8, KF4>(a, (size_t)b * R + r, n, g, qraw);
+  const uint32_t wbits = a.w[((size_t)b * R + r) * kIdxHeads + n];
   // pages every sampled row of the request sees in full: those of its first
   // row, and at least 128 (a row with more than kTakeAll tokens sees them)
   const int64_t first = (L - R + 1) / kBlock;
@@ -162,30 +164,19 @@ __global__ __launch_bounds__(kSampleThreads) void sample_score_kernel(ScoreArgs 
   PageKeys<KF4> pk[PPW];
 #pragma unroll
   for (int i = 0; i < PPW; ++i) load_page<KF4>(a, pid[i], pk[i]);
-  auto score_row = [&](int r) {
-    const size_t row = (size_t)b * R + r;
-    if (L - R + r + 1 <= kTakeAll) return;  // this row keeps every score
-    hold_query(qraw);
-    RowQuery<QFP8, KF4> q;
-    finish_row_query<QFP8, KF4>(qraw, wbits, q);
-    float* out = samp + row * kSampleKeys;
+  const size_t row = (size_t)b * R + r;
+  if (L - R + r + 1 <= kTakeAll) return;  // this row keeps every score
+  hold_query(qraw);
+  RowQuery<QFP8, KF4> q;
+  finish_row_query<QFP8, KF4>(qraw, wbits, q);
+  float* out = samp + row * kSampleKeys;
 #pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-      float v[2];
-      score_page<QFP8, KF4>(q, pk[i], v);
-      if (g == 0) {
-        out[(j0 + i) * kBlock + n] = v[0];
-        out[(j0 + i) * kBlock + 32 + n] = v[1];
-      }
-    }
-  };
-  score_row(wave);
-  if constexpr (MULTI) {  // more than 8 rows: wave w also takes rows w + 8, w + 16, ...
-    for (int r = wave + kSampleThreads / 64; r < R; r += kSampleThreads / 64) {
-      const size_t row = (size_t)b * R + r;
-      fetch_query<QFP8, KF4>(a, row, n, g, qraw);
-      wbits = a.w[row * kIdxHeads + n];
-      score_row(r);
+  for (int i = 0; i < PPW; ++i) {
+    float v[2];
+    score_page<QFP8, KF4>(q, pk[i], v);
+    if (g == 0) {
+      out[(j0 + i) * kBlock + n] = v[0];
+      out[(j0 + i) * kBlock + 32 + n] = v[1];
     }
   }
 }
@@ -349,8 +340,42 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
         copy4_to_lds(table + (base + lane < npages ? base + lane : 0), &L.u.tbl.page[base]);
       }
     }
-    if (in_lds) gather(L.u.elems);
-    else gather(run);
+    // Few regions (a request's rows spread over at most 8 scoring
+    // workgroups, as in a prefill chunk): each region gets a group of waves,
+    // four loads in flight per lane, instead of one wave walking it 64 at a
+    // time.
+    auto gather_grouped = [&](uint2* dst) {
+      const int wpr = (kTF / 64) / nw;  // waves per region (>= 2)
+      const int r = wave / wpr;         // uniform
+      if (r < nw) {
+        const uint32_t o = L.off[r], c = L.off[r + 1] - o;  // c <= sub here
+        const uint32_t step = 64u * (uint32_t)wpr;
+        for (uint32_t j0 = (uint32_t)(wave % wpr) * 64u; j0 < c; j0 += 4u * step) {
+          uint2 x[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {  // clamped: slot 0 of the region exists (c >= 1)
+            const uint32_t j = j0 + q * step + lane;
+            x[q] = regions[(size_t)r * sub + (j < c ? j : 0u)];
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t j = j0 + q * step + lane;
+            if (j < c) {
+              dst[o + j] = x[q];
+              kmax = max(kmax, x[q].x);
+            }
+          }
+        }
+      }
+    };
+    if (2 * nw <= kTF / 64) {
+      if (in_lds) gather_grouped(L.u.elems);
+      else gather_grouped(run);
+    } else if (in_lds) {
+      gather(L.u.elems);
+    } else {
+      gather(run);
+    }
     if (with_tbl) wait_vmcnt<0>();  // the table copies have landed (the barrier below publishes them)
     const uint32_t wm = wave_max32(kmax);
     if (lane == 0) L.wmax[wave] = wm;
@@ -411,9 +436,10 @@ static int sampled_pages(int rows) { return rows > 32 ? 64 : kSamplePages; }
 
 template <bool KF4, int NSP, int PPW, bool MULTI, bool QFP8>
 static void launch_sample_score(const ScoreArgs& a, int rows, float* samp, hipStream_t st) {
-  const int B = rows / a.R, waves = MULTI ? kSampleThreads / 64 : a.R;
-  hipLaunchKernelGGL((sample_score_kernel<KF4, NSP, PPW, MULTI, QFP8>), dim3(B * (NSP / PPW)), dim3(64 * waves), 0,
-                     st, a, samp);
+  constexpr int kWaves = kSampleThreads / 64;
+  const int B = rows / a.R, waves = MULTI ? kWaves : a.R;
+  hipLaunchKernelGGL((sample_score_kernel<KF4, NSP, PPW, MULTI, QFP8>),
+                     dim3(B * (NSP / PPW), MULTI ? (a.R + kWaves - 1) / kWaves : 1), dim3(64 * waves), 0, st, a, samp);
 }
 
 template <bool KF4, bool QFP8>

@@ -325,12 +325,19 @@ __global__ __launch_bounds__(kThreads)
         // lower lane half keeps
         if (i >= 0) {
           const int pos = (jx + i * stride) * kBlock + 32 * h + n;
-          const bool keep = (G == 2 || g == 0) && wr0 + rr < nr && pos <= pos0 + wr0 + rr && v >= thr_w[rr];
+          // the two candidates are read as values, then selected per lane half:
+          // a select of their addresses would put the arrays in scratch
+          float thr_a = thr_w[gi * G], thr_b = thr_w[gi * G + G - 1];
+          asm volatile("" : "+v"(thr_a), "+v"(thr_b));
+          const float thr_rr = (G == 2 && g) ? thr_b : thr_a;
+          const bool keep = (G == 2 || g == 0) && wr0 + rr < nr && pos <= pos0 + wr0 + rr && v >= thr_rr;
           const uint64_t m = __ballot(keep);
           if (m) {
             const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
             const uint32_t rank = g == 0 ? __builtin_amdgcn_mbcnt_lo(mlo, 0u) : __builtin_amdgcn_mbcnt_hi(mhi, 0u);
-            const uint32_t slot = (g == 0 ? fcnt[gi * G] : fcnt[gi * G + G - 1]) + rank;
+            uint32_t f_a = fcnt[gi * G], f_b = fcnt[gi * G + G - 1];
+            asm volatile("" : "+v"(f_a), "+v"(f_b));
+            const uint32_t slot = (g == 0 ? f_a : f_b) + rank;
             if (keep && slot < fsub)
               a.cand[(row0 + wr0 + rr) * (size_t)a.cap + (size_t)jx * fsub + slot] =
                   make_uint2(ordered_key(v), (uint32_t)pos);
@@ -541,8 +548,9 @@ static void launch_format(const ScoreArgs& a, int B, int max_ctx, bool q_fp8, hi
   // Rows per wave: one for decode-sized requests; more when a request brings
   // many FP8 query rows (prefill chunks), so that more rows share each page.
   if (a.cand) {  // filtered decode
-    if (q_fp8) {
-      if (a.R > 4) launch_variant<2, true, KF4, true>(a, B, max_ctx, st);
+    if (q_fp8) {  // up to 16 E4M3 query rows per workgroup, as for stored scores
+      if (a.R > 16) launch_variant<4, true, KF4, true>(a, B, max_ctx, st);
+      else if (a.R > 4) launch_variant<2, true, KF4, true>(a, B, max_ctx, st);
       else launch_variant<1, true, KF4, true>(a, B, max_ctx, st);
     } else {
       if (a.R > 4) launch_variant<2, false, KF4, true>(a, B, max_ctx, st);
@@ -568,6 +576,7 @@ hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8
 
 template <bool KF4, bool QFP8>
 static int filter_grid_fmt(int B, int R, int max_ctx) {
+  if (QFP8 && R > 16) return (int)grid_x<4, QFP8, KF4, true>(B, R, max_ctx);
   return (int)(R > 4 ? grid_x<2, QFP8, KF4, true>(B, R, max_ctx) : grid_x<1, QFP8, KF4, true>(B, R, max_ctx));
 }
 

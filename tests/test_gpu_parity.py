@@ -54,6 +54,12 @@ FUSED_ONLY = {
     "fp8q_2x6_filtered": dict(B=2, R=6, lengths=[50000, 43000], seed=118, fp8_query=True),
     "fp8q_1x10_filtered": dict(B=1, R=10, lengths=[52000], seed=119, permute_blocks=True, fp8_query=True),
     "fp8q_mx_2x4_filtered": dict(B=2, R=4, lengths=[50000, 41500], seed=120, fp8_query=True, key_format="mxfp4"),
+    # many E4M3 rows of one request (a prefill chunk's shape): 16 rows per
+    # scoring workgroup, the sampling pass's row groups in its grid, and (at
+    # 1,024 rows) so few scoring workgroups per row group that the selection
+    # gathers each region with a group of waves
+    "fp8q_1x64_filtered": dict(B=1, R=64, lengths=[50000], seed=121, permute_blocks=True, fp8_query=True),
+    "fp8q_1x1024_filtered": dict(B=1, R=1024, lengths=[46000], seed=122, fp8_query=True),
 }
 
 
@@ -296,7 +302,7 @@ def test_sparse_mla_skips_invalid_entries(gpu):
 @pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "3x3_short_perm", "1x8", "2x2_long_perm",
                                   "5x3_filtered_ragged", "2x7_filtered", "1x10_filtered", "fp8q_2x7",
                                   "fp8q_3x4_filtered", "fp8q_2x6_filtered", "fp8q_1x10_filtered",
-                                  "fp8q_mx_2x4_filtered"])
+                                  "fp8q_mx_2x4_filtered", "fp8q_1x64_filtered"])
 def test_fused_decode_matches_oracle_and_stages(gpu, name):
     case = _case(name)
     out, lse, idx = gpu_decode(case)
@@ -360,7 +366,7 @@ def _kth_scores(case, k):
 
 
 @pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "1x1_8k", "40x4_many_rows", "2x7_filtered",
-                                  "1x10_filtered", "fp8q_3x4_filtered", "fp8q_2x6_filtered"])
+                                  "1x10_filtered", "fp8q_3x4_filtered", "fp8q_2x6_filtered", "fp8q_1x64_filtered"])
 def test_thresholded_decode_equals_the_staged_path_whatever_the_threshold(gpu, name):
     """The filtered decode with caller-given thresholds against the stored
     path (dsa_index_score -> dsa_topk -> dsa_sparse_mla_decode). Too high a
@@ -400,7 +406,7 @@ def test_thresholded_decode_equals_the_staged_path_whatever_the_threshold(gpu, n
 
 @pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "2x4_ragged_perm", "40x4_many_rows",
                                   "2x7_filtered", "1x10_filtered", "fp8q_3x4_filtered", "fp8q_1x10_filtered",
-                                  "fp8q_mx_2x4_filtered"])
+                                  "fp8q_mx_2x4_filtered", "fp8q_1x64_filtered", "fp8q_1x1024_filtered"])
 def test_filter_stage_entry_points_select_the_stored_top_k(gpu, name):
     """dsa_filter_threshold -> dsa_filter_score -> dsa_filter_select, called
     one by one on a workspace that starts with stale bytes, select exactly
