@@ -54,9 +54,11 @@ def _b(x):
 
 def sample_kernels(rows, R, mxfp4, q_fp8=False):
     """The sampling pass's two kernels as profiles name them: 128 sampled pages per row up to 32
-    rows, 64 beyond; waves take several rows past 8 rows per request (filter.hip)."""
+    rows, 64 beyond; past 8 rows per request the many-rows kernel (filter.hip)."""
     nsp = 128 if rows <= 32 else 64
-    return [f"sample_score_kernel<{_b(mxfp4)},{nsp},2,{_b(R > 8)},{_b(q_fp8)}>", "sample_select_kernel"]
+    if R > 8:
+        return [f"sample_score_rows_kernel<{_b(mxfp4)},{nsp},{_b(q_fp8)}>", "sample_select_kernel"]
+    return [f"sample_score_kernel<{_b(mxfp4)},{nsp},2,{_b(q_fp8)}>", "sample_select_kernel"]
 
 
 def score_rpw(R, q_fp8=False):

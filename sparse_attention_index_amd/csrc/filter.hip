@@ -138,14 +138,13 @@ DSA_DEV void score_page(const RowQuery<QFP8, KF4>& q, const PageKeys<KF4>& p, fl
 // workgroup). The second takes
 // each row's threshold from its samples (sample_select: a little below the
 // sampled rank that leaves about 1.25k of the row's scores above it).
-template <bool KF4, int NSP, int PPW, bool MULTI, bool QFP8>
+template <bool KF4, int NSP, int PPW, bool QFP8>
 __global__ __launch_bounds__(kSampleThreads) void sample_score_kernel(ScoreArgs a, float* __restrict__ samp) {
   static_assert(NSP <= kSamplePages, "the workspace holds 128 sampled pages per row");
   constexpr int WPQ = NSP / PPW;  // workgroups per request
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, n = lane & 31;
   const int R = a.R, b = blockIdx.x / WPQ, j0 = (blockIdx.x % WPQ) * PPW;
-  const int r = MULTI ? (int)blockIdx.y * (kSampleThreads / 64) + wave : wave;  // this wave's row
-  if (r >= R) return;  // a spare wave of the last row group (the kernel has no barrier)
+  const int r = wave;  // this wave's row (one workgroup holds all R <= 8 rows)
   const int64_t L = a.ctx_len[b];
   if (L <= kTakeAll) return;  // no row of the request sees more (its last row sees L tokens)
   // the query row and head weights go out first: they depend on nothing, and
@@ -174,6 +173,106 @@ __global__ __launch_bounds__(kSampleThreads) void sample_score_kernel(ScoreArgs 
   for (int i = 0; i < PPW; ++i) {
     float v[2];
     score_page<QFP8, KF4>(q, pk[i], v);
+    if (g == 0) {
+      out[(j0 + i) * kBlock + n] = v[0];
+      out[(j0 + i) * kBlock + 32 + n] = v[1];
+    }
+  }
+}
+
+// Past 8 rows per request: a workgroup stages kRowPages sampled pages of one
+// request in LDS once (each thread copies one 16-byte chunk of each page's
+// keys and one scale word, into the scorer's swizzled layout) and scores
+// them for 8 of the request's rows, one wave per row (workgroup row y of the
+// grid takes rows 8y .. 8y + 7), one page at a time from LDS: a sampled page
+// then crosses from L2 once per 8 rows rather than once per row.
+static constexpr int kRowPages = 8;
+
+template <bool KF4>
+DSA_DEV int staged_chunk_off(int key, int j) {  // LDS offset of 16-byte chunk j of a staged key
+  return KF4 ? key * (kIdxDim / 2) + ((j ^ ((key >> 2) & 3)) << 4) : key * kIdxDim + ((j ^ ((key >> 1) & 7)) << 4);
+}
+
+template <bool KF4>
+DSA_DEV void lds_page(const uint8_t* keys, const uint32_t* ks, PageKeys<KF4>& p) {
+  const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int key = 32 * h + n;
+    if constexpr (KF4) {
+      const uint32_t sw = ks[key];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(keys + staged_chunk_off<true>(key, 2 * g + st));
+        p.b[h][st] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        p.sb[h][st] = (int)((sw >> (8 * (2 * g + st))) & 0xffu);
+      }
+      p.ks[h] = 1.f;
+    } else {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(keys + staged_chunk_off<false>(key, 4 * g + 2 * st));
+        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(keys + staged_chunk_off<false>(key, 4 * g + 2 * st + 1));
+        p.b[h][st] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                           (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+        p.sb[h][st] = 127;
+      }
+      p.ks[h] = __uint_as_float(ks[key]);
+    }
+  }
+}
+
+template <bool KF4, int NSP, bool QFP8>
+__global__ __launch_bounds__(kSampleThreads) void sample_score_rows_kernel(ScoreArgs a, float* __restrict__ samp) {
+  static_assert(NSP <= kSamplePages && NSP % kRowPages == 0, "whole groups of the sampled pages");
+  constexpr int WPQ = NSP / kRowPages;                     // workgroups per request and row group
+  constexpr int KB = KF4 ? kBlock * kIdxDim / 2 : kBlock * kIdxDim;  // key bytes of a page
+  constexpr int NCH = KB / 16;                             // 16-byte chunks of a page (512 or 256)
+  static_assert(NCH <= kSampleThreads, "one chunk per thread and page");
+  __shared__ __attribute__((aligned(16))) uint8_t keys_s[kRowPages][KB];
+  __shared__ uint32_t ks_s[kRowPages][kBlock];  // fp32 key scales, or 4 E8M0 per key
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, n = lane & 31;
+  const int R = a.R, b = blockIdx.x / WPQ, j0 = (blockIdx.x % WPQ) * kRowPages;
+  const int r = (int)blockIdx.y * (kSampleThreads / 64) + wave;  // this wave's row
+  const int64_t L = a.ctx_len[b];
+  if (L <= kTakeAll) return;  // the whole workgroup: no row of the request sees more
+  const bool has_row = r < R;  // the last row group may have spare waves
+  QueryRaw<QFP8, KF4> qraw;
+  fetch_query<QFP8, KF4>(a, (size_t)b * R + (has_row ? r : 0), n, g, qraw);
+  const uint32_t wbits = a.w[((size_t)b * R + (has_row ? r : 0)) * kIdxHeads + n];
+  const int64_t first = (L - R + 1) / kBlock;
+  const uint32_t full = (uint32_t)(first > kSamplePages ? first : kSamplePages);
+  const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
+  // stage the workgroup's pages: every load first, then the LDS writes
+  u32x4 ch[kRowPages];
+  uint32_t sc[kRowPages];
+  const int tc = t < NCH ? t : 0;  // threads past a page's chunks re-read chunk 0 and write nothing
+#pragma unroll
+  for (int i = 0; i < kRowPages; ++i) {
+    const size_t pid = (uint32_t)table[(uint32_t)((uint64_t)(j0 + i) * full / NSP)];
+    ch[i] = *reinterpret_cast<const u32x4*>((KF4 ? a.key_fp4 : a.key_fp8) + pid * KB + 16 * tc);
+    sc[i] = KF4 ? reinterpret_cast<const uint32_t*>(a.key_e8m0)[pid * kBlock + (t & 63)]
+                : __float_as_uint(a.key_scale[pid * kBlock + (t & 63)]);
+  }
+#pragma unroll
+  for (int i = 0; i < kRowPages; ++i) {
+    if (t < NCH) {
+      const int key = t / (KB / kBlock / 16), j = t % (KB / kBlock / 16);
+      *reinterpret_cast<u32x4*>(&keys_s[i][staged_chunk_off<KF4>(key, j)]) = ch[i];
+    }
+    if (t < kBlock) ks_s[i][t] = sc[i];
+  }
+  __syncthreads();  // the pages are staged (every wave reaches this)
+  if (!has_row || L - R + r + 1 <= kTakeAll) return;  // no row, or a row that keeps every score
+  hold_query(qraw);
+  RowQuery<QFP8, KF4> q;
+  finish_row_query<QFP8, KF4>(qraw, wbits, q);
+  float* out = samp + ((size_t)b * R + r) * kSampleKeys;
+  for (int i = 0; i < kRowPages; ++i) {
+    PageKeys<KF4> pk;
+    lds_page<KF4>(keys_s[i], ks_s[i], pk);
+    float v[2];
+    score_page<QFP8, KF4>(q, pk, v);
     if (g == 0) {
       out[(j0 + i) * kBlock + n] = v[0];
       out[(j0 + i) * kBlock + 32 + n] = v[1];
@@ -434,24 +533,21 @@ __global__ __launch_bounds__(kTF) void candidate_select_kernel(ScoreArgs a, int 
 // threshold saves the selection.
 static int sampled_pages(int rows) { return rows > 32 ? 64 : kSamplePages; }
 
-template <bool KF4, int NSP, int PPW, bool MULTI, bool QFP8>
+template <bool KF4, int NSP, bool QFP8>
 static void launch_sample_score(const ScoreArgs& a, int rows, float* samp, hipStream_t st) {
   constexpr int kWaves = kSampleThreads / 64;
-  const int B = rows / a.R, waves = MULTI ? kWaves : a.R;
-  hipLaunchKernelGGL((sample_score_kernel<KF4, NSP, PPW, MULTI, QFP8>),
-                     dim3(B * (NSP / PPW), MULTI ? (a.R + kWaves - 1) / kWaves : 1), dim3(64 * waves), 0, st, a, samp);
+  const int B = rows / a.R;
+  if (a.R > kWaves)
+    hipLaunchKernelGGL((sample_score_rows_kernel<KF4, NSP, QFP8>), dim3(B * (NSP / kRowPages), (a.R + kWaves - 1) / kWaves),
+                       dim3(kSampleThreads), 0, st, a, samp);
+  else
+    hipLaunchKernelGGL((sample_score_kernel<KF4, NSP, 2, QFP8>), dim3(B * (NSP / 2)), dim3(64 * a.R), 0, st, a, samp);
 }
 
 template <bool KF4, bool QFP8>
 static void launch_sample_score(const ScoreArgs& a, int rows, float* samp, hipStream_t st) {
-  const bool multi = a.R > kSampleThreads / 64;
-  if (sampled_pages(rows) == kSamplePages) {
-    if (multi) launch_sample_score<KF4, kSamplePages, 2, true, QFP8>(a, rows, samp, st);
-    else launch_sample_score<KF4, kSamplePages, 2, false, QFP8>(a, rows, samp, st);
-  } else {
-    if (multi) launch_sample_score<KF4, 64, 2, true, QFP8>(a, rows, samp, st);
-    else launch_sample_score<KF4, 64, 2, false, QFP8>(a, rows, samp, st);
-  }
+  if (sampled_pages(rows) == kSamplePages) launch_sample_score<KF4, kSamplePages, QFP8>(a, rows, samp, st);
+  else launch_sample_score<KF4, 64, QFP8>(a, rows, samp, st);
 }
 
 // E4M3 query codes arrive with their row scales (a.q_scale set); bf16

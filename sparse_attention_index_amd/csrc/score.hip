@@ -324,15 +324,23 @@ __global__ __launch_bounds__(kThreads)
         // few per page at long contexts); with one row per group only the
         // lower lane half keeps
         if (i >= 0) {
-          const int pos = (jx + i * stride) * kBlock + 32 * h + n;
-          // the two candidates are read as values, then selected per lane half:
+          const int half_pos = (jx + i * stride) * kBlock + 32 * h;  // the half's first key
+          const int pos = half_pos + n;
+          // keys of the half each row sees (uniform): the group's first row
+          // in lanes < 32, its second above; a row past the group's last
+          // sees none, and so does the upper half with one row per group
+          const int nva = wr0 + gi * G < nr ? pos0 + wr0 + gi * G - half_pos + 1 : 0;
+          const int nvb = G == 2 && wr0 + gi * G + 1 < nr ? pos0 + wr0 + gi * G + 1 - half_pos + 1 : 0;
+          auto lanes_below = [](int nv) { return nv >= 32 ? ~0u : (nv <= 0 ? 0u : (1u << nv) - 1u); };
+          const uint64_t vis = (uint64_t)lanes_below(nva) | ((uint64_t)lanes_below(nvb) << 32);
+          // the two thresholds are read as values, then selected per lane half:
           // a select of their addresses would put the arrays in scratch
           float thr_a = thr_w[gi * G], thr_b = thr_w[gi * G + G - 1];
           asm volatile("" : "+v"(thr_a), "+v"(thr_b));
           const float thr_rr = (G == 2 && g) ? thr_b : thr_a;
-          const bool keep = (G == 2 || g == 0) && wr0 + rr < nr && pos <= pos0 + wr0 + rr && v >= thr_rr;
-          const uint64_t m = __ballot(keep);
+          const uint64_t m = __ballot(v >= thr_rr) & vis;
           if (m) {
+            const bool keep = v >= thr_rr && n < (g ? nvb : nva);  // this lane's bit of m
             const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
             const uint32_t rank = g == 0 ? __builtin_amdgcn_mbcnt_lo(mlo, 0u) : __builtin_amdgcn_mbcnt_hi(mhi, 0u);
             uint32_t f_a = fcnt[gi * G], f_b = fcnt[gi * G + G - 1];
@@ -576,7 +584,9 @@ hipError_t launch_index_score(const ScoreArgs& a, int B, int max_ctx, bool q_fp8
 
 template <bool KF4, bool QFP8>
 static int filter_grid_fmt(int B, int R, int max_ctx) {
-  if (QFP8 && R > 16) return (int)grid_x<4, QFP8, KF4, true>(B, R, max_ctx);
+  if constexpr (QFP8) {  // (bf16 rows never take the 16-row variant)
+    if (R > 16) return (int)grid_x<4, QFP8, KF4, true>(B, R, max_ctx);
+  }
   return (int)(R > 4 ? grid_x<2, QFP8, KF4, true>(B, R, max_ctx) : grid_x<1, QFP8, KF4, true>(B, R, max_ctx));
 }
 

@@ -90,11 +90,10 @@ def test_counters_need_the_current_source(monkeypatch, tmp_path):
 
 
 def test_sample_kernel_names_follow_the_row_count():
-    assert bench.sample_kernels(16, 4, False) == ["sample_score_kernel<false,128,2,false,false>",
-                                                  "sample_select_kernel"]
-    assert bench.sample_kernels(64, 4, True) == ["sample_score_kernel<true,64,2,false,false>", "sample_select_kernel"]
-    assert bench.sample_kernels(10, 10, False)[0] == "sample_score_kernel<false,128,2,true,false>"
-    assert bench.sample_kernels(16, 4, False, True)[0] == "sample_score_kernel<false,128,2,false,true>"
+    assert bench.sample_kernels(16, 4, False) == ["sample_score_kernel<false,128,2,false>", "sample_select_kernel"]
+    assert bench.sample_kernels(64, 4, True) == ["sample_score_kernel<true,64,2,false>", "sample_select_kernel"]
+    assert bench.sample_kernels(10, 10, False)[0] == "sample_score_rows_kernel<false,128,false>"
+    assert bench.sample_kernels(16, 4, False, True)[0] == "sample_score_kernel<false,128,2,true>"
 
 
 def test_counter_hash_follows_code_not_comments():
