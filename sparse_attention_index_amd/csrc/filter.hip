@@ -130,12 +130,12 @@ DSA_DEV void score_page(const RowQuery<QFP8, KF4>& q, const PageKeys<KF4>& p, fl
 // kTakeAll tokens: NSP whole pages (128, or 64 past 32 rows) evenly spaced
 // over the `full` pages that every such row of the request sees in full (at
 // least 128, so the sampled pages are distinct), sampled page j being page
-// floor(j * full / NSP). A workgroup takes PPW sampled pages of one request
-// for its rows, one wave per row (past 8 rows, workgroup row y of the grid
-// takes rows 8y .. 8y + 7): the waves load the same pages, so all but the
-// first copy come from the CU's cache, and the pages' latency is spread
-// over the workgroups (each wave splits its row's query once per
-// workgroup). The second takes
+// floor(j * full / NSP). With up to 8 rows per request, a workgroup takes
+// PPW sampled pages of one request for all its rows, one wave per row: the
+// waves load the same pages, so all but the first copy come from the CU's
+// cache, and the pages' latency is spread over the workgroups (each wave
+// splits its row's query once per workgroup); more rows take
+// sample_score_rows_kernel below. The second takes
 // each row's threshold from its samples (sample_select: a little below the
 // sampled rank that leaves about 1.25k of the row's scores above it).
 template <bool KF4, int NSP, int PPW, bool QFP8>
