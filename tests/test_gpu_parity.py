@@ -60,6 +60,11 @@ FUSED_ONLY = {
     # gathers each region with a group of waves
     "fp8q_1x64_filtered": dict(B=1, R=64, lengths=[50000], seed=121, permute_blocks=True, fp8_query=True),
     "fp8q_1x1024_filtered": dict(B=1, R=1024, lengths=[46000], seed=122, fp8_query=True),
+    # MXFP4 keys past 8 rows per request: the sampling pass stages its pages in
+    # LDS for each group of 8 rows; two rows per scoring wave (bf16 queries)
+    # and 16 rows per scoring workgroup with 64 sampled pages (E4M3 queries)
+    "mx_1x12_filtered": dict(B=1, R=12, lengths=[52000], seed=123, permute_blocks=True, key_format="mxfp4"),
+    "fp8q_mx_1x40_filtered": dict(B=1, R=40, lengths=[47000], seed=124, fp8_query=True, key_format="mxfp4"),
 }
 
 
@@ -302,7 +307,8 @@ def test_sparse_mla_skips_invalid_entries(gpu):
 @pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "3x3_short_perm", "1x8", "2x2_long_perm",
                                   "5x3_filtered_ragged", "2x7_filtered", "1x10_filtered", "fp8q_2x7",
                                   "fp8q_3x4_filtered", "fp8q_2x6_filtered", "fp8q_1x10_filtered",
-                                  "fp8q_mx_2x4_filtered", "fp8q_1x64_filtered"])
+                                  "fp8q_mx_2x4_filtered", "fp8q_1x64_filtered", "mx_1x12_filtered",
+                                  "fp8q_mx_1x40_filtered"])
 def test_fused_decode_matches_oracle_and_stages(gpu, name):
     case = _case(name)
     out, lse, idx = gpu_decode(case)
@@ -366,7 +372,8 @@ def _kth_scores(case, k):
 
 
 @pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "1x1_8k", "40x4_many_rows", "2x7_filtered",
-                                  "1x10_filtered", "fp8q_3x4_filtered", "fp8q_2x6_filtered", "fp8q_1x64_filtered"])
+                                  "1x10_filtered", "fp8q_3x4_filtered", "fp8q_2x6_filtered", "fp8q_1x64_filtered",
+                                  "mx_1x12_filtered"])
 def test_thresholded_decode_equals_the_staged_path_whatever_the_threshold(gpu, name):
     """The filtered decode with caller-given thresholds against the stored
     path (dsa_index_score -> dsa_topk -> dsa_sparse_mla_decode). Too high a
@@ -406,7 +413,8 @@ def test_thresholded_decode_equals_the_staged_path_whatever_the_threshold(gpu, n
 
 @pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "2x4_ragged_perm", "40x4_many_rows",
                                   "2x7_filtered", "1x10_filtered", "fp8q_3x4_filtered", "fp8q_1x10_filtered",
-                                  "fp8q_mx_2x4_filtered", "fp8q_1x64_filtered", "fp8q_1x1024_filtered"])
+                                  "fp8q_mx_2x4_filtered", "fp8q_1x64_filtered", "fp8q_1x1024_filtered",
+                                  "mx_1x12_filtered", "fp8q_mx_1x40_filtered"])
 def test_filter_stage_entry_points_select_the_stored_top_k(gpu, name):
     """dsa_filter_threshold -> dsa_filter_score -> dsa_filter_select, called
     one by one on a workspace that starts with stale bytes, select exactly
