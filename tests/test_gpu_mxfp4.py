@@ -22,6 +22,7 @@ CASES = {
     "f4_2x1_tiny": dict(B=2, R=1, lengths=[130, 64], seed=504),
     "f4_fp8q_1x64": dict(B=1, R=64, lengths=[2048 + 64], seed=505, fp8_query=True),
     "f4_fp8q_2x7": dict(B=2, R=7, lengths=[3333, 5000], seed=506, fp8_query=True, permute_blocks=True),
+    "f4_fp8q_2x3": dict(B=2, R=3, lengths=[3000, 4500], seed=507, fp8_query=True),
 }
 
 
@@ -53,7 +54,7 @@ def test_mxfp4_topk_exact_and_in_band(gpu, name):
         check_topk_band(idx[row], oracle.row_scores(case, row), 2048, f"{name} row {row}")
 
 
-@pytest.mark.parametrize("name", ["f4_1x4_3k", "f4_2x3_perm", "f4_1x8"])
+@pytest.mark.parametrize("name", ["f4_1x4_3k", "f4_2x3_perm", "f4_1x8", "f4_fp8q_2x3"])
 def test_mxfp4_fused_decode_matches_oracle(gpu, name):
     case = _case(name)
     out, lse, idx = gpu_decode(case)

@@ -29,6 +29,8 @@ CASES = {
     "1x2_tiny": dict(B=1, R=2, lengths=[130], seed=106),
     "fp8q_1x64": dict(B=1, R=64, lengths=[2048 + 64], seed=107, fp8_query=True),
     "fp8q_2x7": dict(B=2, R=7, lengths=[5000, 3333], seed=108, fp8_query=True, permute_blocks=True),
+    # E4M3 query rows with one row per scoring wave (decode-sized requests)
+    "fp8q_2x3_perm": dict(B=2, R=3, lengths=[4100, 1500], seed=125, fp8_query=True, permute_blocks=True),
 }
 
 # fused decode only: rows past the single-workgroup top-k path (sliced
@@ -65,6 +67,8 @@ FUSED_ONLY = {
     # and 16 rows per scoring workgroup with 64 sampled pages (E4M3 queries)
     "mx_1x12_filtered": dict(B=1, R=12, lengths=[52000], seed=123, permute_blocks=True, key_format="mxfp4"),
     "fp8q_mx_1x40_filtered": dict(B=1, R=40, lengths=[47000], seed=124, fp8_query=True, key_format="mxfp4"),
+    # E4M3 queries over MXFP4 keys with two rows per scoring wave
+    "fp8q_mx_1x12_filtered": dict(B=1, R=12, lengths=[50000], seed=126, fp8_query=True, key_format="mxfp4"),
 }
 
 
@@ -305,10 +309,10 @@ def test_sparse_mla_skips_invalid_entries(gpu):
 
 
 @pytest.mark.parametrize("name", ["1x1_8k", "2x4_ragged_perm", "3x3_short_perm", "1x8", "2x2_long_perm",
-                                  "5x3_filtered_ragged", "2x7_filtered", "1x10_filtered", "fp8q_2x7",
+                                  "fp8q_2x3_perm", "5x3_filtered_ragged", "2x7_filtered", "1x10_filtered", "fp8q_2x7",
                                   "fp8q_3x4_filtered", "fp8q_2x6_filtered", "fp8q_1x10_filtered",
                                   "fp8q_mx_2x4_filtered", "fp8q_1x64_filtered", "mx_1x12_filtered",
-                                  "fp8q_mx_1x40_filtered"])
+                                  "fp8q_mx_1x40_filtered", "fp8q_mx_1x12_filtered"])
 def test_fused_decode_matches_oracle_and_stages(gpu, name):
     case = _case(name)
     out, lse, idx = gpu_decode(case)
@@ -414,7 +418,7 @@ def test_thresholded_decode_equals_the_staged_path_whatever_the_threshold(gpu, n
 @pytest.mark.parametrize("name", ["2x2_long_perm", "5x3_filtered_ragged", "2x4_ragged_perm", "40x4_many_rows",
                                   "2x7_filtered", "1x10_filtered", "fp8q_3x4_filtered", "fp8q_1x10_filtered",
                                   "fp8q_mx_2x4_filtered", "fp8q_1x64_filtered", "fp8q_1x1024_filtered",
-                                  "mx_1x12_filtered", "fp8q_mx_1x40_filtered"])
+                                  "mx_1x12_filtered", "fp8q_mx_1x40_filtered", "fp8q_mx_1x12_filtered"])
 def test_filter_stage_entry_points_select_the_stored_top_k(gpu, name):
     """dsa_filter_threshold -> dsa_filter_score -> dsa_filter_select, called
     one by one on a workspace that starts with stale bytes, select exactly
