@@ -367,7 +367,7 @@ int32_t dsa_dcp_topk(const float* scores, int64_t ld, const int32_t* row_len, in
  * output and its lse; the W partials are combined as
  *   L = log sum_w exp(lse_w),  out = sum_w exp(lse_w - L) out_w,
  * into out (bf16 [rows][16][512]) and lse (fp32 [rows][16], may be NULL).
- * Arguments as for dsa_sparse_mla_decode, plus W (2..64); at most 65535 rows.
+ * Arguments as for dsa_sparse_mla_decode, plus W (2..64); rows * W at most 65535.
  *   ws  dsa_dcp_workspace_size(DSA_WS_DCP_MLA, rows, 0, k, W, 0) bytes.
  */
 int32_t dsa_dcp_mla_decode(const dsa_batch* batch, const dsa_cache* cache, const void* q, int32_t num_heads,

@@ -531,7 +531,7 @@ int32_t dsa_dcp_mla_decode(const dsa_batch* batch, const dsa_cache* cache, const
   if ((r = check_mla(num_heads, k, q, idx, out, true))) return r;
   if (W < 2 || W > 64) return fail(DSA_ERR_UNSUPPORTED, "W must be in [2, 64]");
   const int32_t rows = batch->num_requests * batch->rows_per_request;
-  if (rows > 65535) return fail(DSA_ERR_UNSUPPORTED, "at most 65535 rows");
+  if ((int64_t)rows * W > 65535) return fail(DSA_ERR_UNSUPPORTED, "rows * W must be <= 65535");
   const size_t need = dsa_dcp_workspace_size(DSA_WS_DCP_MLA, rows, 0, k, W, 0);
   if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "dcp mla needs %zu workspace bytes", need);
   MlaArgs a;

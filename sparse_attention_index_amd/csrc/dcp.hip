@@ -313,19 +313,35 @@ hipError_t launch_dcp_topk(const float* scores, int64_t ld, const int32_t* row_l
 
 // ---------------------------------------------------------------- attention
 
+// Shard w's part of row r is virtual row w * rows + r: its winners, its
+// partial output and LSE.
 size_t dcp_mla_ws_bytes(int rows, int k, int W) {
-  return a256((size_t)W * rows * k * 4) + a256((size_t)W * rows * kMlaHeads * kV * 2) +
-         a256((size_t)W * rows * kMlaHeads * 4) + a256(mla_ws_bytes(rows, k, true));
+  const int vrows = W * rows;
+  return a256((size_t)vrows * k * 4) + a256((size_t)vrows * 4) + a256((size_t)vrows * kMlaHeads * kV * 2) +
+         a256((size_t)vrows * kMlaHeads * 4) + a256(mla_ws_bytes(vrows, k, true));
 }
 
-// idx_w[w][r][j] = idx[r][j] where shard w owns it, else -1.
-__global__ __launch_bounds__(kDcpThreads) void dcp_owner_kernel(const int32_t* __restrict__ idx, int rows, int k,
-                                                                int W, int32_t* __restrict__ idx_w) {
-  const size_t n = (size_t)rows * k;
-  const size_t i = (size_t)blockIdx.x * kDcpThreads + threadIdx.x;
-  if (i >= n) return;
-  const int p = idx[i];
-  for (int w = 0; w < W; ++w) idx_w[(size_t)w * n + i] = (p >= 0 && p % W == w) ? p : -1;
+// The winners of row r that shard w owns (positions p with p mod W = w), in
+// their order: idx_w[w * rows + r][0 .. cnt_w[w * rows + r]). One wave per
+// virtual row, 64 winners per step: a ballot marks the owned ones and each
+// takes its slot from the ballot's prefix count.
+__global__ __launch_bounds__(256) void dcp_owner_kernel(const int32_t* __restrict__ idx, int rows, int k, int W,
+                                                       int32_t* __restrict__ idx_w, int32_t* __restrict__ cnt_w) {
+  const int lane = threadIdx.x & 63;
+  const int vr = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (vr >= W * rows) return;  // the whole wave
+  const int w = vr / rows, r = vr - w * rows;
+  const int32_t* src = idx + (size_t)r * k;
+  int32_t* dst = idx_w + (size_t)vr * k;
+  uint32_t cnt = 0;
+  for (int j0 = 0; j0 < k; j0 += 64) {
+    const int p = j0 + lane < k ? src[j0 + lane] : -1;
+    const bool own = p >= 0 && p % W == w;
+    const uint64_t m = __ballot(own);
+    if (own) dst[cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = p;
+    cnt += (uint32_t)__popcll(m);
+  }
+  if (lane == 0) cnt_w[vr] = (int32_t)cnt;
 }
 
 // out = sum_w exp(lse_w - L) out_w, L = log sum_w exp(lse_w); one thread per
@@ -361,27 +377,31 @@ __global__ __launch_bounds__(kDcpThreads) void dcp_combine_kernel(const uint16_t
 }
 
 hipError_t launch_dcp_mla(const MlaArgs& a, int rows, int W, void* ws, hipStream_t st) {
+  const int vrows = W * rows;
   char* b = static_cast<char*>(ws);
   int32_t* idx_w = reinterpret_cast<int32_t*>(b);
-  b += a256((size_t)W * rows * a.k * 4);
+  b += a256((size_t)vrows * a.k * 4);
+  int32_t* cnt_w = reinterpret_cast<int32_t*>(b);
+  b += a256((size_t)vrows * 4);
   uint16_t* out_w = reinterpret_cast<uint16_t*>(b);
-  b += a256((size_t)W * rows * kMlaHeads * kV * 2);
+  b += a256((size_t)vrows * kMlaHeads * kV * 2);
   float* lse_w = reinterpret_cast<float*>(b);
-  b += a256((size_t)W * rows * kMlaHeads * 4);
+  b += a256((size_t)vrows * kMlaHeads * 4);
   void* mla_ws = b;
-  const size_t n = (size_t)rows * a.k;
-  hipLaunchKernelGGL(dcp_owner_kernel, dim3((unsigned)((n + kDcpThreads - 1) / kDcpThreads)), dim3(kDcpThreads), 0,
-                     st, a.idx, rows, a.k, W, idx_w);
+  hipLaunchKernelGGL(dcp_owner_kernel, dim3((unsigned)((vrows + 3) / 4)), dim3(256), 0, st, a.idx, rows, a.k, W,
+                     idx_w, cnt_w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  for (int w = 0; w < W; ++w) {  // each shard's partial attention over the winners it owns
-    MlaArgs s = a;
-    s.idx = idx_w + (size_t)w * n;
-    s.slots = nullptr;
-    s.out = out_w + (size_t)w * rows * kMlaHeads * kV;
-    s.lse = lse_w + (size_t)w * rows * kMlaHeads;
-    if ((e = launch_sparse_mla(s, rows, true, mla_ws, st)) != hipSuccess) return e;
-  }
+  // every shard's partial attention over the winners it owns, in one launch
+  // over the virtual rows (each takes its query and request from row r)
+  MlaArgs s = a;
+  s.idx = idx_w;
+  s.slots = nullptr;
+  s.out = out_w;
+  s.lse = lse_w;
+  s.q_rows = rows;
+  s.nvalid = cnt_w;
+  if ((e = launch_sparse_mla(s, vrows, true, mla_ws, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(dcp_combine_kernel, dim3(kV / 64, rows), dim3(kDcpThreads), 0, st, out_w, lse_w, rows, W,
                      a.out, a.lse);
   return hipGetLastError();

@@ -107,6 +107,9 @@ struct MlaArgs {
   float sm_scale;
   uint16_t* out;            // bf16 [rows][16][512]
   float* lse;               // [rows][16] or null
+  int32_t q_rows = 0;               // nonzero: row r takes its query, request and block-table row
+                                    // from row r % q_rows (several virtual shards of the same rows)
+  const int32_t* nvalid = nullptr;  // [rows] or null: row r attends to idx[r][0 .. nvalid[r]) only
 };
 
 size_t mla_ws_bytes(int rows, int k, bool split);

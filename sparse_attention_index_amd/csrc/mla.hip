@@ -122,9 +122,10 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
   const int n = lane & 15;
   const int row = blockIdx.y;
   const int split = blockIdx.x;
-  const int b = row / a.R;
+  const int qrow = a.q_rows ? row % a.q_rows : row;  // the query row (and request) this row attends for
+  const int b = qrow / a.R;
   const int kbeg = split * part.keys_per_split;
-  const int kend = min(a.k, kbeg + part.keys_per_split);
+  const int kend = min(a.nvalid ? a.nvalid[row] : a.k, min(a.k, kbeg + part.keys_per_split));
   const int nkeys = max(0, kend - kbeg);
   const int ntiles = (nkeys + TK - 1) / TK;
   const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(512) void sparse_mla_kernel(MlaArgs a, MlaPart part
   uint32_t qpair[9];
   {
     const uint32_t* qp = reinterpret_cast<const uint32_t*>(a.q) +
-                         (((size_t)row * kMlaHeads + (tid >> 5)) * kLat + 18 * (tid & 31)) / 2;
+                         (((size_t)qrow * kMlaHeads + (tid >> 5)) * kLat + 18 * (tid & 31)) / 2;
 #pragma unroll
     for (int j = 0; j < 9; ++j) qpair[j] = qp[j];
   }
