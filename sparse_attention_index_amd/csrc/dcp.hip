@@ -323,10 +323,13 @@ size_t dcp_mla_ws_bytes(int rows, int k, int W) {
 
 // The winners of row r that shard w owns (positions p with p mod W = w), in
 // their order: idx_w[w * rows + r][0 .. cnt_w[w * rows + r]). One wave per
-// virtual row, 64 winners per step: a ballot marks the owned ones and each
-// takes its slot from the ballot's prefix count.
+// virtual row. The row's winners are loaded 2,048 at a time, every load at
+// a clamped (always valid) address so that all are in flight together;
+// then, 64 at a time, a ballot marks the owned ones and each takes its slot
+// from the ballot's prefix count.
 __global__ __launch_bounds__(256) void dcp_owner_kernel(const int32_t* __restrict__ idx, int rows, int k, int W,
                                                        int32_t* __restrict__ idx_w, int32_t* __restrict__ cnt_w) {
+  constexpr int kPerLane = 32;
   const int lane = threadIdx.x & 63;
   const int vr = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (vr >= W * rows) return;  // the whole wave
@@ -334,12 +337,18 @@ __global__ __launch_bounds__(256) void dcp_owner_kernel(const int32_t* __restric
   const int32_t* src = idx + (size_t)r * k;
   int32_t* dst = idx_w + (size_t)vr * k;
   uint32_t cnt = 0;
-  for (int j0 = 0; j0 < k; j0 += 64) {
-    const int p = j0 + lane < k ? src[j0 + lane] : -1;
-    const bool own = p >= 0 && p % W == w;
-    const uint64_t m = __ballot(own);
-    if (own) dst[cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = p;
-    cnt += (uint32_t)__popcll(m);
+  for (int c0 = 0; c0 < k; c0 += 64 * kPerLane) {
+    int32_t p[kPerLane];
+#pragma unroll
+    for (int t = 0; t < kPerLane; ++t) p[t] = src[min(c0 + 64 * t + lane, k - 1)];
+#pragma unroll
+    for (int t = 0; t < kPerLane; ++t) {
+      const bool own = c0 + 64 * t + lane < k && p[t] >= 0 && p[t] % W == w;
+      const uint64_t m = __ballot(own);
+      if (own)
+        dst[cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = p[t];
+      cnt += (uint32_t)__popcll(m);
+    }
   }
   if (lane == 0) cnt_w[vr] = (int32_t)cnt;
 }
